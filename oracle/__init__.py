@@ -1,0 +1,190 @@
+"""CPU oracle for MoE token dispatch and combine -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, the package smoke check and the benchmark's CPU-baseline leg
+may import this module.  It wraps ``oracle.c`` (plain C, built with gcc) with
+numpy in and numpy out; it shares no code with the HIP path.
+
+What each function computes is the plain definition of the three calls on the
+sglang page "[jit_kernel] Add prepare_moe_input JIT kernels" (section
+"Changes"); ``oracle.c`` states the readings taken where the page is silent.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+# The oracle's own element-type numbering (see oracle.c).
+DTYPES = {"f32": 0, "f16": 1, "bf16": 2}
+
+_lib = None
+
+
+def build(out_path: str | None = None, src_path: str | None = None) -> str:
+    """Compile the oracle with gcc; returns the library path."""
+    out_path = out_path or _LIB_PATH
+    src_path = src_path or _SRC
+    tmp = out_path + ".tmp"
+    cmd = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c11", "-Wall",
+           "-Werror", "-fPIC", "-shared", src_path, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out_path)
+    return out_path
+
+
+def load(path: str | None = None):
+    """Load (building first if absent) the oracle library.  With ``path``,
+    load that build instead of the default one (used by the mutation tests)."""
+    global _lib
+    if path is not None:
+        return _declare(ctypes.CDLL(path))
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build()
+        _lib = _declare(ctypes.CDLL(_LIB_PATH))
+    return _lib
+
+
+def _declare(lib):
+    c_i32p = ctypes.POINTER(ctypes.c_int32)
+    lib.oracle_prepare_moe_input.restype = ctypes.c_int
+    lib.oracle_prepare_moe_input.argtypes = [
+        ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+        ctypes.c_int32, ctypes.c_int32,
+        c_i32p, c_i32p, c_i32p, c_i32p, ctypes.c_int64, c_i32p, c_i32p]
+    lib.oracle_shuffle_rows.restype = None
+    lib.oracle_shuffle_rows.argtypes = [
+        ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, c_i32p, ctypes.c_int64, ctypes.c_void_p]
+    lib.oracle_apply_shuffle_mul_sum.restype = None
+    lib.oracle_apply_shuffle_mul_sum.argtypes = [
+        ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, c_i32p, ctypes.c_void_p, ctypes.c_int,
+        ctypes.c_int64, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int]
+    for name in ("oracle_f32_to_bf16", "oracle_f32_to_f16"):
+        getattr(lib, name).restype = ctypes.c_uint16
+        getattr(lib, name).argtypes = [ctypes.c_float]
+    for name in ("oracle_bf16_to_f32", "oracle_f16_to_f32"):
+        getattr(lib, name).restype = ctypes.c_float
+        getattr(lib, name).argtypes = [ctypes.c_uint16]
+    return lib
+
+
+def _i32p(a: np.ndarray | None):
+    if a is None:
+        return None
+    assert a.dtype == np.int32 and a.flags.c_contiguous
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def capacity_rows(T: int, k: int, E: int, row_align: int) -> int:
+    """Rows a dispatched buffer needs for any routing: every pick plus at most
+    row_align - 1 padding rows per expert."""
+    return T * k + E * (row_align - 1)
+
+
+def prepare_moe_input(ids: np.ndarray, num_experts: int, row_align: int = 1,
+                      blockscale_align: int = 128, gemm: tuple = (0, 0, 0, 0),
+                      r_max: int | None = None, lib=None) -> dict:
+    """Routing metadata for top-k ids [T, k] (int32 or int64)."""
+    lib = lib or load()
+    ids = np.ascontiguousarray(ids)
+    if ids.dtype not in (np.int32, np.int64) or ids.ndim != 2:
+        raise TypeError("ids must be a 2-D int32 or int64 array")
+    T, k = ids.shape
+    E = int(num_experts)
+    if r_max is None:
+        r_max = capacity_rows(T, k, E, row_align)
+    eo = np.zeros(E + 1, np.int32)
+    ps1 = np.zeros((E, 3), np.int32)
+    ps2 = np.zeros((E, 3), np.int32)
+    inp = np.zeros(r_max, np.int32)
+    outp = np.zeros(T * k, np.int32)
+    bso = np.zeros(E + 1, np.int32)
+    rc = lib.oracle_prepare_moe_input(
+        ids.ctypes.data, ids.dtype.itemsize, T, k, E, *[int(g) for g in gemm],
+        row_align, blockscale_align, _i32p(eo), _i32p(ps1), _i32p(ps2), _i32p(inp), r_max,
+        _i32p(outp), _i32p(bso))
+    if rc != 0:
+        raise ValueError(f"oracle_prepare_moe_input failed with {rc}")
+    return {"expert_offsets": eo, "problem_sizes1": ps1, "problem_sizes2": ps2,
+            "input_permutation": inp, "output_permutation": outp,
+            "blockscale_offsets": bso}
+
+
+def shuffle_rows(src: np.ndarray, dst2src: np.ndarray, num_dst_rows: int | None = None,
+                 dst: np.ndarray | None = None, lib=None) -> np.ndarray:
+    """dst[r] = src[dst2src[r]] byte for byte (src is [n, ...] of any dtype).
+    Rows whose index is out of range keep the contents of ``dst`` (zeros when
+    ``dst`` is not given)."""
+    lib = lib or load()
+    src = np.ascontiguousarray(src)
+    dst2src = np.ascontiguousarray(dst2src, dtype=np.int32)
+    n_dst = len(dst2src) if num_dst_rows is None else num_dst_rows
+    row_bytes = src[0:1].nbytes if len(src) else int(np.prod(src.shape[1:])) * src.itemsize
+    if dst is None:
+        dst = np.zeros((n_dst,) + src.shape[1:], dtype=src.dtype)
+    assert dst.flags.c_contiguous and dst.dtype == src.dtype
+    lib.oracle_shuffle_rows(src.ctypes.data, len(src), row_bytes, _i32p(dst2src), n_dst,
+                            dst.ctypes.data)
+    return dst
+
+
+def _elem_array(a: np.ndarray, dtype: str) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    want = np.float32 if dtype == "f32" else np.uint16
+    if a.dtype != want:
+        a = a.view(want)
+    return a
+
+
+def apply_shuffle_mul_sum(y: np.ndarray, y_dtype: str, permutation: np.ndarray,
+                          factors: np.ndarray | None, factors_dtype: str, T: int, k: int,
+                          out_dtype: str, lib=None) -> np.ndarray:
+    """out[t] = round(sum_j factors[t, j] * y[permutation[t*k + j]]) in fp32.
+
+    bf16 / f16 arrays are passed as their 16-bit patterns (uint16 / int16
+    views); f32 as float32.  Returns float32 for "f32", else uint16 patterns.
+    """
+    lib = lib or load()
+    y = _elem_array(y, y_dtype)
+    H = y.shape[1] if y.ndim == 2 else 0
+    perm = np.ascontiguousarray(permutation, dtype=np.int32)
+    assert perm.size == T * k
+    f = _elem_array(factors, factors_dtype) if factors is not None else None
+    out = np.zeros((T, H), dtype=np.float32 if out_dtype == "f32" else np.uint16)
+    lib.oracle_apply_shuffle_mul_sum(
+        y.ctypes.data, DTYPES[y_dtype], len(y), _i32p(perm),
+        f.ctypes.data if f is not None else None, DTYPES[factors_dtype], T, k, H,
+        out.ctypes.data, DTYPES[out_dtype])
+    return out
+
+
+def f32_to_bf16(x: np.ndarray, lib=None) -> np.ndarray:
+    lib = lib or load()
+    return np.array([lib.oracle_f32_to_bf16(float(v)) for v in np.asarray(x, np.float32).ravel()],
+                    dtype=np.uint16)
+
+
+def f32_to_f16(x: np.ndarray, lib=None) -> np.ndarray:
+    lib = lib or load()
+    return np.array([lib.oracle_f32_to_f16(float(v)) for v in np.asarray(x, np.float32).ravel()],
+                    dtype=np.uint16)
+
+
+def bf16_to_f32(h: np.ndarray, lib=None) -> np.ndarray:
+    lib = lib or load()
+    return np.array([lib.oracle_bf16_to_f32(int(v)) for v in np.asarray(h, np.uint16).ravel()],
+                    dtype=np.float32)
+
+
+def f16_to_f32(h: np.ndarray, lib=None) -> np.ndarray:
+    lib = lib or load()
+    return np.array([lib.oracle_f16_to_f32(int(v)) for v in np.asarray(h, np.uint16).ravel()],
+                    dtype=np.float32)

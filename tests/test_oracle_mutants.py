@@ -1,0 +1,77 @@
+"""Planted mistakes in the oracle must fail its pins (no GPU).
+
+Each mutant is a copy of oracle/oracle.c with one plausible mistake (a dropped
+term, a wrong index, a wrong sign, a wrong rounding rule, lost stability),
+built with gcc into a temporary directory.  The full pin suite runs against
+it in a child process (so a mutant that crashes cannot take the test runner
+down); the mutant is "caught" when that process fails.
+"""
+
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "oracle.c")
+
+MUTANTS = {
+    "count_ignores_padding": ("off += round_up(count[e], row_align);", "off += count[e];"),
+    "token_index_mod": ("input_perm[r] = (int32_t)(i / k);", "input_perm[r] = (int32_t)(i % k);"),
+    "pick_instead_of_token": ("input_perm[r] = (int32_t)(i / k);", "input_perm[r] = (int32_t)i;"),
+    "blockscale_uses_row_align": ("bs += round_up(count[e], bs_align);",
+                                  "bs += round_up(count[e], row_align);"),
+    "segment_right_aligned": ("cursor[e] = off;",
+                              "cursor[e] = off + round_up(count[e], row_align) - count[e];"),
+    "unstable_reverse_within_expert": (
+        "int64_t r = cursor[e]++;",
+        "int64_t seen = cursor[e]++ - expert_offsets[e]; "
+        "int64_t r = expert_offsets[e] + count[e] - 1 - seen;"),
+    "combine_drops_accumulator": ("acc = fmaf(v, w, acc);", "acc = fmaf(v, w, 0.0f);"),
+    "combine_wrong_sign": ("acc = fmaf(v, w, acc);", "acc = fmaf(v, -w, acc);"),
+    "combine_unfused": ("acc = fmaf(v, w, acc);", "acc = (float)(v * w) + acc;"),
+    "factor_index_t_plus_j": ("load_elem(factors, f_dtype, t * k + j)",
+                              "load_elem(factors, f_dtype, t + j)"),
+    "combine_reads_transposed_column": ("load_elem(y, y_dtype, r * H + h)",
+                                        "load_elem(y, y_dtype, r * H + (H - 1 - h))"),
+    "bf16_ties_away_from_zero": ("if (rest > 0x8000u || (rest == 0x8000u && (t & 1u)))",
+                                 "if (rest >= 0x8000u)"),
+    "bf16_truncates": ("t += 1;", "t += 0;"),
+    "f16_subnormal_scale": ("float q = rintf(a * 0x1p24f);", "float q = rintf(a * 0x1p23f);"),
+    "f16_bias_off_by_one": ("(((ex + 15) << 10)", "(((ex + 14) << 10)"),
+    "f16_widen_bias": ("v = ldexpf((float)(1024 + fr), ex - 25);",
+                       "v = ldexpf((float)(1024 + fr), ex - 24);"),
+    "shuffle_accepts_last_plus_one": ("if (s < 0 || s >= n_src) continue;",
+                                      "if (s < 0 || s > n_src) continue;"),
+    "invalid_id_kept_as_expert0": ("output_perm[i] = -1;\n",
+                                   "output_perm[i] = 0;\n"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} is not unique in oracle.c"
+    mutant_c = tmp_path / "oracle_mutant.c"
+    mutant_c.write_text(src.replace(old, new))
+    lib = oracle.build(out_path=str(tmp_path / "liboracle_mutant.so"), src_path=str(mutant_c))
+    env = dict(os.environ, PYTHONPATH=ROOT)
+    proc = subprocess.run([sys.executable, "-c",
+                           f"import tests.oracle_pins as p; p.run_all({lib!r})"],
+                          cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
+    assert proc.returncode != 0, f"mutant {name} passed every pin"
+
+
+def test_unmutated_copy_passes(tmp_path):
+    """The same harness accepts the real oracle (so a failure above is the
+    mutation, not the harness)."""
+    lib = oracle.build(out_path=str(tmp_path / "liboracle_copy.so"))
+    env = dict(os.environ, PYTHONPATH=ROOT)
+    proc = subprocess.run([sys.executable, "-c",
+                           f"import tests.oracle_pins as p; p.run_all({lib!r})"],
+                          cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
+    assert proc.returncode == 0, proc.stderr[-2000:]
