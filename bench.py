@@ -1,0 +1,252 @@
+#!/usr/bin/env python3
+"""Benchmark: MoE dispatch + combine on one MI355X.
+
+One step = the whole hot path on one batch: prepare_moe_input (routing
+metadata) -> dispatch_rows (token rows into expert-contiguous rows) ->
+apply_shuffle_mul_sum (gather, weight, fp32 sum back to tokens).  Inputs are
+seeded synthetic routing and activations, resident in HBM before timing.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Prints one JSON line: tokens/s over the K timed steps (wall clock between
+two device synchronisations), per-stage times from HIP events recorded on
+the launch stream inside the timed region, the dominant kernel's achieved
+algorithmic HBM bandwidth against MI355X's 8 TB/s, and the CPU oracle timed
+on a bounded sample of the same workload on the host.
+
+--copy-probe BYTES times a plain device copy of BYTES bytes instead (the
+reference kernel whose HBM counters calibrate the traffic figures).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+DEFAULT_WORKLOAD = "uniform_T4096_H7168_E256_k8_pad128"
+METRIC = "dispatch+combine tokens/s; achieved HBM GB/s vs MI355X peak"
+KERNEL_SOURCES = ("route.hip", "rows.hip", "combine.hip", "device_common.h")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "combine_topk_ids_expert_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="wall-clock budget of the CPU-oracle sample")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-probe", type=int, default=0, metavar="BYTES")
+    return p.parse_args()
+
+
+def algorithmic_bytes(w, n_valid: int, cap: int, id_bytes: int) -> dict:
+    """Bytes each stage must move: every source row read once, every
+    destination row written once, index and weight arrays once; padding
+    rows are never touched."""
+    T, k, E = w.T, w.k, w.E
+    row = w.H * w.x_elem_bytes
+    side = w.scale_width * 4
+    y_b = {"bf16": 2, "f16": 2, "f32": 4}[w.y_dtype]
+    o_b = {"bf16": 2, "f16": 2, "f32": 4}[w.out_dtype]
+    prep = T * k * id_bytes + T * k * 4 + cap * 4 + E * 4 * 3 + E * 12 * 2
+    disp = T * (row + side) + n_valid * (row + side) + T * k * 4
+    comb = n_valid * w.H * y_b + T * w.H * o_b + T * k * 4 + T * k * 4
+    return {"prepare": prep, "dispatch": disp, "combine": comb}
+
+
+def load_traffic(workload: str, kernel: str) -> dict | None:
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("kernels", {}).get(kernel)
+
+
+def cpu_baseline(w, inp, x, y, budget_s: float) -> dict:
+    """The oracle, as it stands, on the same workload: whole steps (prepare,
+    row gather, combine) repeated until the time budget is spent."""
+    import numpy as np
+    import torch
+    import oracle
+
+    ids = inp["ids"]
+    x_bits = x.cpu().contiguous()
+    x_bits = x_bits.view(torch.uint8).numpy()
+    y_bits = y.cpu().view(torch.int16).numpy().view(np.uint16) if y.dtype != torch.float32 \
+        else y.cpu().numpy()
+    y_code = {"bf16": "bf16", "f16": "f16", "f32": "f32"}[w.y_dtype]
+    steps, t_total = 0, 0.0
+    while steps == 0 or (t_total < budget_s and steps < 50):
+        t0 = time.perf_counter()
+        m = oracle.prepare_moe_input(ids, w.E, row_align=w.row_align)
+        oracle.shuffle_rows(x_bits, m["input_permutation"])
+        oracle.apply_shuffle_mul_sum(y_bits, y_code, m["output_permutation"], inp["weights"],
+                                     "f32", w.T, w.k, w.out_dtype)
+        t_total += time.perf_counter() - t0
+        steps += 1
+    return {"value": w.T * steps / t_total, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{steps} whole step(s) of {w.name} (T={w.T}), single-threaded C oracle, "
+                      f"{t_total:.1f} s"}
+
+
+def copy_probe(nbytes: int, steps: int) -> None:
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    print(json.dumps({"copy_probe_bytes": nbytes, "steps": steps, "ms": dt * 1e3,
+                      "gbps_read_plus_write": 2 * nbytes / dt / 1e9}), flush=True)
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    if args.copy_probe:
+        copy_probe(args.copy_probe, max(args.steps, 1))
+        return
+
+    import combine_topk_ids_expert_amd as mx
+    from workloads import get_workload, build_inputs
+    from workloads.configs import expert_output
+
+    w = get_workload(args.workload)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = build_inputs(w, dev)
+    T, k, E, H = w.T, w.k, w.E, w.H
+    ids = torch.from_numpy(inp["ids"]).to(dev)
+    weights = torch.from_numpy(inp["weights"]).to(dev)
+    x, scales = inp["x"], inp["scales"]
+    r = mx.empty_routing(T, k, E, dev, row_align=w.row_align, blockscale=w.blockscale)
+    cap = r["input_permutation"].numel()
+    xd = torch.empty((cap, H), dtype=x.dtype, device=dev)
+    sd = torch.empty((cap, scales.shape[1]), dtype=torch.float32, device=dev) \
+        if scales is not None else None
+    y = expert_output(w, cap, dev)
+    odt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[w.out_dtype]
+    out = torch.empty((T, H), dtype=odt, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def prepare():
+        mx.prepare_moe_input(ids, r["expert_offsets"], r["problem_sizes1"], r["problem_sizes2"],
+                             r["input_permutation"], r["output_permutation"], E, 2048, H,
+                             r["blockscale_offsets"], row_align=w.row_align,
+                             workspace=r["workspace"])
+
+    def dispatch():
+        mx.dispatch_rows(x, r["output_permutation"], k, xd, scales, sd)
+
+    def combine():
+        mx.apply_shuffle_mul_sum(y, out, r["output_permutation"], weights)
+
+    stages = (("prepare", prepare), ("dispatch", dispatch), ("combine", combine))
+    for _ in range(args.warmup):
+        for _, fn in stages:
+            fn()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+          for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(K):
+        ev[s][0].record(stream)
+        for i, (_, fn) in enumerate(stages):
+            fn()
+            ev[s][i + 1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    stage_ms = {}
+    for i, (name, _) in enumerate(stages):
+        ts = np.array([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(K)])
+        stage_ms[name] = {"mean": float(ts.mean()), "p50": float(np.percentile(ts, 50)),
+                          "p90": float(np.percentile(ts, 90)), "p99": float(np.percentile(ts, 99)),
+                          "min": float(ts.min())}
+    counts = r["problem_sizes1"][:, 0].cpu().numpy()
+    n_valid = int(counts.sum())
+    nbytes = algorithmic_bytes(w, n_valid, cap, ids.element_size())
+    dom = max(("dispatch", "combine"), key=lambda n: stage_ms[n]["mean"])
+    kernel_name = {"dispatch": "dispatch_rows_kernel", "combine": "combine_vec_kernel"}[dom]
+    achieved = nbytes[dom] / (stage_ms[dom]["mean"] * 1e-3) / 1e9
+    traffic = load_traffic(w.name, kernel_name)
+    step_bytes = sum(nbytes.values())
+    ms_per_step = elapsed / K * 1e3
+    value = T * K / elapsed
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, inp, x, y, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"fp8": "fp8-e4m3 rows, bf16 combine"}.get(w.x_dtype, w.x_dtype),
+        "data": "synthetic",
+        "config": {"workload": w.name, "T": T, "H": H, "E": E, "topk": k, "routing": w.mode,
+                   "row_align": w.row_align, "x_dtype": w.x_dtype, "out_dtype": w.out_dtype},
+        "roofline": {"bound": "hbm", "kernel": kernel_name, "achieved": achieved,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": traffic},
+        "cpu_baseline": cpu,
+        "stages_ms": stage_ms,
+        "algorithmic_bytes": nbytes,
+        "step_hbm_gbps": step_bytes / (ms_per_step * 1e-3) / 1e9,
+        "step_frac_of_peak": step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "expert_load": {"max": int(counts.max()), "min": int(counts.min()),
+                        "mean": float(counts.mean()),
+                        "imbalance_ratio": float(counts.max() / max(counts.mean(), 1e-9))},
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

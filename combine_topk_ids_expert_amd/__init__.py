@@ -1,0 +1,292 @@
+"""MoE token dispatch and combine on one AMD MI355X (gfx950).
+
+A thin ctypes binding over ``libmxmoe.so`` (HIP kernels behind the C ABI in
+``include/mxmoe.h``).  Every function here only checks and marshals
+arguments: torch tensors supply device pointers and the current HIP stream,
+and all work runs in the library's kernels.  There is no fallback: without
+the built library every call raises.
+
+The calls follow the sglang page "[jit_kernel] Add prepare_moe_input JIT
+kernels" (section "Changes"): ``prepare_moe_input`` (routing metadata),
+``shuffle_rows`` (row gather), ``apply_shuffle_mul_sum`` (gather, scale,
+fp32 sum); ``dispatch_rows`` is the token-major form of the row gather.
+Outputs are written in place, as the page's custom-op registration marks.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch  # loads the HIP runtime this library must share; keep before CDLL
+
+__all__ = [
+    "prepare_moe_input", "shuffle_rows", "dispatch_rows", "apply_shuffle_mul_sum",
+    "dispatch_capacity", "prepare_workspace_size", "empty_routing", "MxError",
+    "library_path", "load_library", "EXPORTED_SYMBOLS",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libmxmoe.so")
+
+# mx_dtype codes of mxmoe.h
+MX_F32, MX_F16, MX_BF16, MX_FP8_E4M3, MX_I32, MX_I64 = range(6)
+_FLOAT_CODES = {torch.float32: MX_F32, torch.float16: MX_F16, torch.bfloat16: MX_BF16}
+MAX_EXPERTS = 1024
+
+EXPORTED_SYMBOLS = (
+    "mx_status_string", "mx_last_hip_error", "mx_dispatch_capacity",
+    "mx_prepare_workspace_size", "mx_prepare_moe_input", "mx_shuffle_rows",
+    "mx_dispatch_rows", "mx_apply_shuffle_mul_sum",
+)
+
+
+class MxError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        lib = load_library()
+        msg = lib.mx_status_string(status).decode()
+        if status == 6:
+            msg += f" (hipError_t {lib.mx_last_hip_error()})"
+        super().__init__(f"{what}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libmxmoe.so (built by ``python -m combine_topk_ids_expert_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is missing: build it with "
+                          "`python -m combine_topk_ids_expert_amd.build`; there is no fallback")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.mx_status_string.restype = ctypes.c_char_p
+    lib.mx_status_string.argtypes = [ctypes.c_int]
+    lib.mx_last_hip_error.restype = ctypes.c_int
+    lib.mx_last_hip_error.argtypes = []
+    lib.mx_dispatch_capacity.restype = i64
+    lib.mx_dispatch_capacity.argtypes = [i64, i32, i32, i32]
+    lib.mx_prepare_workspace_size.restype = sz
+    lib.mx_prepare_workspace_size.argtypes = [i64, i32, i32]
+    lib.mx_prepare_moe_input.restype = ctypes.c_int
+    lib.mx_prepare_moe_input.argtypes = [
+        vp, i32, i64, i32, i32, i32, i32, i32, i32, i32,
+        vp, vp, vp, vp, i64, vp, vp, i32, vp, sz, vp]
+    lib.mx_shuffle_rows.restype = ctypes.c_int
+    lib.mx_shuffle_rows.argtypes = [vp, i64, i64, vp, i64, vp, vp]
+    lib.mx_dispatch_rows.restype = ctypes.c_int
+    lib.mx_dispatch_rows.argtypes = [vp, i64, i32, i64, vp, vp, i64, vp, i64, vp, vp]
+    lib.mx_apply_shuffle_mul_sum.restype = ctypes.c_int
+    lib.mx_apply_shuffle_mul_sum.argtypes = [vp, i32, i64, i64, vp, vp, i32, i64, i32, vp, i32, vp]
+    _lib = lib
+    return lib
+
+
+def _ptr(t: torch.Tensor | None):
+    if t is None or t.numel() == 0:
+        return None
+    return t.data_ptr()
+
+
+def _check_dev(name: str, t: torch.Tensor, device: torch.device | None = None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU (got {t.device})")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_i32(name: str, t: torch.Tensor, numel: int | None = None):
+    if t.dtype != torch.int32:
+        raise TypeError(f"{name} must be int32 (got {t.dtype})")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} must have {numel} elements (got {t.numel()})")
+
+
+def _row_bytes(t: torch.Tensor) -> int:
+    return math.prod(t.shape[1:]) * t.element_size()
+
+
+def _stream(device: torch.device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _call(status: int, what: str):
+    if status != 0:
+        raise MxError(status, what)
+
+
+def dispatch_capacity(num_tokens: int, topk: int, num_experts: int, row_align: int = 1) -> int:
+    """Rows a dispatched buffer needs for any routing (T*k + E*(row_align-1))."""
+    cap = load_library().mx_dispatch_capacity(num_tokens, topk, num_experts, row_align)
+    if cap < 0:
+        raise ValueError("dispatch capacity out of range")
+    return cap
+
+
+def prepare_workspace_size(num_tokens: int, topk: int, num_experts: int) -> int:
+    return load_library().mx_prepare_workspace_size(num_tokens, topk, num_experts)
+
+
+def empty_routing(num_tokens: int, topk: int, num_experts: int, device, row_align: int = 1,
+                  blockscale: bool = False) -> dict:
+    """Output and workspace tensors for prepare_moe_input (torch.empty)."""
+    cap = dispatch_capacity(num_tokens, topk, num_experts, row_align)
+    E = num_experts
+    out = {
+        "expert_offsets": torch.empty(E + 1, dtype=torch.int32, device=device),
+        "problem_sizes1": torch.empty(E, 3, dtype=torch.int32, device=device),
+        "problem_sizes2": torch.empty(E, 3, dtype=torch.int32, device=device),
+        "input_permutation": torch.empty(cap, dtype=torch.int32, device=device),
+        "output_permutation": torch.empty(num_tokens * topk, dtype=torch.int32, device=device),
+        "blockscale_offsets": (torch.empty(E + 1, dtype=torch.int32, device=device)
+                               if blockscale else None),
+        "workspace": torch.empty(max(prepare_workspace_size(num_tokens, topk, E), 4),
+                                 dtype=torch.uint8, device=device),
+    }
+    return out
+
+
+def prepare_moe_input(topk_ids: torch.Tensor, expert_offsets: torch.Tensor,
+                      problem_sizes1: torch.Tensor | None, problem_sizes2: torch.Tensor | None,
+                      input_permutation: torch.Tensor, output_permutation: torch.Tensor,
+                      num_experts: int, n: int, k: int,
+                      blockscale_offsets: torch.Tensor | None = None, *,
+                      row_align: int = 1, blockscale_align: int = 128,
+                      workspace: torch.Tensor | None = None) -> None:
+    """Routing metadata for ``topk_ids`` [T, topk] (int32 or int64), in place.
+
+    ``n`` and ``k`` are the expert MLP's intermediate and hidden sizes; the
+    problem sizes are (count, 2n, k) for the gate+up GEMM and (count, k, n)
+    for the down GEMM.  ``input_permutation`` must hold at least
+    ``dispatch_capacity(T, topk, num_experts, row_align)`` entries.
+    """
+    lib = load_library()
+    _check_dev("topk_ids", topk_ids)
+    dev = topk_ids.device
+    if topk_ids.dim() != 2 or topk_ids.dtype not in (torch.int32, torch.int64):
+        raise TypeError("topk_ids must be a 2-D int32 or int64 tensor")
+    T, topk = topk_ids.shape
+    E = int(num_experts)
+    for name, t, numel in [("expert_offsets", expert_offsets, E + 1),
+                           ("output_permutation", output_permutation, T * topk),
+                           ("input_permutation", input_permutation, None),
+                           ("problem_sizes1", problem_sizes1, 3 * E),
+                           ("problem_sizes2", problem_sizes2, 3 * E),
+                           ("blockscale_offsets", blockscale_offsets, E + 1)]:
+        if t is None:
+            if name in ("expert_offsets", "output_permutation", "input_permutation"):
+                raise ValueError(f"{name} is required")
+            continue
+        _check_dev(name, t, dev)
+        _check_i32(name, t, numel)
+    if workspace is None:
+        workspace = torch.empty(max(lib.mx_prepare_workspace_size(T, topk, E), 4),
+                                dtype=torch.uint8, device=dev)
+    _check_dev("workspace", workspace, dev)
+    _call(lib.mx_prepare_moe_input(
+        _ptr(topk_ids), MX_I64 if topk_ids.dtype == torch.int64 else MX_I32, T, topk, E,
+        2 * n, k, k, n, row_align,
+        _ptr(expert_offsets), _ptr(problem_sizes1), _ptr(problem_sizes2),
+        _ptr(input_permutation), input_permutation.numel(), _ptr(output_permutation),
+        _ptr(blockscale_offsets), blockscale_align,
+        _ptr(workspace), workspace.numel(), _stream(dev)), "prepare_moe_input")
+
+
+def shuffle_rows(input: torch.Tensor, dst2src_map: torch.Tensor,
+                 output: torch.Tensor | None = None) -> torch.Tensor:
+    """output[r] = input[dst2src_map[r]] byte for byte (rows with an index out
+    of range keep their contents).  Any dtype; row = everything past dim 0."""
+    lib = load_library()
+    _check_dev("input", input)
+    dev = input.device
+    _check_dev("dst2src_map", dst2src_map, dev)
+    _check_i32("dst2src_map", dst2src_map)
+    n_dst = dst2src_map.numel()
+    if output is None:
+        output = torch.empty((n_dst,) + tuple(input.shape[1:]), dtype=input.dtype, device=dev)
+    _check_dev("output", output, dev)
+    if output.dtype != input.dtype or output.shape[1:] != input.shape[1:] or len(output) != n_dst:
+        raise ValueError("output must be [len(dst2src_map), *input.shape[1:]] of input's dtype")
+    row_bytes = _row_bytes(input)
+    if n_dst:
+        _call(lib.mx_shuffle_rows(_ptr(input), input.shape[0], row_bytes, _ptr(dst2src_map),
+                                  n_dst, _ptr(output), _stream(dev)), "shuffle_rows")
+    return output
+
+
+def dispatch_rows(input: torch.Tensor, output_permutation: torch.Tensor, topk: int,
+                  output: torch.Tensor, side_input: torch.Tensor | None = None,
+                  side_output: torch.Tensor | None = None) -> torch.Tensor:
+    """output[output_permutation[t*topk + j]] = input[t] for every token t and
+    pick j (destinations out of range are skipped); optionally the same for
+    a side row per token (e.g. FP8 block scales)."""
+    lib = load_library()
+    _check_dev("input", input)
+    dev = input.device
+    _check_dev("output_permutation", output_permutation, dev)
+    _check_i32("output_permutation", output_permutation, input.shape[0] * topk)
+    _check_dev("output", output, dev)
+    if output.dtype != input.dtype or output.shape[1:] != input.shape[1:]:
+        raise ValueError("output must have input's dtype and row shape")
+    side_rb = 0
+    if side_input is not None or side_output is not None:
+        if side_input is None or side_output is None:
+            raise ValueError("side_input and side_output go together")
+        _check_dev("side_input", side_input, dev)
+        _check_dev("side_output", side_output, dev)
+        if side_input.shape[0] != input.shape[0] or side_output.shape[0] != output.shape[0] or \
+                side_output.shape[1:] != side_input.shape[1:] or side_output.dtype != side_input.dtype:
+            raise ValueError("side rows must match the main rows' counts and each other's shape")
+        side_rb = _row_bytes(side_input)
+    T = input.shape[0]
+    if T and output.shape[0]:
+        _call(lib.mx_dispatch_rows(_ptr(input), T, topk, _row_bytes(input),
+                                   _ptr(output_permutation), _ptr(output), output.shape[0],
+                                   _ptr(side_input), side_rb, _ptr(side_output), _stream(dev)),
+              "dispatch_rows")
+    return output
+
+
+def apply_shuffle_mul_sum(input: torch.Tensor, output: torch.Tensor,
+                          permutation: torch.Tensor, factors: torch.Tensor | None = None) -> None:
+    """output[t] = round(sum_j factors[t, j] * input[permutation[t*k + j]]) with
+    fp32 accumulation (k = permutation.numel() // output.shape[0]); in place."""
+    lib = load_library()
+    _check_dev("input", input)
+    dev = input.device
+    _check_dev("output", output, dev)
+    _check_dev("permutation", permutation, dev)
+    _check_i32("permutation", permutation)
+    if input.dtype not in _FLOAT_CODES or output.dtype not in _FLOAT_CODES:
+        raise TypeError("input and output must be float32, float16 or bfloat16")
+    if input.dim() != 2 or output.dim() != 2 or input.shape[1] != output.shape[1]:
+        raise ValueError("input [rows, hidden] and output [tokens, hidden] must share hidden")
+    T, H = output.shape
+    if T == 0:
+        return
+    if permutation.numel() % T:
+        raise ValueError("permutation length must be a multiple of the token count")
+    topk = permutation.numel() // T
+    fcode = 0
+    if factors is not None:
+        _check_dev("factors", factors, dev)
+        if factors.dtype not in _FLOAT_CODES or factors.numel() != T * topk:
+            raise ValueError("factors must be [tokens, topk] float32 / float16 / bfloat16")
+        fcode = _FLOAT_CODES[factors.dtype]
+    _call(lib.mx_apply_shuffle_mul_sum(
+        _ptr(input), _FLOAT_CODES[input.dtype], input.shape[0], H, _ptr(permutation),
+        _ptr(factors), fcode, T, topk, _ptr(output), _FLOAT_CODES[output.dtype], _stream(dev)),
+        "apply_shuffle_mul_sum")

@@ -1,0 +1,49 @@
+// Internal launcher interface between the C ABI (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mxmoe {
+
+struct RouteArgs {
+    const void* ids;
+    bool ids64;
+    int64_t num_picks;        // T * k
+    int32_t topk;
+    int32_t num_experts;
+    int32_t row_align;
+    int32_t bs_align;
+    int32_t gemm[4];          // gemm1_n, gemm1_k, gemm2_n, gemm2_k
+    int32_t* expert_offsets;  // [E+1]
+    int32_t* problem_sizes1;  // [E][3] or null
+    int32_t* problem_sizes2;  // [E][3] or null
+    int32_t* blockscale_offsets;  // [E+1] or null
+    int32_t* input_perm;      // [input_perm_len]
+    int64_t input_perm_len;
+    int32_t* output_perm;     // [T*k]
+    int32_t* workspace;
+};
+
+// Device workspace the routing kernels need for `num_picks` picks.
+size_t route_workspace_bytes(int64_t num_picks, int32_t num_experts);
+hipError_t launch_route(const RouteArgs& a, hipStream_t stream);
+
+hipError_t launch_shuffle_rows(const void* src, int64_t num_src_rows, int64_t row_bytes,
+                               const int32_t* dst2src, int64_t num_dst_rows, void* dst,
+                               hipStream_t stream);
+
+hipError_t launch_dispatch_rows(const void* src, int64_t num_tokens, int32_t topk,
+                                int64_t row_bytes, const int32_t* output_perm, void* dst,
+                                int64_t num_dst_rows, const void* side_src,
+                                int64_t side_row_bytes, void* side_dst, hipStream_t stream);
+
+// dtype codes as in mxmoe.h (MX_F32 = 0, MX_F16 = 1, MX_BF16 = 2); factors_dtype
+// is ignored when factors is null.
+hipError_t launch_combine(const void* y, int y_dtype, int64_t num_y_rows, int64_t hidden,
+                          const int32_t* perm, const void* factors, int factors_dtype,
+                          int64_t num_tokens, int32_t topk, void* out, int out_dtype,
+                          hipStream_t stream);
+
+}  // namespace mxmoe

@@ -1,0 +1,362 @@
+// Routing metadata for MoE dispatch: tokens per expert, padded expert offsets,
+// block-scale offsets, and the stable input / output permutations (the
+// prepare_moe_input call of the sglang page "[jit_kernel] Add
+// prepare_moe_input JIT kernels", section "Changes", item 1).
+//
+// The permutations are a stable counting sort of the flat picks i = t*k + j
+// by expert id.  The picks are cut into tiles; each tile is one workgroup of
+// 8 waves, and each wave owns a contiguous stretch of the tile.  Inside a
+// wave, 64 picks at a time, lanes holding the same expert find each other
+// with one ballot per id bit (match_key); the lowest such lane updates that
+// wave's private LDS counter for the expert, and every lane's rank among
+// equal ids is the popcount of matching lanes below it.  Since the wave
+// stretches, the 64-pick groups and the lanes are each walked in ascending
+// pick order, base(wave, expert) + rank is the stable position.
+//
+//   small inputs: one workgroup counts, scans and scatters (one launch);
+//   larger inputs: count (one workgroup per tile, per-tile totals to the
+//   workspace) -> scan (one workgroup: expert totals, padded offsets, the
+//   metadata, and each tile's base per expert) -> scatter (one workgroup per
+//   tile: recount per wave, then write both permutations).
+#include "device_common.h"
+#include "launch.h"
+
+namespace mxmoe {
+namespace {
+
+constexpr int kRouteThreads = 512;
+constexpr int kRouteWaves = kRouteThreads / kWave;
+constexpr int kBatch = 8;                 // 64-pick groups loaded per round
+constexpr int kMaxE = 1024;
+constexpr int kTile = 4096;               // picks per workgroup, multi-tile path
+constexpr int64_t kFusedMax = 8192;       // single-launch path up to this many picks
+constexpr int kScanThreads = 1024;
+
+struct Shape {
+    int64_t n;        // picks
+    int E, nbits, k;
+};
+
+__device__ __forceinline__ int round_up_i(int v, int a) { return (v + a - 1) / a * a; }
+
+template <typename IdT>
+__device__ __forceinline__ int load_key(const IdT* ids, int64_t i, int64_t end, int E) {
+    if (i >= end) return -1;
+    const IdT v = ids[i];
+    return (v >= 0 && v < (IdT)E) ? (int)v : -1;
+}
+
+// This wave's stretch [w0, w1) of the tile [t0, t1): equal stretches of a
+// multiple of 64 picks, in wave order.
+__device__ __forceinline__ void wave_stretch(int64_t t0, int64_t t1, int wave, int64_t& w0,
+                                             int64_t& w1) {
+    const int64_t per = ((t1 - t0 + kRouteWaves * kWave - 1) / (kRouteWaves * kWave)) * kWave;
+    w0 = t0 + per * wave;
+    w1 = w0 + per < t1 ? w0 + per : t1;
+    if (w0 > t1) w0 = t1;
+}
+
+// Count the valid picks of [w0, w1) per expert into this wave's LDS row.
+template <typename IdT>
+__device__ void count_stretch(const IdT* ids, int64_t w0, int64_t w1, const Shape& s,
+                              int* row) {
+    const int lane = lane_id();
+    for (int64_t g0 = w0; g0 < w1; g0 += kBatch * kWave) {
+        int key[kBatch];
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) key[b] = load_key(ids, g0 + b * kWave + lane, w1, s.E);
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) {
+            const uint64_t m = match_key(key[b], s.nbits);
+            if (key[b] >= 0 && lanes_below(m) == 0) row[key[b]] += __popcll(m);
+        }
+    }
+}
+
+// Scatter the picks of [w0, w1): row[e] holds the next free dispatched row of
+// expert e for this wave on entry and is advanced as picks are placed.
+template <typename IdT>
+__device__ void scatter_stretch(const IdT* ids, int64_t w0, int64_t w1, const Shape& s,
+                                int* row, int32_t* outp, int32_t* inp, int64_t inp_len) {
+    const int lane = lane_id();
+    for (int64_t g0 = w0; g0 < w1; g0 += kBatch * kWave) {
+        int key[kBatch];
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) key[b] = load_key(ids, g0 + b * kWave + lane, w1, s.E);
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) {
+            const int64_t i = g0 + b * kWave + lane;
+            const uint64_t m = match_key(key[b], s.nbits);
+            const int rank = lanes_below(m);
+            if (key[b] >= 0) {
+                const int r = row[key[b]] + rank;   // every lane reads before the update below
+                outp[i] = r;
+                if (r < inp_len) inp[r] = (int32_t)((uint32_t)i / (uint32_t)s.k);
+            } else if (i < w1) {
+                outp[i] = -1;
+            }
+            if (key[b] >= 0 && rank == 0) row[key[b]] += __popcll(m);
+        }
+    }
+}
+
+// Exclusive scan over experts of the padded counts (row_align and
+// blockscale_align) in one workgroup; writes expert_offsets, problem sizes
+// and block-scale offsets, and leaves each segment start in off[e].
+// Returns the padded row total R.
+__device__ int scan_experts(const RouteArgs& a, const int* cnt, int* off, int* tmp) {
+    const int E = a.num_experts;
+    const int nt = blockDim.x, tid = threadIdx.x;
+    const int per = (E + nt - 1) / nt;
+    const int e0 = tid * per < E ? tid * per : E;
+    const int e1 = e0 + per < E ? e0 + per : E;
+    int sr = 0, sb = 0;
+    for (int e = e0; e < e1; ++e) {
+        sr += round_up_i(cnt[e], a.row_align);
+        sb += round_up_i(cnt[e], a.bs_align);
+    }
+    const int ir = wave_inclusive_sum(sr), ib = wave_inclusive_sum(sb);
+    const int wave = tid / kWave, nw = nt / kWave;
+    if ((tid & (kWave - 1)) == kWave - 1) { tmp[wave] = ir; tmp[32 + wave] = ib; }
+    __syncthreads();
+    if (tid < kWave) {
+        const int vr = tid < nw ? tmp[tid] : 0, vb = tid < nw ? tmp[32 + tid] : 0;
+        const int cr = wave_inclusive_sum(vr), cb = wave_inclusive_sum(vb);
+        if (tid < nw) { tmp[64 + tid] = cr - vr; tmp[96 + tid] = cb - vb; }
+        if (tid == nw - 1) { tmp[128] = cr; }
+    }
+    __syncthreads();
+    int xr = tmp[64 + wave] + ir - sr, xb = tmp[96 + wave] + ib - sb;
+    if (tid == 0) {
+        a.expert_offsets[0] = 0;
+        if (a.blockscale_offsets) a.blockscale_offsets[0] = 0;
+    }
+    for (int e = e0; e < e1; ++e) {
+        const int c = cnt[e];
+        off[e] = xr;
+        xr += round_up_i(c, a.row_align);
+        xb += round_up_i(c, a.bs_align);
+        a.expert_offsets[e + 1] = xr;
+        if (a.blockscale_offsets) a.blockscale_offsets[e + 1] = xb;
+        if (a.problem_sizes1) {
+            a.problem_sizes1[3 * e] = c;
+            a.problem_sizes1[3 * e + 1] = a.gemm[0];
+            a.problem_sizes1[3 * e + 2] = a.gemm[1];
+        }
+        if (a.problem_sizes2) {
+            a.problem_sizes2[3 * e] = c;
+            a.problem_sizes2[3 * e + 1] = a.gemm[2];
+            a.problem_sizes2[3 * e + 2] = a.gemm[3];
+        }
+    }
+    return tmp[128];
+}
+
+// -1 into the padding rows of every expert handled by this wave and into
+// the rows past the last segment, [R, inp_len), strided over all threads.
+__device__ void fill_unused_rows(const RouteArgs& a, const int* cnt, const int* off, int R,
+                                 int first_wave, int wave_stride, int64_t first_thread,
+                                 int64_t thread_stride) {
+    const int lane = lane_id();
+    for (int e = first_wave; e < a.num_experts; e += wave_stride) {
+        const int c = cnt[e];
+        const int64_t r0 = (int64_t)off[e] + c, r1 = (int64_t)off[e] + round_up_i(c, a.row_align);
+        for (int64_t r = r0 + lane; r < r1; r += kWave) a.input_perm[r] = -1;
+    }
+    for (int64_t r = R + first_thread; r < a.input_perm_len; r += thread_stride)
+        a.input_perm[r] = -1;
+}
+
+// ---- single workgroup: count, scan and scatter in one launch -----------------
+
+template <typename IdT>
+__global__ __launch_bounds__(kRouteThreads) void route_fused_kernel(RouteArgs a, Shape s) {
+    __shared__ int rows[kRouteWaves][kMaxE];
+    __shared__ int cnt[kMaxE];
+    __shared__ int off[kMaxE];
+    __shared__ int tmp[160];
+    const int tid = threadIdx.x, wave = tid / kWave;
+    const IdT* ids = static_cast<const IdT*>(a.ids);
+
+    for (int e = tid; e < s.E; e += kRouteThreads)
+#pragma unroll
+        for (int w = 0; w < kRouteWaves; ++w) rows[w][e] = 0;
+    __syncthreads();
+    int64_t w0, w1;
+    wave_stretch(0, s.n, wave, w0, w1);
+    count_stretch<IdT>(ids, w0, w1, s, rows[wave]);
+    __syncthreads();
+    for (int e = tid; e < s.E; e += kRouteThreads) {
+        int run = 0;
+#pragma unroll
+        for (int w = 0; w < kRouteWaves; ++w) {
+            const int c = rows[w][e];
+            rows[w][e] = run;
+            run += c;
+        }
+        cnt[e] = run;
+    }
+    __syncthreads();
+    const int R = scan_experts(a, cnt, off, tmp);
+    __syncthreads();
+    for (int e = tid; e < s.E; e += kRouteThreads)
+#pragma unroll
+        for (int w = 0; w < kRouteWaves; ++w) rows[w][e] += off[e];
+    __syncthreads();
+    scatter_stretch<IdT>(ids, w0, w1, s, rows[wave], a.output_perm, a.input_perm,
+                         a.input_perm_len);
+    fill_unused_rows(a, cnt, off, R, wave, kRouteWaves, tid, kRouteThreads);
+}
+
+// ---- multi-tile path -------------------------------------------------------------
+
+// Per-tile totals per expert: workspace[tile * E + e].
+template <typename IdT>
+__global__ __launch_bounds__(kRouteThreads) void route_count_kernel(RouteArgs a, Shape s) {
+    __shared__ int rows[kRouteWaves][kMaxE];
+    const int tid = threadIdx.x, wave = tid / kWave;
+    for (int e = tid; e < s.E; e += kRouteThreads)
+#pragma unroll
+        for (int w = 0; w < kRouteWaves; ++w) rows[w][e] = 0;
+    __syncthreads();
+    const int64_t t0 = (int64_t)blockIdx.x * kTile;
+    const int64_t t1 = t0 + kTile < s.n ? t0 + kTile : s.n;
+    int64_t w0, w1;
+    wave_stretch(t0, t1, wave, w0, w1);
+    count_stretch<IdT>(static_cast<const IdT*>(a.ids), w0, w1, s, rows[wave]);
+    __syncthreads();
+    int32_t* out = a.workspace + (int64_t)blockIdx.x * s.E;
+    for (int e = tid; e < s.E; e += kRouteThreads) {
+        int sum = 0;
+#pragma unroll
+        for (int w = 0; w < kRouteWaves; ++w) sum += rows[w][e];
+        out[e] = sum;
+    }
+}
+
+// One workgroup: expert totals over the tiles, the metadata, and each tile's
+// first row per expert (replacing the tile totals in the workspace).  The
+// expert counts go to workspace[tiles * E + e] for the scatter pass.
+__global__ __launch_bounds__(kScanThreads) void route_scan_kernel(RouteArgs a, Shape s,
+                                                                  int tiles) {
+    __shared__ int part[kScanThreads];
+    __shared__ int cnt[kMaxE];
+    __shared__ int off[kMaxE];
+    __shared__ int tmp[160];
+    const int tid = threadIdx.x, E = s.E;
+    int slices = kScanThreads / E;
+    if (slices < 1) slices = 1;
+    if (slices > tiles) slices = tiles;
+    int32_t* hist = a.workspace;
+    const int e = tid % E, sl = tid / E;
+    const bool active = tid < slices * E;
+    const int b0 = active ? (int)((int64_t)tiles * sl / slices) : 0;
+    const int b1 = active ? (int)((int64_t)tiles * (sl + 1) / slices) : 0;
+    if (active) {
+        int sum = 0;
+        int b = b0;
+        for (; b + 8 <= b1; b += 8) {
+            int v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = hist[(int64_t)(b + u) * E + e];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) sum += v[u];
+        }
+        for (; b < b1; ++b) sum += hist[(int64_t)b * E + e];
+        part[sl * E + e] = sum;
+    }
+    __syncthreads();
+    for (int x = tid; x < E; x += kScanThreads) {
+        int run = 0;
+        for (int q = 0; q < slices; ++q) {
+            const int c = part[q * E + x];
+            part[q * E + x] = run;
+            run += c;
+        }
+        cnt[x] = run;
+    }
+    __syncthreads();
+    scan_experts(a, cnt, off, tmp);
+    __syncthreads();
+    for (int x = tid; x < E; x += kScanThreads) hist[(int64_t)tiles * E + x] = cnt[x];
+    if (active) {
+        int run = off[e] + part[sl * E + e];
+        for (int b = b0; b < b1; ++b) {
+            const int64_t idx = (int64_t)b * E + e;
+            const int c = hist[idx];
+            hist[idx] = run;
+            run += c;
+        }
+    }
+}
+
+template <typename IdT>
+__global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(RouteArgs a, Shape s,
+                                                                      int tiles) {
+    __shared__ int rows[kRouteWaves][kMaxE];
+    const int tid = threadIdx.x, wave = tid / kWave;
+    const IdT* ids = static_cast<const IdT*>(a.ids);
+    for (int e = tid; e < s.E; e += kRouteThreads)
+#pragma unroll
+        for (int w = 0; w < kRouteWaves; ++w) rows[w][e] = 0;
+    __syncthreads();
+    const int64_t t0 = (int64_t)blockIdx.x * kTile;
+    const int64_t t1 = t0 + kTile < s.n ? t0 + kTile : s.n;
+    int64_t w0, w1;
+    wave_stretch(t0, t1, wave, w0, w1);
+    count_stretch<IdT>(ids, w0, w1, s, rows[wave]);
+    __syncthreads();
+    const int32_t* base = a.workspace + (int64_t)blockIdx.x * s.E;
+    for (int e = tid; e < s.E; e += kRouteThreads) {
+        int run = base[e];
+#pragma unroll
+        for (int w = 0; w < kRouteWaves; ++w) {
+            const int c = rows[w][e];
+            rows[w][e] = run;
+            run += c;
+        }
+    }
+    __syncthreads();
+    scatter_stretch<IdT>(ids, w0, w1, s, rows[wave], a.output_perm, a.input_perm,
+                         a.input_perm_len);
+    // Unused rows: counts from the workspace, segment starts from expert_offsets.
+    const int32_t* cnt = a.workspace + (int64_t)tiles * s.E;
+    const int R = a.expert_offsets[s.E];
+    fill_unused_rows(a, cnt, a.expert_offsets, R, blockIdx.x * kRouteWaves + wave,
+                     tiles * kRouteWaves, (int64_t)blockIdx.x * kRouteThreads + tid,
+                     (int64_t)tiles * kRouteThreads);
+}
+
+int id_bits(int E) { return E <= 1 ? 0 : 32 - __builtin_clz((unsigned)(E - 1)); }
+
+template <typename IdT>
+hipError_t launch_typed(const RouteArgs& a, hipStream_t stream) {
+    Shape s{a.num_picks, a.num_experts, id_bits(a.num_experts), a.topk};
+    if (a.num_picks <= kFusedMax) {
+        route_fused_kernel<IdT><<<1, kRouteThreads, 0, stream>>>(a, s);
+        return hipGetLastError();
+    }
+    const int tiles = (int)((a.num_picks + kTile - 1) / kTile);
+    route_count_kernel<IdT><<<tiles, kRouteThreads, 0, stream>>>(a, s);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    route_scan_kernel<<<1, kScanThreads, 0, stream>>>(a, s, tiles);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    route_scatter_kernel<IdT><<<tiles, kRouteThreads, 0, stream>>>(a, s, tiles);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t route_workspace_bytes(int64_t num_picks, int32_t num_experts) {
+    if (num_picks <= kFusedMax) return 0;
+    const int64_t tiles = (num_picks + kTile - 1) / kTile;
+    return (size_t)((tiles + 1) * (int64_t)num_experts * (int64_t)sizeof(int32_t));
+}
+
+hipError_t launch_route(const RouteArgs& a, hipStream_t stream) {
+    return a.ids64 ? launch_typed<int64_t>(a, stream) : launch_typed<int32_t>(a, stream);
+}
+
+}  // namespace mxmoe

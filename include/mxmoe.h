@@ -1,0 +1,191 @@
+/*
+ * mxmoe -- MoE token dispatch and combine on one AMD MI355X (gfx950).
+ *
+ * A C ABI over hand-written HIP kernels for the three host calls the sglang
+ * page "[jit_kernel] Add prepare_moe_input JIT kernels" (section "Changes")
+ * describes: prepare_moe_input builds routing metadata from top-k expert ids,
+ * shuffle_rows gathers rows byte for byte, apply_shuffle_mul_sum gathers,
+ * scales by the top-k weight and sums with fp32 accumulation.  A token-major
+ * scatter form of the row gather (mx_dispatch_rows) is added because it
+ * reads every token row once.
+ *
+ * Conventions shared by every call
+ *   - Every array argument is a DEVICE pointer to memory the caller owns,
+ *     laid out row-major and contiguous.  The library allocates and frees
+ *     nothing, keeps no state between calls and never synchronises.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream).
+ *     Outputs are written in place when the stream reaches the work.
+ *   - Argument errors (null pointers, sizes out of range, unsupported dtypes,
+ *     misaligned index arrays, short buffers) are detected on the host before
+ *     any HIP call and returned as a status; nothing is enqueued then.  After
+ *     each launch the HIP launch error is checked and reported as
+ *     MX_ERR_HIP (mx_last_hip_error() gives the hipError_t value).
+ *   - Index data is never trusted: ids outside [0, E) are dropped, row
+ *     indices outside the given row counts are skipped.  No index value can
+ *     make a kernel access memory outside the arrays described here.
+ *   - Rows and picks are indexed with 32-bit integers: T*k, row capacities
+ *     and row counts must stay below 2^31.
+ */
+#ifndef MXMOE_H
+#define MXMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mx_status {
+    MX_OK = 0,
+    MX_ERR_INVALID_ARGUMENT = 1,  /* null pointer, size out of range            */
+    MX_ERR_UNSUPPORTED_DTYPE = 2, /* dtype not accepted by this call            */
+    MX_ERR_MISALIGNED = 3,        /* pointer not aligned to its element size    */
+    MX_ERR_WORKSPACE_TOO_SMALL = 4,
+    MX_ERR_CAPACITY = 5,          /* input_permutation shorter than capacity    */
+    MX_ERR_HIP = 6                /* a HIP launch failed                        */
+} mx_status;
+
+typedef enum mx_dtype {
+    MX_F32 = 0,
+    MX_F16 = 1,
+    MX_BF16 = 2,
+    MX_FP8_E4M3 = 3, /* OCP e4m3fn bytes; only as opaque row bytes          */
+    MX_I32 = 4,
+    MX_I64 = 5
+} mx_dtype;
+
+/* Largest expert count prepare_moe_input accepts. */
+#define MX_MAX_EXPERTS 1024
+
+/* Text for a status code (static storage). */
+const char* mx_status_string(mx_status status);
+
+/* hipError_t of the last launch that returned MX_ERR_HIP on this thread. */
+int mx_last_hip_error(void);
+
+/*
+ * Rows a dispatched buffer (and input_permutation) needs for ANY routing of
+ * T tokens x k picks over E experts with segments padded to row_align:
+ * T*k + E*(row_align - 1).  Returns -1 when an argument is out of range or
+ * the result does not fit in 31 bits.  Host-only arithmetic.
+ */
+int64_t mx_dispatch_capacity(int64_t num_tokens, int32_t topk, int32_t num_experts,
+                             int32_t row_align);
+
+/* Bytes of device workspace mx_prepare_moe_input needs for these sizes
+ * (0 when the arguments are out of range).  Host-only arithmetic. */
+size_t mx_prepare_workspace_size(int64_t num_tokens, int32_t topk, int32_t num_experts);
+
+/*
+ * prepare_moe_input -- routing metadata (sglang prepare_moe_input page,
+ * "Changes" item 1: compute_problem_sizes counts tokens per expert,
+ * compute_expert_offsets takes the prefix sum, compute_expert_blockscale_
+ * offsets gives the optional FP8 block-scale offsets, compute_arg_sorts
+ * builds the input and output permutations).
+ *
+ * Picks are flattened i = t*k + j.  A pick is valid iff 0 <= id < E; with
+ * count_e the number of valid picks of expert e:
+ *
+ *   expert_offsets[0] = 0,
+ *   expert_offsets[e+1] = expert_offsets[e] + ceil(count_e / row_align) * row_align
+ *   problem_sizes1[e] = {count_e, gemm1_n, gemm1_k}
+ *   problem_sizes2[e] = {count_e, gemm2_n, gemm2_k}
+ *   blockscale_offsets: the same running sum with blockscale_align in place
+ *                       of row_align
+ *   output_permutation[i] = dispatched row of pick i (-1 if the pick is dropped)
+ *   input_permutation[r]  = source token (i / k) of dispatched row r, -1 for
+ *                           padding rows and for rows past the last segment
+ *
+ * Rows of one expert hold its picks in ascending i (a stable counting sort),
+ * so the result is deterministic and independent of launch shapes.
+ *
+ * topk_ids            [T, k] MX_I32 or MX_I64 (ids_dtype), 4- / 8-byte aligned
+ * num_tokens (T) >= 0, topk (k) >= 1, 1 <= num_experts (E) <= MX_MAX_EXPERTS
+ * row_align >= 1      1 = plain prefix sum; e.g. 128 pads each segment for a
+ *                     grouped GEMM tile
+ * expert_offsets      out [E+1] int32
+ * problem_sizes1/2    out [E][3] int32, or NULL to skip
+ * input_permutation   out [input_permutation_len] int32; every entry is
+ *                     written.  input_permutation_len must be at least
+ *                     mx_dispatch_capacity(T, k, E, row_align), else
+ *                     MX_ERR_CAPACITY.
+ * output_permutation  out [T*k] int32
+ * blockscale_offsets  out [E+1] int32, or NULL to skip; blockscale_align >= 1
+ *                     (128 for 1x128 FP8 block scales) when given
+ * workspace           device scratch of at least
+ *                     mx_prepare_workspace_size(T, k, E) bytes, 4-byte
+ *                     aligned; contents on entry do not matter
+ */
+mx_status mx_prepare_moe_input(const void* topk_ids, int32_t ids_dtype, int64_t num_tokens,
+                               int32_t topk, int32_t num_experts,
+                               int32_t gemm1_n, int32_t gemm1_k, int32_t gemm2_n, int32_t gemm2_k,
+                               int32_t row_align,
+                               int32_t* expert_offsets, int32_t* problem_sizes1,
+                               int32_t* problem_sizes2,
+                               int32_t* input_permutation, int64_t input_permutation_len,
+                               int32_t* output_permutation,
+                               int32_t* blockscale_offsets, int32_t blockscale_align,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * shuffle_rows -- dtype-agnostic row gather (sglang page, "Changes" item 2):
+ *
+ *   dst[r] = src[dst2src[r]]   (row_bytes bytes) for r < num_dst_rows
+ *
+ * Rows with dst2src[r] outside [0, num_src_rows) are left untouched.
+ * src [num_src_rows, row_bytes], dst [num_dst_rows, row_bytes], any element
+ * type; dst2src [num_dst_rows] int32 (e.g. input_permutation).  row_bytes >= 1.
+ * Copies use 16-byte accesses when row_bytes and both base pointers are
+ * multiples of 16, else the widest width that divides all three.
+ */
+mx_status mx_shuffle_rows(const void* src, int64_t num_src_rows, int64_t row_bytes,
+                          const int32_t* dst2src, int64_t num_dst_rows, void* dst,
+                          void* stream);
+
+/*
+ * dispatch_rows -- the same rows as shuffle_rows(src, input_permutation),
+ * produced token by token so each source row is read once:
+ *
+ *   dst[output_permutation[t*k + j]] = src[t]   for t < T, j < k
+ *
+ * Destinations outside [0, num_dst_rows) are skipped.  Optionally a second
+ * "side" row per token (e.g. the fp32 1x128 block scales of an FP8 row) is
+ * copied the same way: side_dst[output_permutation[t*k+j]] = side_src[t]
+ * (pass side_src = side_dst = NULL and side_row_bytes = 0 to skip).
+ * src [T, row_bytes], dst [num_dst_rows, row_bytes], side arrays
+ * [*, side_row_bytes]; output_permutation [T*k] int32.
+ */
+mx_status mx_dispatch_rows(const void* src, int64_t num_tokens, int32_t topk, int64_t row_bytes,
+                           const int32_t* output_permutation, void* dst, int64_t num_dst_rows,
+                           const void* side_src, int64_t side_row_bytes, void* side_dst,
+                           void* stream);
+
+/*
+ * apply_shuffle_mul_sum -- gather, scale, reduce (sglang page, "Changes"
+ * item 3: FP32 accumulation, fp16 / bf16 / fp32):
+ *
+ *   out[t][h] = round_out( sum_{j=0..k-1} f[t][j] * y[permutation[t*k+j]][h] )
+ *
+ * The sum runs in fp32 in ascending j, each step one fused multiply-add
+ * starting from +0; round_out rounds to nearest even (identity for fp32).
+ * Picks whose row is outside [0, num_y_rows) contribute nothing.
+ *
+ * y           [num_y_rows, hidden], y_dtype MX_F32 / MX_F16 / MX_BF16
+ * permutation [T*k] int32 (output_permutation of prepare_moe_input)
+ * factors     [T, k] in MX_F32, MX_F16 or MX_BF16 (factors_dtype), or NULL
+ *             for unit weights
+ * out         [T, hidden], out_dtype MX_F32 / MX_F16 / MX_BF16
+ * Pointers must be aligned to their element size.
+ */
+mx_status mx_apply_shuffle_mul_sum(const void* y, int32_t y_dtype, int64_t num_y_rows,
+                                   int64_t hidden, const int32_t* permutation,
+                                   const void* factors, int32_t factors_dtype,
+                                   int64_t num_tokens, int32_t topk,
+                                   void* out, int32_t out_dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXMOE_H */

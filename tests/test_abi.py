@@ -1,0 +1,134 @@
+"""The C ABI on the host (no GPU): the library loads, exports every entry
+point include/mxmoe.h declares, and rejects bad arguments with the
+documented status before making any HIP call (fake device addresses are
+never dereferenced on these paths)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import combine_topk_ids_expert_amd as mx
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxmoe.h")
+
+OK, INVALID, DTYPE, MISALIGNED, WORKSPACE, CAPACITY, HIP = range(7)
+F32, F16, BF16, FP8, I32, I64 = range(6)
+P = 0x10000          # a fake, 64 KiB-aligned "device" address, never dereferenced
+S = None             # stream (never reached)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return mx.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    text = open(HEADER).read()
+    declared = set(re.findall(r"\b(mx_\w+)\s*\(", text))
+    assert declared == set(mx.EXPORTED_SYMBOLS)
+    for name in declared:
+        assert hasattr(lib, name), name
+    ext = ctypes.CDLL(mx.library_path())
+    for name in declared:
+        getattr(ext, name)
+
+
+def test_status_strings(lib):
+    for code in range(7):
+        assert lib.mx_status_string(code)
+    assert lib.mx_status_string(99) == b"unknown status"
+
+
+def test_capacity_and_workspace(lib):
+    assert lib.mx_dispatch_capacity(4096, 8, 256, 128) == 4096 * 8 + 256 * 127
+    assert lib.mx_dispatch_capacity(0, 8, 256, 1) == 0
+    assert lib.mx_dispatch_capacity(2**31, 1, 1, 1) == -1
+    assert lib.mx_dispatch_capacity(2**28, 8, 1, 1) == -1
+    assert lib.mx_dispatch_capacity(10, 0, 1, 1) == -1
+    assert lib.mx_dispatch_capacity(10, 1, 1, 0) == -1
+    assert lib.mx_prepare_workspace_size(32, 8, 256) == 0          # one-launch path
+    big = lib.mx_prepare_workspace_size(65536, 8, 288)
+    assert big >= 288 * 4 * (65536 * 8 // 4096)
+    assert lib.mx_prepare_workspace_size(10, 8, 2000) == 0
+
+
+def _prep(lib, **kw):
+    a = dict(ids=P, dt=I32, T=64, k=8, E=256, g=(1, 2, 3, 4), A=1, eo=P, ps1=P, ps2=P,
+             inp=P, inp_len=64 * 8, outp=P, bso=None, bsa=128, ws=P, wsb=1 << 20)
+    a.update(kw)
+    return lib.mx_prepare_moe_input(a["ids"], a["dt"], a["T"], a["k"], a["E"], *a["g"], a["A"],
+                                    a["eo"], a["ps1"], a["ps2"], a["inp"], a["inp_len"],
+                                    a["outp"], a["bso"], a["bsa"], a["ws"], a["wsb"], S)
+
+
+def test_prepare_rejects(lib):
+    assert _prep(lib, dt=F32) == DTYPE
+    assert _prep(lib, E=0) == INVALID
+    assert _prep(lib, E=1025) == INVALID
+    assert _prep(lib, k=0) == INVALID
+    assert _prep(lib, T=-1) == INVALID
+    assert _prep(lib, A=0) == INVALID
+    assert _prep(lib, T=2**31, k=1) == INVALID
+    assert _prep(lib, eo=None) == INVALID
+    assert _prep(lib, ids=None) == INVALID
+    assert _prep(lib, outp=None) == INVALID
+    assert _prep(lib, inp=None) == INVALID
+    assert _prep(lib, inp_len=64 * 8 - 1) == CAPACITY
+    assert _prep(lib, A=128, inp_len=64 * 8) == CAPACITY
+    assert _prep(lib, bso=P, bsa=0) == INVALID
+    assert _prep(lib, ids=P + 2) == MISALIGNED
+    assert _prep(lib, ids=P + 4, dt=I64) == MISALIGNED
+    assert _prep(lib, outp=P + 1) == MISALIGNED
+    assert _prep(lib, T=65536, inp_len=65536 * 8, ws=None) == WORKSPACE
+    assert _prep(lib, T=65536, inp_len=65536 * 8, wsb=16) == WORKSPACE
+
+
+def test_shuffle_rejects(lib):
+    f = lib.mx_shuffle_rows
+    assert f(P, 10, 0, P, 10, P, S) == INVALID
+    assert f(P, -1, 16, P, 10, P, S) == INVALID
+    assert f(P, 10, 16, None, 10, P, S) == INVALID
+    assert f(P, 10, 16, P, 10, None, S) == INVALID
+    assert f(P, 10, 16, P + 2, 10, P, S) == MISALIGNED
+    assert f(P, 10, 16, P, 0, P, S) == OK            # nothing to do, nothing launched
+
+
+def test_dispatch_rejects(lib):
+    f = lib.mx_dispatch_rows
+    assert f(P, 10, 0, 16, P, P, 80, None, 0, None, S) == INVALID
+    assert f(P, 10, 8, 0, P, P, 80, None, 0, None, S) == INVALID
+    assert f(P, 10, 8, 16, P, P, 80, P, 0, P, S) == INVALID          # side rows of 0 bytes
+    assert f(P, 10, 8, 16, P, P, 80, P, 16, None, S) == INVALID      # side without destination
+    assert f(P, 10, 8, 16, P, P, 80, None, 16, None, S) == INVALID   # side bytes without arrays
+    assert f(None, 10, 8, 16, P, P, 80, None, 0, None, S) == INVALID
+    assert f(P, 10, 8, 16, P + 1, P, 80, None, 0, None, S) == MISALIGNED
+    assert f(P, 0, 8, 16, P, P, 80, None, 0, None, S) == OK
+
+
+def test_combine_rejects(lib):
+    f = lib.mx_apply_shuffle_mul_sum
+    assert f(P, I32, 10, 8, P, None, 0, 4, 2, P, BF16, S) == DTYPE
+    assert f(P, BF16, 10, 8, P, None, 0, 4, 2, P, FP8, S) == DTYPE
+    assert f(P, BF16, 10, 8, P, P, I64, 4, 2, P, BF16, S) == DTYPE
+    assert f(P, BF16, 10, 8, P, None, 0, 4, 0, P, BF16, S) == INVALID
+    assert f(P, BF16, -1, 8, P, None, 0, 4, 2, P, BF16, S) == INVALID
+    assert f(P, BF16, 10, 8, None, None, 0, 4, 2, P, BF16, S) == INVALID
+    assert f(P, BF16, 10, 8, P, None, 0, 4, 2, None, BF16, S) == INVALID
+    assert f(P + 1, BF16, 10, 8, P, None, 0, 4, 2, P, BF16, S) == MISALIGNED
+    assert f(P, BF16, 10, 8, P, None, 0, 4, 2, P + 2, F32, S) == MISALIGNED
+    assert f(P, BF16, 10, 8, P, P + 2, F32, 4, 2, P, BF16, S) == MISALIGNED
+    assert f(P, BF16, 10, 8, P, None, 0, 0, 2, P, BF16, S) == OK
+    assert f(P, BF16, 10, 0, P, None, 0, 4, 2, P, BF16, S) == OK
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    ids = torch.zeros(4, 2, dtype=torch.int32)
+    r = {k: torch.zeros(3, dtype=torch.int32) for k in ("a", "b", "c", "d")}
+    with pytest.raises(ValueError):
+        mx.prepare_moe_input(ids, r["a"], None, None, r["b"], r["c"], 2, 1, 1)
+    with pytest.raises(ValueError):
+        mx.shuffle_rows(torch.zeros(4, 8), torch.zeros(4, dtype=torch.int32))

@@ -1,0 +1,279 @@
+"""HIP path against the CPU oracle, element by element (needs the GPU).
+
+Metadata, permutations and dispatched rows must match bit for bit; the
+combine must be within rtol 1.6e-2 / atol 1e-2 (16-bit output) or rtol 1e-5
+(fp32 output), and is also expected to match bit for bit because both sides
+take the same fused multiply-add order.  Sizes span several routing tiles
+(4096 picks each) with ragged tails, rows wider than one workgroup chunk,
+and every workload's real shape at a reduced token count; the full-size
+workloads are checked on sampled outputs and whole-array properties.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import combine_topk_ids_expert_amd as mx
+import oracle
+from tests import gpu_util as gu
+from workloads import WORKLOADS, build_inputs, routing
+from workloads.configs import expert_output
+
+pytestmark = pytest.mark.gpu
+
+DEV = gu.DEV
+
+
+def _print_case(*args):
+    print("case:", *args, flush=True)
+
+
+# --------------------------------------------------------------------------
+# prepare_moe_input
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,E,k,A,mode,bad", [
+    (0, 256, 8, 1, "uniform", 0.0),
+    (1, 256, 8, 1, "uniform", 0.0),
+    (7, 5, 3, 4, "dups", 0.2),
+    (32, 256, 8, 1, "uniform", 0.0),
+    (1000, 256, 8, 128, "uniform", 0.0),        # one-launch path, padded
+    (1024, 256, 8, 1, "uniform", 0.0),          # exactly 8192 picks
+    (1025, 256, 8, 1, "uniform", 0.0),          # first multi-tile size
+    (3001, 256, 8, 128, "uniform", 0.05),       # several tiles, ragged tail, invalid ids
+    (4096, 256, 8, 128, "uniform", 0.0),
+    (5000, 256, 8, 1, "k_hot", 0.0),
+    (4000, 128, 8, 1, "zipf", 0.0),
+    (3000, 1024, 8, 16, "uniform", 0.0),        # largest expert count
+    (2500, 1, 4, 1, "dups", 0.0),               # one expert takes everything
+    (700, 33, 70, 3, "dups", 0.1),              # topk > 64
+])
+@pytest.mark.parametrize("ids_dtype", [torch.int32, torch.int64])
+def test_prepare_matches_oracle(T, E, k, A, mode, bad, ids_dtype):
+    _print_case("prepare", T, E, k, A, mode, bad, ids_dtype)
+    rng = np.random.default_rng(T * 7 + E)
+    if mode == "dups":
+        ids = rng.integers(0, E, (T, k))
+    elif mode == "k_hot":
+        ids = routing.k_hot_topk(rng, T, E, k, 8, 0.8)
+    elif mode == "zipf":
+        ids = routing.zipf_topk(rng, T, E, k, 1.2)
+    else:
+        ids = routing.uniform_topk(rng, T, E, k)
+    if bad:
+        m = rng.random(ids.shape) < bad
+        ids = np.where(m, rng.choice([-1, -5, E, E + 77], size=ids.shape), ids)
+    gu.check_prepare(ids, E, A, ids_dtype)
+
+
+def test_prepare_all_invalid_and_int64_extremes():
+    _print_case("prepare invalid")
+    ids = np.full((5000, 8), 300, np.int64)
+    ids[::3, 1] = -(2**40)
+    ids[::5, 2] = 2**40
+    gu.check_prepare(ids, 256, 128, torch.int64)
+
+
+def test_prepare_deterministic_across_calls():
+    _print_case("prepare twice")
+    rng = np.random.default_rng(5)
+    ids = routing.k_hot_topk(rng, 6000, 256, 8, 8, 0.8)
+    a = gu.gpu_prepare(ids, 256, 128)
+    b = gu.gpu_prepare(ids, 256, 128)
+    for key in ("expert_offsets", "input_permutation", "output_permutation"):
+        np.testing.assert_array_equal(a[key], b[key])
+
+
+# --------------------------------------------------------------------------
+# dispatch rows (scatter and gather)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,H,dtype,E,k,A", [
+    (37, 7168, torch.bfloat16, 64, 8, 128),     # 14 KiB rows
+    (300, 4096, torch.bfloat16, 256, 8, 1),
+    (50, 100, torch.bfloat16, 16, 4, 8),        # 200 B rows: 8-byte accesses
+    (40, 7, torch.bfloat16, 8, 3, 1),           # 14 B rows: 2-byte accesses
+    (33, 13, torch.uint8, 8, 2, 4),             # 13 B rows: byte accesses
+    (20, 20000, torch.float32, 16, 2, 1),       # 80 KB rows: several column chunks
+    (64, 1024, torch.float16, 32, 70, 1),       # topk > 64
+])
+def test_dispatch_matches_oracle(T, H, dtype, E, k, A):
+    _print_case("dispatch", T, H, dtype, E, k, A)
+    rng = np.random.default_rng(T + H)
+    ids = rng.integers(-1, E + 1, (T, k))
+    meta = gu.check_prepare(ids, E, A)
+    if dtype == torch.uint8:
+        x = torch.from_numpy(rng.integers(0, 256, (T, H), dtype=np.uint8)).to(DEV)
+    else:
+        x = routing.normal_rows(T, H, gu.code(dtype), seed=T, device=DEV)
+    gu.check_dispatch(x, meta, k)
+
+
+def test_dispatch_misaligned_base():
+    """A base pointer off the 16-byte grid takes a narrower access width and
+    still copies exactly."""
+    _print_case("dispatch misaligned")
+    T, H, E, k = 64, 512, 32, 4
+    rng = np.random.default_rng(9)
+    meta = gu.check_prepare(routing.uniform_topk(rng, T, E, k), E, 1)
+    big = routing.normal_rows(T * H + 1, 1, "bf16", seed=3, device=DEV).view(-1)
+    x = big[1:].view(T, H)                               # 2-byte offset
+    assert x.data_ptr() % 16 != 0
+    gu.check_dispatch(x, meta, k)
+
+
+def test_dispatch_fp8_with_scale_rows():
+    _print_case("dispatch fp8")
+    w = WORKLOADS["zipf1.2_T16384_H4096fp8_E128_k8"]
+    inp = build_inputs(w, DEV, T=1500)
+    meta = gu.check_prepare(inp["ids"], w.E, 1)
+    gu.check_dispatch(inp["x"], meta, w.k, inp["scales"])
+
+
+# --------------------------------------------------------------------------
+# combine
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("ydt", [torch.bfloat16, torch.float16, torch.float32])
+@pytest.mark.parametrize("odt", [torch.bfloat16, torch.float16, torch.float32])
+@pytest.mark.parametrize("fdt", [None, torch.float32, torch.bfloat16, torch.float16])
+def test_combine_dtypes(ydt, odt, fdt):
+    _print_case("combine", ydt, odt, fdt)
+    T, H, k, R = 150, 512, 8, 1500
+    rng = np.random.default_rng(42)
+    y = routing.normal_rows(R, H, gu.code(ydt), seed=11, device=DEV)
+    perm = torch.from_numpy(rng.integers(0, R, T * k).astype(np.int32)).to(DEV)
+    f = None
+    if fdt is not None:
+        f = torch.from_numpy(routing.softmax_weights(rng, T, k)).to(fdt).to(DEV)
+    gu.check_combine(y, perm, f, odt, T)
+
+
+@pytest.mark.parametrize("T,H,k,R", [
+    (33, 7168, 8, 400),        # 896 threads per token
+    (20, 16400, 8, 200),       # two column chunks with a ragged end
+    (50, 104, 8, 300),         # short rows, vector path
+    (40, 77, 3, 90),           # H % 8 != 0: scalar path
+    (30, 256, 9, 300),         # pick batch remainder
+    (25, 64, 70, 500),         # topk > 64
+    (1, 8, 1, 1),
+])
+def test_combine_shapes(T, H, k, R):
+    _print_case("combine shape", T, H, k, R)
+    rng = np.random.default_rng(T * H)
+    y = routing.normal_rows(R, H, "bf16", seed=R, device=DEV)
+    p = rng.integers(0, R, T * k).astype(np.int32)
+    p[rng.random(p.size) < 0.1] = -1
+    p[rng.random(p.size) < 0.05] = R + 3                 # out of range: skipped
+    perm = torch.from_numpy(p).to(DEV)
+    f = torch.from_numpy(rng.standard_normal((T, k)).astype(np.float32)).to(DEV)
+    gu.check_combine(y, perm, f, torch.bfloat16, T)
+    gu.check_combine(y, perm, f, torch.float32, T)
+
+
+def test_combine_misaligned_base():
+    _print_case("combine misaligned")
+    T, H, k, R = 16, 256, 4, 64
+    rng = np.random.default_rng(3)
+    big = routing.normal_rows(R * H + 1, 1, "bf16", seed=5, device=DEV).view(-1)
+    y = big[1:].view(R, H)
+    perm = torch.from_numpy(rng.integers(0, R, T * k).astype(np.int32)).to(DEV)
+    gu.check_combine(y, perm, None, torch.bfloat16, T)
+
+
+def test_combine_identity_experts_reproduce_x():
+    """Closed form on the GPU: identity experts with weights 1/8 give x back
+    bit for bit (the partial sums are exact)."""
+    _print_case("combine identity")
+    T, H, E, k = 500, 1024, 64, 8
+    rng = np.random.default_rng(8)
+    ids = routing.uniform_topk(rng, T, E, k)
+    meta = gu.gpu_prepare(ids, E, 128)
+    x = routing.normal_rows(T, H, "bf16", seed=1, device=DEV)
+    xd = torch.empty(meta["_t"]["input_permutation"].numel(), H, dtype=torch.bfloat16, device=DEV)
+    mx.dispatch_rows(x, meta["_t"]["output_permutation"], k, xd)
+    out = torch.empty_like(x)
+    mx.apply_shuffle_mul_sum(xd, out, meta["_t"]["output_permutation"],
+                             torch.full((T, k), 0.125, device=DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), x.view(torch.int16))
+
+
+# --------------------------------------------------------------------------
+# every workload end to end at a reduced token count (same E, H, k, routing)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", sorted(WORKLOADS))
+def test_workload_end_to_end_reduced(name):
+    w = WORKLOADS[name]
+    T = min(w.T, 2048)
+    _print_case("workload reduced", name, T)
+    inp = build_inputs(w, DEV, T=T)
+    meta = gu.check_prepare(inp["ids"], w.E, w.row_align)
+    gu.check_dispatch(inp["x"], meta, w.k, inp["scales"])
+    rows = meta["_t"]["input_permutation"].numel()
+    y = expert_output(w, rows, DEV)
+    f = torch.from_numpy(inp["weights"]).to(DEV)
+    odt = {"bf16": torch.bfloat16, "f32": torch.float32}[w.out_dtype]
+    gu.check_combine(y, meta["_t"]["output_permutation"], f, odt, T)
+
+
+# --------------------------------------------------------------------------
+# full sizes, launched as the benchmark launches them; sampled outputs
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", sorted(WORKLOADS))
+def test_workload_full_size_sampled(name):
+    w = WORKLOADS[name]
+    _print_case("workload full", name, w.T)
+    inp = build_inputs(w, DEV)
+    T, k = w.T, w.k
+    meta = gu.check_prepare(inp["ids"], w.E, w.row_align)     # metadata: every entry
+    t = meta["_t"]
+    rows = t["input_permutation"].numel()
+    x = inp["x"]
+    xd = torch.empty((rows, w.H), dtype=x.dtype, device=DEV)
+    sd = None
+    if inp["scales"] is not None:
+        sd = torch.empty((rows, inp["scales"].shape[1]), dtype=torch.float32, device=DEV)
+    mx.dispatch_rows(x, t["output_permutation"], k, xd, inp["scales"], sd)
+    y = expert_output(w, rows, DEV)
+    f = torch.from_numpy(inp["weights"]).to(DEV)
+    odt = {"bf16": torch.bfloat16, "f32": torch.float32}[w.out_dtype]
+    out = torch.empty((T, w.H), dtype=odt, device=DEV)
+    mx.apply_shuffle_mul_sum(y, out, t["output_permutation"], f)
+    torch.cuda.synchronize()
+
+    rng = np.random.default_rng(123)
+    inp_perm = meta["input_permutation"]
+    used = np.nonzero(inp_perm >= 0)[0]
+    # dispatched rows: 512 sampled rows against the oracle's gather
+    sample = np.sort(rng.choice(used, size=min(512, used.size), replace=False))
+    x_host = gu.bits(x)
+    want = oracle.shuffle_rows(x_host, inp_perm[sample])
+    got = gu.bits(xd[torch.from_numpy(sample).to(DEV)])
+    np.testing.assert_array_equal(got, want)
+    if sd is not None:
+        np.testing.assert_array_equal(gu.bits(sd[torch.from_numpy(sample).to(DEV)]),
+                                      oracle.shuffle_rows(gu.bits(inp["scales"]),
+                                                          inp_perm[sample]))
+    # every used row holds its source token's bytes (exact, in chunks)
+    for c0 in range(0, used.size, 16384):
+        idx = torch.from_numpy(used[c0:c0 + 16384]).to(DEV)
+        src = torch.from_numpy(inp_perm[used[c0:c0 + 16384]].astype(np.int64)).to(DEV)
+        assert torch.equal(xd[idx].view(torch.uint8), x[src].view(torch.uint8))
+        if sd is not None:
+            assert torch.equal(sd[idx], inp["scales"][src])
+    # combine: 64 sampled tokens through the oracle, reading only their rows
+    toks = rng.choice(T, size=64, replace=False)
+    perm = meta["output_permutation"].reshape(T, k)[toks]
+    need = np.unique(perm[perm >= 0])
+    remap = np.full(rows, -1, np.int64)
+    remap[need] = np.arange(need.size)
+    sub_perm = np.where(perm >= 0, remap[np.maximum(perm, 0)], -1).astype(np.int32).ravel()
+    sub_y = gu.bits(y[torch.from_numpy(need).to(DEV)])
+    want = oracle.apply_shuffle_mul_sum(sub_y, gu.code(y.dtype), sub_perm,
+                                        inp["weights"][toks], "f32", toks.size, k,
+                                        w.out_dtype)
+    got = gu.bits(out[torch.from_numpy(toks).to(DEV)])
+    np.testing.assert_array_equal(got, want)
