@@ -10,9 +10,10 @@ seeded synthetic routing and activations, resident in HBM before timing.
 
 Prints one JSON line: tokens/s over the K timed steps (wall clock between
 two device synchronisations), per-stage times from HIP events recorded on
-the launch stream inside the timed region, the dominant kernel's achieved
-algorithmic HBM bandwidth against MI355X's 8 TB/s, and the CPU oracle timed
-on a bounded sample of the same workload on the host.
+the launch stream around each stage in a second pass of K steps, the
+dominant kernel's achieved algorithmic HBM bandwidth against MI355X's
+8 TB/s, and the CPU oracle timed on a bounded sample of the same workload on
+the host.
 
 --copy-probe BYTES times a plain device copy of BYTES bytes instead (the
 reference kernel whose HBM counters calibrate the traffic figures).
@@ -74,8 +75,10 @@ def algorithmic_bytes(w, n_valid: int, cap: int, id_bytes: int) -> dict:
 
 
 def load_traffic(workload: str, kernel: str) -> dict | None:
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if
-    it was taken on the current kernel sources."""
+    """HBM bytes per launch of ``kernel`` from the committed rocprofv3
+    counter summary (FETCH_SIZE and WRITE_SIZE, each scaled by what the same
+    counter reads for a plain copy of known size), if it was taken on the
+    current kernel sources; None otherwise."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     try:
         with open(path) as f:
@@ -184,17 +187,27 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
+    # Headline: exactly K steps between two device synchronisations.
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K):
+        for _, fn in stages:
+            fn()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    # Per-kernel durations: a second pass of K steps with HIP events recorded
+    # on the launch stream around every stage (kept out of the headline pass,
+    # since each event record adds a few microseconds between kernels).
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
           for _ in range(K)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for s in range(K):
         ev[s][0].record(stream)
         for i, (_, fn) in enumerate(stages):
             fn()
             ev[s][i + 1].record(stream)
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
 
     stage_ms = {}
     for i, (name, _) in enumerate(stages):
@@ -234,7 +247,9 @@ def main():
                    "row_align": w.row_align, "x_dtype": w.x_dtype, "out_dtype": w.out_dtype},
         "roofline": {"bound": "hbm", "kernel": kernel_name, "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": traffic},
+                     "traffic": traffic["traffic_bytes"] if traffic else None,
+                     "traffic_detail": traffic, "bytes_per_launch": nbytes[dom],
+                     "avg_launch_ms": stage_ms[dom]["mean"]},
         "cpu_baseline": cpu,
         "stages_ms": stage_ms,
         "algorithmic_bytes": nbytes,

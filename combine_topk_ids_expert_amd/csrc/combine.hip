@@ -24,41 +24,46 @@ constexpr int kGroup = 8;      // columns per thread in the vector path
 constexpr int kPickBatch = 8;  // picks whose loads are issued together
 constexpr int kMaxThreads = 1024;
 
-// 8 consecutive elements of a row, moved with 16-byte accesses.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 8 consecutive elements of a row, moved with 16-byte accesses.  Expert
+// output rows are read exactly once, so the loads carry the non-temporal
+// hint; so do the stores of the write-once output rows.
 template <typename TY> struct Pack;
-template <> struct Pack<BF16> { uint4 q; __device__ float at(int e) const { const uint32_t w = (&q.x)[e >> 1]; return to_f32(BF16{}, (uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu))); } };
-template <> struct Pack<F16> { uint4 q; __device__ float at(int e) const { const uint32_t w = (&q.x)[e >> 1]; return to_f32(F16{}, (uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu))); } };
-template <> struct Pack<F32> { uint4 q[2]; __device__ float at(int e) const { return __uint_as_float((&q[e >> 2].x)[e & 3]); } };
+template <> struct Pack<BF16> { u32x4 q; __device__ float at(int e) const { const uint32_t w = q[e >> 1]; return to_f32(BF16{}, (uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu))); } };
+template <> struct Pack<F16> { u32x4 q; __device__ float at(int e) const { const uint32_t w = q[e >> 1]; return to_f32(F16{}, (uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu))); } };
+template <> struct Pack<F32> { u32x4 q[2]; __device__ float at(int e) const { return __uint_as_float(q[e >> 2][e & 3]); } };
 
 template <typename TY>
 __device__ __forceinline__ Pack<TY> load_pack(const typename TY::storage* p) {
     Pack<TY> v;
+    const u32x4* q = reinterpret_cast<const u32x4*>(p);
     if constexpr (sizeof(typename TY::storage) == 2) {
-        v.q = *reinterpret_cast<const uint4*>(p);
+        v.q = __builtin_nontemporal_load(q);
     } else {
-        v.q[0] = reinterpret_cast<const uint4*>(p)[0];
-        v.q[1] = reinterpret_cast<const uint4*>(p)[1];
+        v.q[0] = __builtin_nontemporal_load(q);
+        v.q[1] = __builtin_nontemporal_load(q + 1);
     }
     return v;
 }
 
 template <typename TO>
 __device__ __forceinline__ void store_pack(typename TO::storage* p, const float* acc) {
+    u32x4* o = reinterpret_cast<u32x4*>(p);
     if constexpr (sizeof(typename TO::storage) == 2) {
-        uint4 q;
-        uint32_t* w = &q.x;
+        u32x4 q;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            w[i] = (uint32_t)from_f32(TO{}, acc[2 * i]) |
+            q[i] = (uint32_t)from_f32(TO{}, acc[2 * i]) |
                    ((uint32_t)from_f32(TO{}, acc[2 * i + 1]) << 16);
-        *reinterpret_cast<uint4*>(p) = q;
+        __builtin_nontemporal_store(q, o);
     } else {
-        uint4 q0 = make_uint4(__float_as_uint(acc[0]), __float_as_uint(acc[1]),
-                              __float_as_uint(acc[2]), __float_as_uint(acc[3]));
-        uint4 q1 = make_uint4(__float_as_uint(acc[4]), __float_as_uint(acc[5]),
-                              __float_as_uint(acc[6]), __float_as_uint(acc[7]));
-        reinterpret_cast<uint4*>(p)[0] = q0;
-        reinterpret_cast<uint4*>(p)[1] = q1;
+        const u32x4 q0 = {__float_as_uint(acc[0]), __float_as_uint(acc[1]),
+                          __float_as_uint(acc[2]), __float_as_uint(acc[3])};
+        const u32x4 q1 = {__float_as_uint(acc[4]), __float_as_uint(acc[5]),
+                          __float_as_uint(acc[6]), __float_as_uint(acc[7])};
+        __builtin_nontemporal_store(q0, o);
+        __builtin_nontemporal_store(q1, o + 1);
     }
 }
 

@@ -14,10 +14,14 @@
 // pick order, base(wave, expert) + rank is the stable position.
 //
 //   small inputs: one workgroup counts, scans and scatters (one launch);
-//   larger inputs: count (one workgroup per tile, per-tile totals to the
-//   workspace) -> scan (one workgroup: expert totals, padded offsets, the
-//   metadata, and each tile's base per expert) -> scatter (one workgroup per
-//   tile: recount per wave, then write both permutations).
+//   larger inputs, two launches:
+//     count   -- one workgroup per tile writes the tile's count of every
+//                expert to the workspace, expert-major ([E][tiles]);
+//     scatter -- every workgroup reads the whole count table (a thread sums
+//                one expert's row with 16-byte loads issued together), scans
+//                the padded totals over experts itself, takes its tile's base
+//                per expert, recounts its tile per wave and writes both
+//                permutations; workgroup 0 writes the offsets and sizes.
 #include "device_common.h"
 #include "launch.h"
 
@@ -28,9 +32,26 @@ constexpr int kRouteThreads = 512;
 constexpr int kRouteWaves = kRouteThreads / kWave;
 constexpr int kBatch = 8;                 // 64-pick groups loaded per round
 constexpr int kMaxE = 1024;
-constexpr int kTile = 4096;               // picks per workgroup, multi-tile path
-constexpr int64_t kFusedMax = 8192;       // single-launch path up to this many picks
-constexpr int kScanThreads = 1024;
+constexpr int kTableBatch = 8;            // 16-byte count-table loads in flight per thread
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+#ifndef MXMOE_FUSED_MAX
+#define MXMOE_FUSED_MAX 8192
+#endif
+#ifndef MXMOE_MAX_TILES
+#define MXMOE_MAX_TILES 128
+#endif
+constexpr int64_t kFusedMax = MXMOE_FUSED_MAX;  // single-launch path up to this many picks
+constexpr int64_t kMaxTiles = MXMOE_MAX_TILES;  // tiles of the two-launch path (at most)
+constexpr int64_t kTileQuantum = kRouteThreads; // tile sizes are multiples of this
+
+// Tile size of the two-launch path: the smallest multiple of kTileQuantum
+// that covers n picks in at most kMaxTiles tiles.
+__host__ __device__ inline int64_t tile_picks(int64_t n) {
+    int64_t per = (n + kMaxTiles - 1) / kMaxTiles;
+    per = (per + kTileQuantum - 1) / kTileQuantum * kTileQuantum;
+    return per < kTileQuantum ? kTileQuantum : per;
+}
 
 struct Shape {
     int64_t n;        // picks
@@ -56,47 +77,65 @@ __device__ __forceinline__ void wave_stretch(int64_t t0, int64_t t1, int wave, i
     if (w0 > t1) w0 = t1;
 }
 
+// One round of up to kBatch 64-pick groups starting at g0, keys loaded.
+template <typename IdT>
+__device__ __forceinline__ void load_keys(const IdT* ids, int64_t g0, int64_t w1, int E,
+                                          int (&key)[kBatch]) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) key[b] = load_key(ids, g0 + b * kWave + lane, w1, E);
+}
+
+// Count a round of keys per expert into this wave's LDS row.
+__device__ __forceinline__ void count_keys(const int (&key)[kBatch], const Shape& s, int* row) {
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+        const uint64_t m = match_key(key[b], s.nbits);
+        if (key[b] >= 0 && lanes_below(m) == 0) row[key[b]] += __popcll(m);
+    }
+}
+
+// Place a round of keys: row[e] holds the next free dispatched row of expert
+// e for this wave on entry and is advanced as picks are placed.
+__device__ __forceinline__ void scatter_keys(const int (&key)[kBatch], int64_t g0, int64_t w1,
+                                             const Shape& s, int* row, int32_t* outp,
+                                             int32_t* inp, int64_t inp_len) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+        const int64_t i = g0 + b * kWave + lane;
+        const uint64_t m = match_key(key[b], s.nbits);
+        const int rank = lanes_below(m);
+        if (key[b] >= 0) {
+            const int r = row[key[b]] + rank;   // every lane reads before the update below
+            outp[i] = r;
+            if (r < inp_len) inp[r] = (int32_t)((uint32_t)i / (uint32_t)s.k);
+        } else if (i < w1) {
+            outp[i] = -1;
+        }
+        if (key[b] >= 0 && rank == 0) row[key[b]] += __popcll(m);
+    }
+}
+
 // Count the valid picks of [w0, w1) per expert into this wave's LDS row.
 template <typename IdT>
 __device__ void count_stretch(const IdT* ids, int64_t w0, int64_t w1, const Shape& s,
                               int* row) {
-    const int lane = lane_id();
     for (int64_t g0 = w0; g0 < w1; g0 += kBatch * kWave) {
         int key[kBatch];
-#pragma unroll
-        for (int b = 0; b < kBatch; ++b) key[b] = load_key(ids, g0 + b * kWave + lane, w1, s.E);
-#pragma unroll
-        for (int b = 0; b < kBatch; ++b) {
-            const uint64_t m = match_key(key[b], s.nbits);
-            if (key[b] >= 0 && lanes_below(m) == 0) row[key[b]] += __popcll(m);
-        }
+        load_keys(ids, g0, w1, s.E, key);
+        count_keys(key, s, row);
     }
 }
 
-// Scatter the picks of [w0, w1): row[e] holds the next free dispatched row of
-// expert e for this wave on entry and is advanced as picks are placed.
+// Scatter the picks of [w0, w1) (see scatter_keys).
 template <typename IdT>
 __device__ void scatter_stretch(const IdT* ids, int64_t w0, int64_t w1, const Shape& s,
                                 int* row, int32_t* outp, int32_t* inp, int64_t inp_len) {
-    const int lane = lane_id();
     for (int64_t g0 = w0; g0 < w1; g0 += kBatch * kWave) {
         int key[kBatch];
-#pragma unroll
-        for (int b = 0; b < kBatch; ++b) key[b] = load_key(ids, g0 + b * kWave + lane, w1, s.E);
-#pragma unroll
-        for (int b = 0; b < kBatch; ++b) {
-            const int64_t i = g0 + b * kWave + lane;
-            const uint64_t m = match_key(key[b], s.nbits);
-            const int rank = lanes_below(m);
-            if (key[b] >= 0) {
-                const int r = row[key[b]] + rank;   // every lane reads before the update below
-                outp[i] = r;
-                if (r < inp_len) inp[r] = (int32_t)((uint32_t)i / (uint32_t)s.k);
-            } else if (i < w1) {
-                outp[i] = -1;
-            }
-            if (key[b] >= 0 && rank == 0) row[key[b]] += __popcll(m);
-        }
+        load_keys(ids, g0, w1, s.E, key);
+        scatter_keys(key, g0, w1, s, row, outp, inp, inp_len);
     }
 }
 
@@ -104,7 +143,8 @@ __device__ void scatter_stretch(const IdT* ids, int64_t w0, int64_t w1, const Sh
 // blockscale_align) in one workgroup; writes expert_offsets, problem sizes
 // and block-scale offsets, and leaves each segment start in off[e].
 // Returns the padded row total R.
-__device__ int scan_experts(const RouteArgs& a, const int* cnt, int* off, int* tmp) {
+__device__ int scan_experts(const RouteArgs& a, const int* cnt, int* off, int* tmp,
+                            bool write_meta) {
     const int E = a.num_experts;
     const int nt = blockDim.x, tid = threadIdx.x;
     const int per = (E + nt - 1) / nt;
@@ -127,6 +167,13 @@ __device__ int scan_experts(const RouteArgs& a, const int* cnt, int* off, int* t
     }
     __syncthreads();
     int xr = tmp[64 + wave] + ir - sr, xb = tmp[96 + wave] + ib - sb;
+    if (!write_meta) {
+        for (int e = e0; e < e1; ++e) {
+            off[e] = xr;
+            xr += round_up_i(cnt[e], a.row_align);
+        }
+        return tmp[128];
+    }
     if (tid == 0) {
         a.expert_offsets[0] = 0;
         if (a.blockscale_offsets) a.blockscale_offsets[0] = 0;
@@ -197,7 +244,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_fused_kernel(RouteArgs a,
         cnt[e] = run;
     }
     __syncthreads();
-    const int R = scan_experts(a, cnt, off, tmp);
+    const int R = scan_experts(a, cnt, off, tmp, true);
     __syncthreads();
     for (int e = tid; e < s.E; e += kRouteThreads)
 #pragma unroll
@@ -208,107 +255,90 @@ __global__ __launch_bounds__(kRouteThreads) void route_fused_kernel(RouteArgs a,
     fill_unused_rows(a, cnt, off, R, wave, kRouteWaves, tid, kRouteThreads);
 }
 
-// ---- multi-tile path -------------------------------------------------------------
+// ---- two-launch path -------------------------------------------------------
 
-// Per-tile totals per expert: workspace[tile * E + e].
+// Tile counts per expert, expert-major: workspace[e * stride + tile] with the
+// row stride rounded up to 4 tiles (16 bytes).
 template <typename IdT>
-__global__ __launch_bounds__(kRouteThreads) void route_count_kernel(RouteArgs a, Shape s) {
+__global__ __launch_bounds__(kRouteThreads) void route_count_kernel(RouteArgs a, Shape s,
+                                                                   int64_t tile, int tiles) {
     __shared__ int rows[kRouteWaves][kMaxE];
     const int tid = threadIdx.x, wave = tid / kWave;
     for (int e = tid; e < s.E; e += kRouteThreads)
 #pragma unroll
         for (int w = 0; w < kRouteWaves; ++w) rows[w][e] = 0;
     __syncthreads();
-    const int64_t t0 = (int64_t)blockIdx.x * kTile;
-    const int64_t t1 = t0 + kTile < s.n ? t0 + kTile : s.n;
+    const int64_t t0 = (int64_t)blockIdx.x * tile;
+    const int64_t t1 = t0 + tile < s.n ? t0 + tile : s.n;
     int64_t w0, w1;
     wave_stretch(t0, t1, wave, w0, w1);
     count_stretch<IdT>(static_cast<const IdT*>(a.ids), w0, w1, s, rows[wave]);
     __syncthreads();
-    int32_t* out = a.workspace + (int64_t)blockIdx.x * s.E;
     for (int e = tid; e < s.E; e += kRouteThreads) {
         int sum = 0;
 #pragma unroll
         for (int w = 0; w < kRouteWaves; ++w) sum += rows[w][e];
-        out[e] = sum;
-    }
-}
-
-// One workgroup: expert totals over the tiles, the metadata, and each tile's
-// first row per expert (replacing the tile totals in the workspace).  The
-// expert counts go to workspace[tiles * E + e] for the scatter pass.
-__global__ __launch_bounds__(kScanThreads) void route_scan_kernel(RouteArgs a, Shape s,
-                                                                  int tiles) {
-    __shared__ int part[kScanThreads];
-    __shared__ int cnt[kMaxE];
-    __shared__ int off[kMaxE];
-    __shared__ int tmp[160];
-    const int tid = threadIdx.x, E = s.E;
-    int slices = kScanThreads / E;
-    if (slices < 1) slices = 1;
-    if (slices > tiles) slices = tiles;
-    int32_t* hist = a.workspace;
-    const int e = tid % E, sl = tid / E;
-    const bool active = tid < slices * E;
-    const int b0 = active ? (int)((int64_t)tiles * sl / slices) : 0;
-    const int b1 = active ? (int)((int64_t)tiles * (sl + 1) / slices) : 0;
-    if (active) {
-        int sum = 0;
-        int b = b0;
-        for (; b + 8 <= b1; b += 8) {
-            int v[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) v[u] = hist[(int64_t)(b + u) * E + e];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) sum += v[u];
-        }
-        for (; b < b1; ++b) sum += hist[(int64_t)b * E + e];
-        part[sl * E + e] = sum;
-    }
-    __syncthreads();
-    for (int x = tid; x < E; x += kScanThreads) {
-        int run = 0;
-        for (int q = 0; q < slices; ++q) {
-            const int c = part[q * E + x];
-            part[q * E + x] = run;
-            run += c;
-        }
-        cnt[x] = run;
-    }
-    __syncthreads();
-    scan_experts(a, cnt, off, tmp);
-    __syncthreads();
-    for (int x = tid; x < E; x += kScanThreads) hist[(int64_t)tiles * E + x] = cnt[x];
-    if (active) {
-        int run = off[e] + part[sl * E + e];
-        for (int b = b0; b < b1; ++b) {
-            const int64_t idx = (int64_t)b * E + e;
-            const int c = hist[idx];
-            hist[idx] = run;
-            run += c;
-        }
+        a.workspace[(int64_t)e * round_up_i(tiles, 4) + blockIdx.x] = sum;
     }
 }
 
 template <typename IdT>
 __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(RouteArgs a, Shape s,
-                                                                      int tiles) {
+                                                                      int64_t tile, int tiles) {
     __shared__ int rows[kRouteWaves][kMaxE];
+    __shared__ int cnt[kMaxE];
+    __shared__ int off[kMaxE];
+    __shared__ int pre[kMaxE];
+    __shared__ int tmp[160];
     const int tid = threadIdx.x, wave = tid / kWave;
+    const int b = blockIdx.x;
     const IdT* ids = static_cast<const IdT*>(a.ids);
+    const int64_t t0 = (int64_t)b * tile;
+    const int64_t t1 = t0 + tile < s.n ? t0 + tile : s.n;
+    int64_t w0, w1;
+    wave_stretch(t0, t1, wave, w0, w1);
+    // A stretch of at most one round keeps its keys in registers for both
+    // passes; they are requested first so their latency overlaps the table.
+    const bool one_round = w1 - w0 <= kBatch * kWave;
+    int key[kBatch];
+    if (one_round) load_keys(ids, w0, w1, s.E, key);
+
+    // Expert totals over all tiles and this tile's prefix: a thread per expert
+    // reads the expert's row of the count table with 16-byte loads, issued
+    // together (the row stride is a multiple of 4 tiles).
+    const int stride = round_up_i(tiles, 4);
+    for (int e = tid; e < s.E; e += kRouteThreads) {
+        const u32x4* row = reinterpret_cast<const u32x4*>(a.workspace + (int64_t)e * stride);
+        int tot = 0, before = 0;
+        for (int q0 = 0; q0 < stride / 4; q0 += kTableBatch) {
+            u32x4 v[kTableBatch];
+#pragma unroll
+            for (int u = 0; u < kTableBatch; ++u)
+                if (q0 + u < stride / 4) v[u] = row[q0 + u];
+#pragma unroll
+            for (int u = 0; u < kTableBatch; ++u) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int g = (q0 + u) * 4 + c;
+                    const int x = g < tiles ? (int)v[u][c] : 0;
+                    tot += x;
+                    before += g < b ? x : 0;
+                }
+            }
+        }
+        cnt[e] = tot;
+        pre[e] = before;
+    }
     for (int e = tid; e < s.E; e += kRouteThreads)
 #pragma unroll
         for (int w = 0; w < kRouteWaves; ++w) rows[w][e] = 0;
     __syncthreads();
-    const int64_t t0 = (int64_t)blockIdx.x * kTile;
-    const int64_t t1 = t0 + kTile < s.n ? t0 + kTile : s.n;
-    int64_t w0, w1;
-    wave_stretch(t0, t1, wave, w0, w1);
-    count_stretch<IdT>(ids, w0, w1, s, rows[wave]);
+    const int R = scan_experts(a, cnt, off, tmp, b == 0);
+    if (one_round) count_keys(key, s, rows[wave]);
+    else count_stretch<IdT>(ids, w0, w1, s, rows[wave]);
     __syncthreads();
-    const int32_t* base = a.workspace + (int64_t)blockIdx.x * s.E;
     for (int e = tid; e < s.E; e += kRouteThreads) {
-        int run = base[e];
+        int run = off[e] + pre[e];
 #pragma unroll
         for (int w = 0; w < kRouteWaves; ++w) {
             const int c = rows[w][e];
@@ -317,14 +347,13 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(RouteArgs 
         }
     }
     __syncthreads();
-    scatter_stretch<IdT>(ids, w0, w1, s, rows[wave], a.output_perm, a.input_perm,
-                         a.input_perm_len);
-    // Unused rows: counts from the workspace, segment starts from expert_offsets.
-    const int32_t* cnt = a.workspace + (int64_t)tiles * s.E;
-    const int R = a.expert_offsets[s.E];
-    fill_unused_rows(a, cnt, a.expert_offsets, R, blockIdx.x * kRouteWaves + wave,
-                     tiles * kRouteWaves, (int64_t)blockIdx.x * kRouteThreads + tid,
-                     (int64_t)tiles * kRouteThreads);
+    if (one_round)
+        scatter_keys(key, w0, w1, s, rows[wave], a.output_perm, a.input_perm, a.input_perm_len);
+    else
+        scatter_stretch<IdT>(ids, w0, w1, s, rows[wave], a.output_perm, a.input_perm,
+                             a.input_perm_len);
+    fill_unused_rows(a, cnt, off, R, b * kRouteWaves + wave, tiles * kRouteWaves,
+                     (int64_t)b * kRouteThreads + tid, (int64_t)tiles * kRouteThreads);
 }
 
 int id_bits(int E) { return E <= 1 ? 0 : 32 - __builtin_clz((unsigned)(E - 1)); }
@@ -336,14 +365,12 @@ hipError_t launch_typed(const RouteArgs& a, hipStream_t stream) {
         route_fused_kernel<IdT><<<1, kRouteThreads, 0, stream>>>(a, s);
         return hipGetLastError();
     }
-    const int tiles = (int)((a.num_picks + kTile - 1) / kTile);
-    route_count_kernel<IdT><<<tiles, kRouteThreads, 0, stream>>>(a, s);
+    const int64_t tile = tile_picks(a.num_picks);
+    const int tiles = (int)((a.num_picks + tile - 1) / tile);
+    route_count_kernel<IdT><<<tiles, kRouteThreads, 0, stream>>>(a, s, tile, tiles);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    route_scan_kernel<<<1, kScanThreads, 0, stream>>>(a, s, tiles);
-    err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    route_scatter_kernel<IdT><<<tiles, kRouteThreads, 0, stream>>>(a, s, tiles);
+    route_scatter_kernel<IdT><<<tiles, kRouteThreads, 0, stream>>>(a, s, tile, tiles);
     return hipGetLastError();
 }
 
@@ -351,8 +378,9 @@ hipError_t launch_typed(const RouteArgs& a, hipStream_t stream) {
 
 size_t route_workspace_bytes(int64_t num_picks, int32_t num_experts) {
     if (num_picks <= kFusedMax) return 0;
-    const int64_t tiles = (num_picks + kTile - 1) / kTile;
-    return (size_t)((tiles + 1) * (int64_t)num_experts * (int64_t)sizeof(int32_t));
+    const int64_t tile = tile_picks(num_picks);
+    const int64_t tiles = (num_picks + tile - 1) / tile;
+    return (size_t)((tiles + 3) / 4 * 4 * (int64_t)num_experts * (int64_t)sizeof(int32_t));
 }
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t stream) {

@@ -6,7 +6,8 @@
 //
 // Both are HBM-bound byte copies.  A workgroup owns one row (or a column
 // chunk of one row); each thread loads its kUnroll vectors of a round before
-// storing any, so a wave keeps kUnroll KiB of 16-byte reads in flight.  Rows
+// storing any, so a wave keeps kUnroll KiB of 16-byte reads in flight, and
+// the write-once destination rows are stored with the non-temporal hint.  Rows
 // whose byte width or base pointers are not multiples of 16 fall back to the
 // widest access width that divides them.
 #include "device_common.h"
@@ -18,12 +19,23 @@ namespace {
 constexpr int kRowThreads = 256;
 constexpr int kUnroll = 4;
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
 template <int V> struct Vec;
-template <> struct Vec<16> { using T = uint4; };
-template <> struct Vec<8> { using T = uint2; };
+template <> struct Vec<16> { using T = u32x4; };
+template <> struct Vec<8> { using T = u32x2; };
 template <> struct Vec<4> { using T = uint32_t; };
 template <> struct Vec<2> { using T = uint16_t; };
 template <> struct Vec<1> { using T = uint8_t; };
+
+// Destination rows are written once and not read again by this pass, so
+// stores carry the non-temporal hint (streamed past the caches instead of
+// displacing data still to be read).
+template <typename T>
+__device__ __forceinline__ void put(T* p, T v) {
+    __builtin_nontemporal_store(v, p);
+}
 
 // Copies columns [c0, c1) of one row (vectors of T) to each destination row
 // rows[0..n) that lies in [0, num_dst_rows); with rows == nullptr the only
@@ -61,15 +73,15 @@ __device__ __forceinline__ void copy_row_to(const T* __restrict__ in, int64_t c0
                 if (r < 0) continue;
                 T* out = reinterpret_cast<T*>(dst + (int64_t)r * row_bytes);
                 if (full) {
-                    out[c] = v0;
-                    out[c + kRowThreads] = v1;
-                    out[c + 2 * kRowThreads] = v2;
-                    out[c + 3 * kRowThreads] = v3;
+                    put(out + c, v0);
+                    put(out + c + kRowThreads, v1);
+                    put(out + c + 2 * kRowThreads, v2);
+                    put(out + c + 3 * kRowThreads, v3);
                 } else {
-                    if (c < c1) out[c] = v0;
-                    if (c + kRowThreads < c1) out[c + kRowThreads] = v1;
-                    if (c + 2 * kRowThreads < c1) out[c + 2 * kRowThreads] = v2;
-                    if (c + 3 * kRowThreads < c1) out[c + 3 * kRowThreads] = v3;
+                    if (c < c1) put(out + c, v0);
+                    if (c + kRowThreads < c1) put(out + c + kRowThreads, v1);
+                    if (c + 2 * kRowThreads < c1) put(out + c + 2 * kRowThreads, v2);
+                    if (c + 3 * kRowThreads < c1) put(out + c + 3 * kRowThreads, v3);
                 }
             }
         }
