@@ -9,6 +9,9 @@
 namespace {
 
 constexpr int64_t kMax31 = (int64_t)0x7fffffff;
+// Rows are cut into column chunks of at most 1024 accesses (gridDim.y <= 65535);
+// with 1-byte accesses that bounds a row at 65535 * 1024 bytes.
+constexpr int64_t kMaxRowBytes = (int64_t)65535 * 1024;
 thread_local int g_last_hip_error = 0;
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -124,8 +127,8 @@ mx_status mx_prepare_moe_input(const void* topk_ids, int32_t ids_dtype, int64_t 
 mx_status mx_shuffle_rows(const void* src, int64_t num_src_rows, int64_t row_bytes,
                           const int32_t* dst2src, int64_t num_dst_rows, void* dst,
                           void* stream) {
-    if (num_src_rows < 0 || num_dst_rows < 0 || row_bytes < 1 || num_src_rows > kMax31 ||
-        num_dst_rows > kMax31)
+    if (num_src_rows < 0 || num_dst_rows < 0 || row_bytes < 1 || row_bytes > kMaxRowBytes ||
+        num_src_rows > kMax31 || num_dst_rows > kMax31)
         return MX_ERR_INVALID_ARGUMENT;
     if (num_dst_rows > 0 && (dst2src == nullptr || dst == nullptr ||
                              (num_src_rows > 0 && src == nullptr)))
@@ -141,8 +144,8 @@ mx_status mx_dispatch_rows(const void* src, int64_t num_tokens, int32_t topk, in
                            const int32_t* output_permutation, void* dst, int64_t num_dst_rows,
                            const void* side_src, int64_t side_row_bytes, void* side_dst,
                            void* stream) {
-    if (num_tokens < 0 || topk < 1 || row_bytes < 1 || num_dst_rows < 0 ||
-        num_dst_rows > kMax31 || num_tokens > kMax31 / topk)
+    if (num_tokens < 0 || topk < 1 || row_bytes < 1 || row_bytes > kMaxRowBytes ||
+        num_dst_rows < 0 || num_dst_rows > kMax31 || num_tokens > kMax31 / topk)
         return MX_ERR_INVALID_ARGUMENT;
     const bool side = side_src != nullptr || side_dst != nullptr;
     if (side && (side_src == nullptr || side_dst == nullptr || side_row_bytes < 1))

@@ -5,9 +5,11 @@
 // each of its k dispatched rows.
 //
 // Both are HBM-bound byte copies.  A workgroup owns one row (or a column
-// chunk of one row); each thread loads its kUnroll vectors of a round before
-// storing any, so a wave keeps kUnroll KiB of 16-byte reads in flight, and
-// the write-once destination rows are stored with the non-temporal hint.  Rows
+// chunk of at most 1024 vectors of one row) and each thread moves exactly one
+// 16-byte vector: one load, then one store per destination.  Short-lived
+// workgroups with one access per thread sustained the highest write rate on
+// MI355X (several accesses per thread, or looping workgroups, wrote slower),
+// and the write-once destination rows are stored with the non-temporal hint.  Rows
 // whose byte width or base pointers are not multiples of 16 fall back to the
 // widest access width that divides them.
 #include "device_common.h"
@@ -16,8 +18,7 @@
 namespace mxmoe {
 namespace {
 
-constexpr int kRowThreads = 256;
-constexpr int kUnroll = 4;
+constexpr int kMaxRowThreads = 1024;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -29,103 +30,73 @@ template <> struct Vec<4> { using T = uint32_t; };
 template <> struct Vec<2> { using T = uint16_t; };
 template <> struct Vec<1> { using T = uint8_t; };
 
-// Destination rows are written once and not read again by this pass, so
-// stores carry the non-temporal hint (streamed past the caches instead of
-// displacing data still to be read).
-template <typename T>
-__device__ __forceinline__ void put(T* p, T v) {
-    __builtin_nontemporal_store(v, p);
-}
-
-// Copies columns [c0, c1) of one row (vectors of T) to each destination row
+// Copies vector c of one row (vectors of T) to each destination row
 // rows[0..n) that lies in [0, num_dst_rows); with rows == nullptr the only
-// destination is `single_row`.  The column rounds and the
-// destination loop are uniform across the workgroup, so the destination
-// indices sit one per lane and are broadcast with readlane.
+// destination is `single_row`.  Threads past the row end (c >= nvec) take
+// part in the wave-uniform destination loop but access nothing.  The
+// destination indices sit one per lane and are broadcast with readlane;
+// destination rows are written once and not read again by this pass, so the
+// stores carry the non-temporal hint.
 template <typename T>
-__device__ __forceinline__ void copy_row_to(const T* __restrict__ in, int64_t c0, int64_t c1,
-                                            uint8_t* __restrict__ dst, int64_t row_bytes,
-                                            const int32_t* __restrict__ rows, int n,
-                                            int64_t num_dst_rows, int32_t single_row = -1) {
+__device__ __forceinline__ void copy_vector_to(const T* __restrict__ in, int64_t c, int64_t nvec,
+                                               uint8_t* __restrict__ dst, int64_t row_bytes,
+                                               const int32_t* __restrict__ rows, int n,
+                                               int64_t num_dst_rows, int32_t single_row = -1) {
     const int lane = threadIdx.x & (kWave - 1);
-    constexpr int64_t kStep = (int64_t)kRowThreads * kUnroll;
-    for (int64_t b = c0; b < c1; b += kStep) {
-        const int64_t c = b + threadIdx.x;
-        const bool full = b + kStep <= c1;
-        T v0{}, v1{}, v2{}, v3{};
-        if (full) {
-            v0 = in[c];
-            v1 = in[c + kRowThreads];
-            v2 = in[c + 2 * kRowThreads];
-            v3 = in[c + 3 * kRowThreads];
-        } else {
-            if (c < c1) v0 = in[c];
-            if (c + kRowThreads < c1) v1 = in[c + kRowThreads];
-            if (c + 2 * kRowThreads < c1) v2 = in[c + 2 * kRowThreads];
-            if (c + 3 * kRowThreads < c1) v3 = in[c + 3 * kRowThreads];
-        }
-        for (int j0 = 0; j0 < n; j0 += kWave) {
-            const int nj = n - j0 < kWave ? n - j0 : kWave;
-            int my_r = lane < nj ? (rows ? rows[j0 + lane] : single_row) : -1;
-            if (my_r >= num_dst_rows) my_r = -1;
-            for (int j = 0; j < nj; ++j) {
-                const int32_t r = __builtin_amdgcn_readlane(my_r, j);
-                if (r < 0) continue;
-                T* out = reinterpret_cast<T*>(dst + (int64_t)r * row_bytes);
-                if (full) {
-                    put(out + c, v0);
-                    put(out + c + kRowThreads, v1);
-                    put(out + c + 2 * kRowThreads, v2);
-                    put(out + c + 3 * kRowThreads, v3);
-                } else {
-                    if (c < c1) put(out + c, v0);
-                    if (c + kRowThreads < c1) put(out + c + kRowThreads, v1);
-                    if (c + 2 * kRowThreads < c1) put(out + c + 2 * kRowThreads, v2);
-                    if (c + 3 * kRowThreads < c1) put(out + c + 3 * kRowThreads, v3);
-                }
-            }
+    const bool live = c < nvec;
+    T v{};
+    if (live) v = in[c];
+    for (int j0 = 0; j0 < n; j0 += kWave) {
+        const int nj = n - j0 < kWave ? n - j0 : kWave;
+        int my_r = lane < nj ? (rows ? rows[j0 + lane] : single_row) : -1;
+        if (my_r >= num_dst_rows) my_r = -1;
+        for (int j = 0; j < nj; ++j) {
+            const int32_t r = __builtin_amdgcn_readlane(my_r, j);
+            if (r < 0) continue;
+            if (live) __builtin_nontemporal_store(v, reinterpret_cast<T*>(dst + (int64_t)r * row_bytes) + c);
         }
     }
 }
 
-// dst[r] = src[dst2src[r]] for the column chunk blockIdx.y of row blockIdx.x.
+// dst[r] = src[dst2src[r]]: workgroup (blockIdx.x = r, blockIdx.y = column
+// chunk), one vector per thread.
 template <int V>
-__global__ __launch_bounds__(kRowThreads) void shuffle_rows_kernel(
+__global__ __launch_bounds__(kMaxRowThreads) void shuffle_rows_kernel(
     const uint8_t* __restrict__ src, int64_t num_src_rows, int64_t row_bytes,
-    const int32_t* __restrict__ dst2src, uint8_t* __restrict__ dst, int64_t chunk_vecs) {
+    const int32_t* __restrict__ dst2src, uint8_t* __restrict__ dst) {
     using T = typename Vec<V>::T;
     const int32_t r = (int32_t)blockIdx.x;
     const int32_t s = dst2src[r];
     if (s < 0 || s >= num_src_rows) return;
-    const int64_t nvec = row_bytes / V;
-    const int64_t c0 = (int64_t)blockIdx.y * chunk_vecs;
-    const int64_t c1 = c0 + chunk_vecs < nvec ? c0 + chunk_vecs : nvec;
+    const int64_t c = (int64_t)blockIdx.y * blockDim.x + threadIdx.x;
     const T* in = reinterpret_cast<const T*>(src + (int64_t)s * row_bytes);
-    copy_row_to<T>(in, c0, c1, dst, row_bytes, nullptr, 1, (int64_t)r + 1, r);
+    copy_vector_to<T>(in, c, row_bytes / V, dst, row_bytes, nullptr, 1, (int64_t)r + 1, r);
 }
 
-// dst[output_perm[t*k + j]] = src[t] for the column chunk blockIdx.y of token
-// blockIdx.x and every j; the side row (if any) goes with chunk 0.
+// dst[output_perm[t*k + j]] = src[t] for every j: workgroup (blockIdx.x =
+// token t, blockIdx.y = column chunk), one vector per thread; the side row
+// (if any) goes with chunk 0.
 template <int V, int SV>
-__global__ __launch_bounds__(kRowThreads) void dispatch_rows_kernel(
+__global__ __launch_bounds__(kMaxRowThreads) void dispatch_rows_kernel(
     const uint8_t* __restrict__ src, int64_t row_bytes, int32_t topk,
     const int32_t* __restrict__ output_perm, uint8_t* __restrict__ dst, int64_t num_dst_rows,
-    int64_t chunk_vecs, const uint8_t* __restrict__ side_src, int64_t side_row_bytes,
+    const uint8_t* __restrict__ side_src, int64_t side_row_bytes,
     uint8_t* __restrict__ side_dst) {
     using T = typename Vec<V>::T;
     const int64_t t = blockIdx.x;
     const int32_t* rows = output_perm + t * topk;
-    const int64_t nvec = row_bytes / V;
-    const int64_t c0 = (int64_t)blockIdx.y * chunk_vecs;
-    const int64_t c1 = c0 + chunk_vecs < nvec ? c0 + chunk_vecs : nvec;
-    copy_row_to<T>(reinterpret_cast<const T*>(src + t * row_bytes), c0, c1, dst, row_bytes, rows,
-                   topk, num_dst_rows);
+    const int64_t c = (int64_t)blockIdx.y * blockDim.x + threadIdx.x;
+    copy_vector_to<T>(reinterpret_cast<const T*>(src + t * row_bytes), c, row_bytes / V, dst,
+                      row_bytes, rows, topk, num_dst_rows);
     if constexpr (SV > 0) {
         using S = typename Vec<SV>::T;
-        if (blockIdx.y == 0)
-            copy_row_to<S>(reinterpret_cast<const S*>(side_src + t * side_row_bytes), 0,
-                           side_row_bytes / SV, side_dst, side_row_bytes, rows, topk,
-                           num_dst_rows);
+        if (blockIdx.y == 0) {
+            const int64_t ns = side_row_bytes / SV;
+            for (int64_t c0 = 0; c0 < ns; c0 += blockDim.x)
+                copy_vector_to<S>(reinterpret_cast<const S*>(side_src + t * side_row_bytes),
+                                  c0 + threadIdx.x, ns, side_dst, side_row_bytes, rows, topk,
+                                  num_dst_rows);
+        }
     }
 }
 
@@ -136,26 +107,28 @@ int vec_width(int64_t row_bytes, const void* a, const void* b) {
     return 1;
 }
 
-// Column chunking: a workgroup covers at most kRowThreads * kUnroll * 4
-// vectors of a row; longer rows are split over gridDim.y.
-void row_grid(int64_t rows, int64_t row_bytes, int v, dim3& grid, int64_t& chunk_vecs) {
+// Launch shape: one vector per thread; a row of nvec vectors is cut into the
+// fewest column chunks of at most kMaxRowThreads vectors, and the workgroup
+// width is the chunk rounded up to whole waves.
+void row_grid(int64_t rows, int64_t row_bytes, int v, dim3& grid, dim3& block) {
     const int64_t nvec = row_bytes / v;
-    const int64_t max_chunk = (int64_t)kRowThreads * kUnroll * 4;
-    const int64_t chunks = (nvec + max_chunk - 1) / max_chunk;
-    chunk_vecs = (nvec + chunks - 1) / chunks;
+    const int64_t chunks = (nvec + kMaxRowThreads - 1) / kMaxRowThreads;
+    int64_t threads = (nvec + chunks - 1) / chunks;
+    threads = (threads + kWave - 1) / kWave * kWave;
     grid = dim3((unsigned)rows, (unsigned)chunks, 1);
+    block = dim3((unsigned)threads, 1, 1);
 }
 
 template <int V>
-hipError_t launch_dispatch_v(dim3 grid, int side_vec, const uint8_t* s, int64_t row_bytes,
-                             int32_t topk, const int32_t* output_perm, uint8_t* d,
-                             int64_t num_dst_rows, int64_t chunk, const uint8_t* ss,
+hipError_t launch_dispatch_v(dim3 grid, dim3 block, int side_vec, const uint8_t* s,
+                             int64_t row_bytes, int32_t topk, const int32_t* output_perm,
+                             uint8_t* d, int64_t num_dst_rows, const uint8_t* ss,
                              int64_t side_row_bytes, uint8_t* sd, hipStream_t stream) {
     switch (side_vec) {
-    case 0: dispatch_rows_kernel<V, 0><<<grid, kRowThreads, 0, stream>>>(s, row_bytes, topk, output_perm, d, num_dst_rows, chunk, ss, side_row_bytes, sd); break;
-    case 16: dispatch_rows_kernel<V, 16><<<grid, kRowThreads, 0, stream>>>(s, row_bytes, topk, output_perm, d, num_dst_rows, chunk, ss, side_row_bytes, sd); break;
-    case 4: dispatch_rows_kernel<V, 4><<<grid, kRowThreads, 0, stream>>>(s, row_bytes, topk, output_perm, d, num_dst_rows, chunk, ss, side_row_bytes, sd); break;
-    default: dispatch_rows_kernel<V, 1><<<grid, kRowThreads, 0, stream>>>(s, row_bytes, topk, output_perm, d, num_dst_rows, chunk, ss, side_row_bytes, sd); break;
+    case 0: dispatch_rows_kernel<V, 0><<<grid, block, 0, stream>>>(s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd); break;
+    case 16: dispatch_rows_kernel<V, 16><<<grid, block, 0, stream>>>(s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd); break;
+    case 4: dispatch_rows_kernel<V, 4><<<grid, block, 0, stream>>>(s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd); break;
+    default: dispatch_rows_kernel<V, 1><<<grid, block, 0, stream>>>(s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd); break;
     }
     return hipGetLastError();
 }
@@ -167,17 +140,16 @@ hipError_t launch_shuffle_rows(const void* src, int64_t num_src_rows, int64_t ro
                                hipStream_t stream) {
     if (num_dst_rows == 0) return hipSuccess;
     const int v = vec_width(row_bytes, src, dst);
-    dim3 grid;
-    int64_t chunk;
-    row_grid(num_dst_rows, row_bytes, v, grid, chunk);
+    dim3 grid, block;
+    row_grid(num_dst_rows, row_bytes, v, grid, block);
     const uint8_t* s = static_cast<const uint8_t*>(src);
     uint8_t* d = static_cast<uint8_t*>(dst);
     switch (v) {
-    case 16: shuffle_rows_kernel<16><<<grid, kRowThreads, 0, stream>>>(s, num_src_rows, row_bytes, dst2src, d, chunk); break;
-    case 8: shuffle_rows_kernel<8><<<grid, kRowThreads, 0, stream>>>(s, num_src_rows, row_bytes, dst2src, d, chunk); break;
-    case 4: shuffle_rows_kernel<4><<<grid, kRowThreads, 0, stream>>>(s, num_src_rows, row_bytes, dst2src, d, chunk); break;
-    case 2: shuffle_rows_kernel<2><<<grid, kRowThreads, 0, stream>>>(s, num_src_rows, row_bytes, dst2src, d, chunk); break;
-    default: shuffle_rows_kernel<1><<<grid, kRowThreads, 0, stream>>>(s, num_src_rows, row_bytes, dst2src, d, chunk); break;
+    case 16: shuffle_rows_kernel<16><<<grid, block, 0, stream>>>(s, num_src_rows, row_bytes, dst2src, d); break;
+    case 8: shuffle_rows_kernel<8><<<grid, block, 0, stream>>>(s, num_src_rows, row_bytes, dst2src, d); break;
+    case 4: shuffle_rows_kernel<4><<<grid, block, 0, stream>>>(s, num_src_rows, row_bytes, dst2src, d); break;
+    case 2: shuffle_rows_kernel<2><<<grid, block, 0, stream>>>(s, num_src_rows, row_bytes, dst2src, d); break;
+    default: shuffle_rows_kernel<1><<<grid, block, 0, stream>>>(s, num_src_rows, row_bytes, dst2src, d); break;
     }
     return hipGetLastError();
 }
@@ -193,19 +165,18 @@ hipError_t launch_dispatch_rows(const void* src, int64_t num_tokens, int32_t top
         const int sv = vec_width(side_row_bytes, side_src, side_dst);
         side_vec = sv >= 16 ? 16 : sv >= 4 ? 4 : 1;
     }
-    dim3 grid;
-    int64_t chunk;
-    row_grid(num_tokens, row_bytes, v, grid, chunk);
+    dim3 grid, block;
+    row_grid(num_tokens, row_bytes, v, grid, block);
     const uint8_t* s = static_cast<const uint8_t*>(src);
     uint8_t* d = static_cast<uint8_t*>(dst);
     const uint8_t* ss = static_cast<const uint8_t*>(side_src);
     uint8_t* sd = static_cast<uint8_t*>(side_dst);
     switch (v) {
-    case 16: return launch_dispatch_v<16>(grid, side_vec, s, row_bytes, topk, output_perm, d, num_dst_rows, chunk, ss, side_row_bytes, sd, stream);
-    case 8: return launch_dispatch_v<8>(grid, side_vec, s, row_bytes, topk, output_perm, d, num_dst_rows, chunk, ss, side_row_bytes, sd, stream);
-    case 4: return launch_dispatch_v<4>(grid, side_vec, s, row_bytes, topk, output_perm, d, num_dst_rows, chunk, ss, side_row_bytes, sd, stream);
-    case 2: return launch_dispatch_v<2>(grid, side_vec, s, row_bytes, topk, output_perm, d, num_dst_rows, chunk, ss, side_row_bytes, sd, stream);
-    default: return launch_dispatch_v<1>(grid, side_vec, s, row_bytes, topk, output_perm, d, num_dst_rows, chunk, ss, side_row_bytes, sd, stream);
+    case 16: return launch_dispatch_v<16>(grid, block, side_vec, s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd, stream);
+    case 8: return launch_dispatch_v<8>(grid, block, side_vec, s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd, stream);
+    case 4: return launch_dispatch_v<4>(grid, block, side_vec, s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd, stream);
+    case 2: return launch_dispatch_v<2>(grid, block, side_vec, s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd, stream);
+    default: return launch_dispatch_v<1>(grid, block, side_vec, s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd, stream);
     }
 }
 

@@ -135,7 +135,8 @@ mx_status mx_prepare_moe_input(const void* topk_ids, int32_t ids_dtype, int64_t 
  *
  * Rows with dst2src[r] outside [0, num_src_rows) are left untouched.
  * src [num_src_rows, row_bytes], dst [num_dst_rows, row_bytes], any element
- * type; dst2src [num_dst_rows] int32 (e.g. input_permutation).  row_bytes >= 1.
+ * type; dst2src [num_dst_rows] int32 (e.g. input_permutation).
+ * 1 <= row_bytes <= 65535 * 1024.
  * Copies use 16-byte accesses when row_bytes and both base pointers are
  * multiples of 16, else the widest width that divides all three.
  */
@@ -154,7 +155,8 @@ mx_status mx_shuffle_rows(const void* src, int64_t num_src_rows, int64_t row_byt
  * copied the same way: side_dst[output_permutation[t*k+j]] = side_src[t]
  * (pass side_src = side_dst = NULL and side_row_bytes = 0 to skip).
  * src [T, row_bytes], dst [num_dst_rows, row_bytes], side arrays
- * [*, side_row_bytes]; output_permutation [T*k] int32.
+ * [*, side_row_bytes]; output_permutation [T*k] int32;
+ * 1 <= row_bytes <= 65535 * 1024.
  */
 mx_status mx_dispatch_rows(const void* src, int64_t num_tokens, int32_t topk, int64_t row_bytes,
                            const int32_t* output_permutation, void* dst, int64_t num_dst_rows,

@@ -93,6 +93,7 @@ def test_shuffle_rejects(lib):
     assert f(P, 10, 16, None, 10, P, S) == INVALID
     assert f(P, 10, 16, P, 10, None, S) == INVALID
     assert f(P, 10, 16, P + 2, 10, P, S) == MISALIGNED
+    assert f(P, 10, 65535 * 1024 + 1, P, 10, P, S) == INVALID
     assert f(P, 10, 16, P, 0, P, S) == OK            # nothing to do, nothing launched
 
 
@@ -100,6 +101,7 @@ def test_dispatch_rejects(lib):
     f = lib.mx_dispatch_rows
     assert f(P, 10, 0, 16, P, P, 80, None, 0, None, S) == INVALID
     assert f(P, 10, 8, 0, P, P, 80, None, 0, None, S) == INVALID
+    assert f(P, 10, 8, 65535 * 1024 + 1, P, P, 80, None, 0, None, S) == INVALID
     assert f(P, 10, 8, 16, P, P, 80, P, 0, P, S) == INVALID          # side rows of 0 bytes
     assert f(P, 10, 8, 16, P, P, 80, P, 16, None, S) == INVALID      # side without destination
     assert f(P, 10, 8, 16, P, P, 80, None, 16, None, S) == INVALID   # side bytes without arrays
