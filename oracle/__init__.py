@@ -31,7 +31,7 @@ def build(out_path: str | None = None, src_path: str | None = None) -> str:
     """Compile the oracle with gcc; returns the library path."""
     out_path = out_path or _LIB_PATH
     src_path = src_path or _SRC
-    tmp = out_path + ".tmp"
+    tmp = f"{out_path}.{os.getpid()}.tmp"
     cmd = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c11", "-Wall",
            "-Werror", "-fPIC", "-shared", src_path, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
@@ -67,6 +67,12 @@ def _declare(lib):
     lib.oracle_apply_shuffle_mul_sum.argtypes = [
         ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, c_i32p, ctypes.c_void_p, ctypes.c_int,
         ctypes.c_int64, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int]
+    lib.oracle_output_memset.restype = None
+    lib.oracle_output_memset.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                         ctypes.c_int64, c_i32p]
+    lib.oracle_zero_padding_rows.restype = None
+    lib.oracle_zero_padding_rows.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                             c_i32p, c_i32p, ctypes.c_int32]
     for name in ("oracle_f32_to_bf16", "oracle_f32_to_f16"):
         getattr(lib, name).restype = ctypes.c_uint16
         getattr(lib, name).argtypes = [ctypes.c_float]
@@ -164,6 +170,36 @@ def apply_shuffle_mul_sum(y: np.ndarray, y_dtype: str, permutation: np.ndarray,
         f.ctypes.data if f is not None else None, DTYPES[factors_dtype], T, k, H,
         out.ctypes.data, DTYPES[out_dtype])
     return out
+
+
+def _row_bytes(a: np.ndarray) -> int:
+    return int(np.prod(a.shape[1:], dtype=np.int64)) * a.itemsize
+
+
+def output_memset(out: np.ndarray, topk: int, expanded_to_permuted: np.ndarray,
+                  lib=None) -> np.ndarray:
+    """In place on a copy of ``out`` [T, ...]: row t becomes zero bytes iff one
+    of its picks has a permuted index >= 0.  Returns the new array."""
+    lib = lib or load()
+    res = np.ascontiguousarray(out).copy()
+    perm = np.ascontiguousarray(expanded_to_permuted, dtype=np.int32)
+    assert perm.size == len(res) * topk
+    lib.oracle_output_memset(res.ctypes.data, len(res), topk, _row_bytes(res), _i32p(perm))
+    return res
+
+
+def zero_padding_rows(rows: np.ndarray, input_permutation: np.ndarray,
+                      expert_offsets: np.ndarray | None = None, lib=None) -> np.ndarray:
+    """On a copy of ``rows`` [R, ...]: rows below the padded total whose
+    input_permutation entry is negative become zero bytes."""
+    lib = lib or load()
+    res = np.ascontiguousarray(rows).copy()
+    inp = np.ascontiguousarray(input_permutation, dtype=np.int32)
+    assert inp.size >= len(res)
+    eo = None if expert_offsets is None else np.ascontiguousarray(expert_offsets, dtype=np.int32)
+    lib.oracle_zero_padding_rows(res.ctypes.data, len(res), _row_bytes(res), _i32p(inp),
+                                 _i32p(eo), 0 if eo is None else eo.size - 1)
+    return res
 
 
 def f32_to_bf16(x: np.ndarray, lib=None) -> np.ndarray:

@@ -243,3 +243,33 @@ void oracle_apply_shuffle_mul_sum(const void* y, int y_dtype, int64_t n_rows,
         }
     }
 }
+
+/* ---------------------------------------------------------------------- */
+/* Zeroing rows in place (the output memset of the TensorRT-LLM page        */
+/* "Enable CuteDSL MoE with Large EP", walkthrough and its memset test, and */
+/* the zero-filled padding rows for grouped GEMM tiles).                    */
+/* ---------------------------------------------------------------------- */
+
+/* Output row t (row_bytes bytes) becomes all zero bytes iff at least one of
+ * its k picks has a permuted index >= 0; every other row is left as it is. */
+void oracle_output_memset(uint8_t* out, int64_t T, int32_t k, int64_t row_bytes,
+                          const int32_t* expanded_to_permuted) {
+    for (int64_t t = 0; t < T; ++t) {
+        int any = 0;
+        for (int32_t j = 0; j < k; ++j)
+            if (expanded_to_permuted[t * k + j] >= 0) any = 1;
+        if (any) memset(out + t * row_bytes, 0, (size_t)row_bytes);
+    }
+}
+
+/* Dispatched row r < limit becomes all zero bytes iff input_perm[r] < 0
+ * (a padding row); limit = expert_offsets[E] when expert_offsets is given,
+ * else n_rows.  Rows at or past the limit are left as they are. */
+void oracle_zero_padding_rows(uint8_t* rows, int64_t n_rows, int64_t row_bytes,
+                              const int32_t* input_perm, const int32_t* expert_offsets,
+                              int32_t E) {
+    int64_t limit = expert_offsets ? expert_offsets[E] : n_rows;
+    if (limit > n_rows) limit = n_rows;
+    for (int64_t r = 0; r < limit; ++r)
+        if (input_perm[r] < 0) memset(rows + r * row_bytes, 0, (size_t)row_bytes);
+}

@@ -389,6 +389,56 @@ def pin_conversions(lib):
     np.testing.assert_array_equal(oracle.bf16_to_f32(all16, lib=lib)[finb], bf_ref[finb])
 
 
+# ---------------------------------------------------------------------------
+# zeroing rows in place
+# ---------------------------------------------------------------------------
+
+def _golden_doc(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return yaml.safe_load(f)
+
+
+def pin_golden_zeroing(lib):
+    """Hand-worked output memset and padding zero-fill."""
+    doc = _golden_doc("prepare_small.yaml")
+    for case in doc["memset_cases"]:
+        before = np.array(case["rows_before"], np.float32)
+        k = len(case["output_permutation"]) // len(before)
+        got = oracle.output_memset(before, k, np.array(case["output_permutation"]), lib=lib)
+        np.testing.assert_array_equal(got, np.array(case["rows_after"], np.float32))
+    for case in doc["padding_cases"]:
+        inp = np.array(case["input_permutation"], np.int32)
+        rows = np.arange(1, inp.size + 1, dtype=np.float32)[:, None] * np.ones((1, 3), np.float32)
+        got = oracle.zero_padding_rows(rows, inp, np.array(case["expert_offsets"]), lib=lib)
+        zeroed = np.nonzero((got == 0).all(axis=1))[0]
+        np.testing.assert_array_equal(zeroed, case["zeroed_rows"])
+        np.testing.assert_array_equal(got[(got != 0).any(axis=1)], rows[(got != 0).any(axis=1)])
+
+
+def pin_zeroing_vs_numpy(lib):
+    """Row masks computed with numpy: a token row is zeroed iff any of its
+    picks has an index >= 0; a dispatched row below the padded total is
+    zeroed iff its source index is negative; every other byte is kept."""
+    rng = np.random.default_rng(21)
+    for T, k, W in [(50, 8, 7), (1, 1, 16), (33, 3, 1), (0, 4, 5)]:
+        perm = rng.integers(-1, 30, T * k).astype(np.int32)
+        perm[rng.random(T * k) < 0.5] = -1
+        before = rng.integers(1, 255, (T, W)).astype(np.uint8)
+        got = oracle.output_memset(before, k, perm, lib=lib)
+        mask = (perm.reshape(T, k) >= 0).any(axis=1) if T else np.zeros(0, bool)
+        np.testing.assert_array_equal(got, np.where(mask[:, None], 0, before))
+    for T, E, k, A in [(40, 16, 4, 8), (100, 64, 8, 128), (5, 3, 2, 1)]:
+        ids = routing.uniform_topk(rng, T, E, k)
+        m = oracle.prepare_moe_input(ids, E, row_align=A, lib=lib)
+        inp, eo = m["input_permutation"], m["expert_offsets"]
+        rows = rng.integers(1, 255, (inp.size, 6)).astype(np.uint8)
+        got = oracle.zero_padding_rows(rows, inp, eo, lib=lib)
+        mask = (inp < 0) & (np.arange(inp.size) < eo[-1])
+        np.testing.assert_array_equal(got, np.where(mask[:, None], 0, rows))
+        got = oracle.zero_padding_rows(rows, inp, None, lib=lib)
+        np.testing.assert_array_equal(got, np.where((inp < 0)[:, None], 0, rows))
+
+
 ALL_PINS = [
     pin_golden_prepare,
     pin_prepare_vs_numpy,
@@ -403,6 +453,8 @@ ALL_PINS = [
     pin_combine_f64_bound,
     pin_combine_f16_factors_and_out,
     pin_conversions,
+    pin_golden_zeroing,
+    pin_zeroing_vs_numpy,
 ]
 
 

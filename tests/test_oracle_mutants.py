@@ -48,6 +48,10 @@ MUTANTS = {
                                       "if (s < 0 || s > n_src) continue;"),
     "invalid_id_kept_as_expert0": ("output_perm[i] = -1;\n",
                                    "output_perm[i] = 0;\n"),
+    "memset_needs_all_picks": ("if (expanded_to_permuted[t * k + j] >= 0) any = 1;",
+                               "if (expanded_to_permuted[t * k + j] >= 0) any = 1; else { any = 0; break; }"),
+    "padding_ignores_total": ("int64_t limit = expert_offsets ? expert_offsets[E] : n_rows;",
+                              "int64_t limit = n_rows;"),
 }
 
 
