@@ -56,6 +56,10 @@ def parse_args():
                    help="wall-clock budget of the CPU-oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-probe", type=int, default=0, metavar="BYTES")
+    p.add_argument("--with", dest="extras", default="",
+                   help="comma-separated extra stages added to each step and reported "
+                        "separately: zero_padding (zero-fill the padding rows after "
+                        "dispatch), output_memset (zero the output rows before combine)")
     return p.parse_args()
 
 
@@ -180,7 +184,24 @@ def main():
     def combine():
         mx.apply_shuffle_mul_sum(y, out, r["output_permutation"], weights)
 
-    stages = (("prepare", prepare), ("dispatch", dispatch), ("combine", combine))
+    def zero_padding():
+        mx.zero_padding_rows(xd, r["input_permutation"], r["expert_offsets"])
+
+    def output_memset():
+        mx.moe_output_memset(out, r["output_permutation"], k)
+
+    extras = [e for e in args.extras.split(",") if e]
+    known = {"zero_padding": zero_padding, "output_memset": output_memset}
+    for e in extras:
+        if e not in known:
+            raise SystemExit(f"unknown --with stage {e!r}; known: {sorted(known)}")
+    stages = [("prepare", prepare), ("dispatch", dispatch)]
+    if "zero_padding" in extras:
+        stages.append(("zero_padding", zero_padding))
+    if "output_memset" in extras:
+        stages.append(("output_memset", output_memset))
+    stages.append(("combine", combine))
+    stages = tuple(stages)
     for _ in range(args.warmup):
         for _, fn in stages:
             fn()
@@ -218,6 +239,18 @@ def main():
     counts = r["problem_sizes1"][:, 0].cpu().numpy()
     n_valid = int(counts.sum())
     nbytes = algorithmic_bytes(w, n_valid, cap, ids.element_size())
+    row_b = H * x.element_size()
+    extra_report = {}
+    if "zero_padding" in extras:
+        padded = int(r["expert_offsets"][-1].item())
+        nbytes["zero_padding"] = (padded - n_valid) * row_b + cap * 4
+    if "output_memset" in extras:
+        has_pick = (r["output_permutation"].view(T, k) >= 0).any(dim=1).sum().item()
+        nbytes["output_memset"] = int(has_pick) * H * out.element_size() + T * k * 4
+    for e in extras:
+        gbps = nbytes[e] / (stage_ms[e]["mean"] * 1e-3) / 1e9
+        extra_report[e] = {"ms": stage_ms[e]["mean"], "algorithmic_bytes": nbytes[e],
+                           "achieved_gbps": gbps, "frac": gbps / HBM_PEAK_GBPS}
     dom = max(("dispatch", "combine"), key=lambda n: stage_ms[n]["mean"])
     kernel_name = {"dispatch": "dispatch_rows_kernel", "combine": "combine_vec_kernel"}[dom]
     achieved = nbytes[dom] / (stage_ms[dom]["mean"] * 1e-3) / 1e9
@@ -252,6 +285,7 @@ def main():
                      "avg_launch_ms": stage_ms[dom]["mean"]},
         "cpu_baseline": cpu,
         "stages_ms": stage_ms,
+        "extras": extra_report or None,
         "algorithmic_bytes": nbytes,
         "step_hbm_gbps": step_bytes / (ms_per_step * 1e-3) / 1e9,
         "step_frac_of_peak": step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,

@@ -23,6 +23,7 @@ import torch  # loads the HIP runtime this library must share; keep before CDLL
 
 __all__ = [
     "prepare_moe_input", "shuffle_rows", "dispatch_rows", "apply_shuffle_mul_sum",
+    "moe_output_memset", "zero_padding_rows",
     "dispatch_capacity", "prepare_workspace_size", "empty_routing", "MxError",
     "library_path", "load_library", "EXPORTED_SYMBOLS",
 ]
@@ -38,7 +39,8 @@ MAX_EXPERTS = 1024
 EXPORTED_SYMBOLS = (
     "mx_status_string", "mx_last_hip_error", "mx_dispatch_capacity",
     "mx_prepare_workspace_size", "mx_prepare_moe_input", "mx_shuffle_rows",
-    "mx_dispatch_rows", "mx_apply_shuffle_mul_sum",
+    "mx_dispatch_rows", "mx_apply_shuffle_mul_sum", "mx_moe_output_memset",
+    "mx_zero_padding_rows",
 )
 
 
@@ -87,6 +89,10 @@ def load_library():
     lib.mx_dispatch_rows.argtypes = [vp, i64, i32, i64, vp, vp, i64, vp, i64, vp, vp]
     lib.mx_apply_shuffle_mul_sum.restype = ctypes.c_int
     lib.mx_apply_shuffle_mul_sum.argtypes = [vp, i32, i64, i64, vp, vp, i32, i64, i32, vp, i32, vp]
+    lib.mx_moe_output_memset.restype = ctypes.c_int
+    lib.mx_moe_output_memset.argtypes = [vp, i64, i32, i64, vp, vp]
+    lib.mx_zero_padding_rows.restype = ctypes.c_int
+    lib.mx_zero_padding_rows.argtypes = [vp, i64, i64, vp, vp, i32, vp]
     _lib = lib
     return lib
 
@@ -290,3 +296,42 @@ def apply_shuffle_mul_sum(input: torch.Tensor, output: torch.Tensor,
         _ptr(input), _FLOAT_CODES[input.dtype], input.shape[0], H, _ptr(permutation),
         _ptr(factors), fcode, T, topk, _ptr(output), _FLOAT_CODES[output.dtype], _stream(dev)),
         "apply_shuffle_mul_sum")
+
+
+def moe_output_memset(output: torch.Tensor, output_permutation: torch.Tensor, topk: int) -> None:
+    """In place: output row t becomes zeros iff one of its picks has a
+    permuted index >= 0; the other rows are left untouched."""
+    lib = load_library()
+    _check_dev("output", output)
+    dev = output.device
+    T = output.shape[0]
+    _check_dev("output_permutation", output_permutation, dev)
+    _check_i32("output_permutation", output_permutation, T * topk)
+    if T:
+        _call(lib.mx_moe_output_memset(_ptr(output), T, topk, _row_bytes(output),
+                                       _ptr(output_permutation), _stream(dev)),
+              "moe_output_memset")
+
+
+def zero_padding_rows(rows: torch.Tensor, input_permutation: torch.Tensor,
+                      expert_offsets: torch.Tensor | None = None) -> None:
+    """In place: dispatched rows below the padded total (expert_offsets[-1],
+    read on the device) whose source index is negative become zeros."""
+    lib = load_library()
+    _check_dev("rows", rows)
+    dev = rows.device
+    n = rows.shape[0]
+    _check_dev("input_permutation", input_permutation, dev)
+    _check_i32("input_permutation", input_permutation)
+    if input_permutation.numel() < n:
+        raise ValueError("input_permutation must cover every row")
+    E = 0
+    if expert_offsets is not None:
+        _check_dev("expert_offsets", expert_offsets, dev)
+        _check_i32("expert_offsets", expert_offsets)
+        E = expert_offsets.numel() - 1
+    if n:
+        _call(lib.mx_zero_padding_rows(_ptr(rows), n, _row_bytes(rows), _ptr(input_permutation),
+                                       _ptr(expert_offsets), E, _stream(dev)),
+              "zero_padding_rows")
+

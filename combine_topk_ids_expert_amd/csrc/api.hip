@@ -185,4 +185,34 @@ mx_status mx_apply_shuffle_mul_sum(const void* y, int32_t y_dtype, int64_t num_y
                                             static_cast<hipStream_t>(stream)));
 }
 
+mx_status mx_moe_output_memset(void* out, int64_t num_tokens, int32_t topk, int64_t row_bytes,
+                               const int32_t* output_permutation, void* stream) {
+    if (num_tokens < 0 || topk < 1 || num_tokens > kMax31 / topk || row_bytes < 1 ||
+        row_bytes > kMaxRowBytes)
+        return MX_ERR_INVALID_ARGUMENT;
+    if (num_tokens > 0 && (out == nullptr || output_permutation == nullptr))
+        return MX_ERR_INVALID_ARGUMENT;
+    if (!aligned(output_permutation, 4)) return MX_ERR_MISALIGNED;
+    if (num_tokens == 0) return MX_OK;
+    return hip_status(mxmoe::launch_output_memset(out, num_tokens, topk, row_bytes,
+                                                  output_permutation,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
+mx_status mx_zero_padding_rows(void* rows, int64_t num_rows, int64_t row_bytes,
+                               const int32_t* input_permutation, const int32_t* expert_offsets,
+                               int32_t num_experts, void* stream) {
+    if (num_rows < 0 || num_rows > kMax31 || row_bytes < 1 || row_bytes > kMaxRowBytes)
+        return MX_ERR_INVALID_ARGUMENT;
+    if (expert_offsets != nullptr && (num_experts < 1 || num_experts > MX_MAX_EXPERTS))
+        return MX_ERR_INVALID_ARGUMENT;
+    if (num_rows > 0 && (rows == nullptr || input_permutation == nullptr))
+        return MX_ERR_INVALID_ARGUMENT;
+    if (!aligned(input_permutation, 4) || !aligned(expert_offsets, 4)) return MX_ERR_MISALIGNED;
+    if (num_rows == 0) return MX_OK;
+    return hip_status(mxmoe::launch_zero_padding(rows, num_rows, row_bytes, input_permutation,
+                                                 expert_offsets, num_experts,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -46,4 +46,11 @@ hipError_t launch_combine(const void* y, int y_dtype, int64_t num_y_rows, int64_
                           int64_t num_tokens, int32_t topk, void* out, int out_dtype,
                           hipStream_t stream);
 
+hipError_t launch_zero_padding(void* rows, int64_t num_rows, int64_t row_bytes,
+                               const int32_t* input_perm, const int32_t* expert_offsets,
+                               int32_t num_experts, hipStream_t stream);
+
+hipError_t launch_output_memset(void* out, int64_t num_tokens, int32_t topk, int64_t row_bytes,
+                                const int32_t* expanded_to_permuted, hipStream_t stream);
+
 }  // namespace mxmoe

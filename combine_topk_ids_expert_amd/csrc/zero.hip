@@ -1,0 +1,172 @@
+// Zeroing rows in place: the MoE output memset (the TensorRT-LLM page
+// "Enable CuteDSL MoE with Large EP", walkthrough: zero the output row of
+// every token that has a valid permuted index, leave the others) and the
+// zero-fill of the padding rows of a dispatched buffer, for grouped GEMMs
+// that read whole tiles.
+//
+// The memset has the shape of the row copies: a workgroup per row and column
+// chunk, one 16-byte (or narrower) non-temporal store per thread; whether a
+// row is zeroed is decided once per workgroup from the index data.  The
+// padding fill works per expert segment (see zero_padding_expert_kernel).
+#include "device_common.h"
+#include "launch.h"
+
+namespace mxmoe {
+namespace {
+
+constexpr int kMaxZeroThreads = 1024;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <int V> struct ZVec;
+template <> struct ZVec<16> { using T = u32x4; };
+template <> struct ZVec<8> { using T = u32x2; };
+template <> struct ZVec<4> { using T = uint32_t; };
+template <> struct ZVec<2> { using T = uint16_t; };
+template <> struct ZVec<1> { using T = uint8_t; };
+
+template <int V>
+__device__ __forceinline__ void zero_vector(uint8_t* row, int64_t c, int64_t nvec) {
+    using T = typename ZVec<V>::T;
+    if (c < nvec) __builtin_nontemporal_store(T{}, reinterpret_cast<T*>(row) + c);
+}
+
+// Without expert offsets: row blockIdx.x is zeroed iff its source index is
+// negative (every row of the buffer is considered).
+template <int V>
+__global__ __launch_bounds__(kMaxZeroThreads) void zero_padding_kernel(
+    uint8_t* __restrict__ rows, int64_t num_rows, int64_t row_bytes,
+    const int32_t* __restrict__ input_perm, const int32_t* __restrict__ expert_offsets,
+    int32_t num_experts) {
+    const int64_t r = blockIdx.x;
+    int64_t limit = num_rows;
+    if (expert_offsets != nullptr) {
+        const int64_t total = expert_offsets[num_experts];
+        if (total < limit) limit = total;
+    }
+    if (r >= limit || input_perm[r] >= 0) return;
+    zero_vector<V>(rows + r * row_bytes, (int64_t)blockIdx.y * blockDim.x + threadIdx.x,
+                   row_bytes / V);
+}
+
+// With expert offsets only the rows inside the expert segments are
+// considered: workgroup (e, s) takes every kSlices-th row of segment e
+// [expert_offsets[e], expert_offsets[e+1]) from row seg0 + s, reads 64 of
+// their source indices per ballot, and zeroes exactly the rows whose index
+// is negative (each row over all its columns).  A segment holds at most
+// row_align - 1 padding rows, so the grid is E x kSlices workgroups instead
+// of one per row of capacity.  Segment bounds are clipped to [0, num_rows).
+#ifndef MXMOE_ZERO_SLICES
+#define MXMOE_ZERO_SLICES 16
+#endif
+constexpr int kSlices = MXMOE_ZERO_SLICES;
+
+template <int V>
+__global__ __launch_bounds__(kMaxZeroThreads) void zero_padding_expert_kernel(
+    uint8_t* __restrict__ rows, int64_t num_rows, int64_t row_bytes,
+    const int32_t* __restrict__ input_perm, const int32_t* __restrict__ expert_offsets) {
+    const int e = blockIdx.x;
+    const int lane = threadIdx.x & (kWave - 1);
+    int64_t seg0 = expert_offsets[e];
+    int64_t seg1 = expert_offsets[e + 1];
+    if (seg0 < 0) seg0 = 0;
+    if (seg1 > num_rows) seg1 = num_rows;
+    const int64_t nvec = row_bytes / V;
+    for (int64_t base = seg0 + blockIdx.y; base < seg1; base += (int64_t)kSlices * kWave) {
+        const int64_t r = base + (int64_t)lane * kSlices;
+        const bool pad = r < seg1 && input_perm[r] < 0;
+        uint64_t m = __ballot(pad);                    // wave-uniform from here on
+        while (m != 0ull) {
+            const int l = __builtin_ctzll(m);
+            m &= m - 1;
+            uint8_t* row = rows + (base + (int64_t)l * kSlices) * row_bytes;
+            for (int64_t c = threadIdx.x; c < nvec; c += blockDim.x) zero_vector<V>(row, c, nvec);
+        }
+    }
+}
+
+// Output row blockIdx.x (token t) is zeroed iff one of its topk picks has
+// a permuted index >= 0.
+template <int V>
+__global__ __launch_bounds__(kMaxZeroThreads) void output_memset_kernel(
+    uint8_t* __restrict__ out, int64_t row_bytes, int32_t topk,
+    const int32_t* __restrict__ expanded_to_permuted) {
+    const int64_t t = blockIdx.x;
+    const int lane = threadIdx.x & (kWave - 1);
+    bool any = false;
+    for (int j0 = 0; j0 < topk; j0 += kWave) {       // wave-uniform
+        const int j = j0 + lane;
+        const bool valid = j < topk && expanded_to_permuted[t * topk + j] >= 0;
+        any = any || __ballot(valid) != 0ull;
+    }
+    if (!any) return;
+    zero_vector<V>(out + t * row_bytes, (int64_t)blockIdx.y * blockDim.x + threadIdx.x,
+                   row_bytes / V);
+}
+
+int zvec_width(int64_t row_bytes, const void* p) {
+    const uint64_t bits = (uint64_t)row_bytes | (uint64_t)(uintptr_t)p;
+    for (int v = 16; v > 1; v >>= 1)
+        if ((bits & (uint64_t)(v - 1)) == 0) return v;
+    return 1;
+}
+
+void zero_grid(int64_t rows, int64_t row_bytes, int v, dim3& grid, dim3& block) {
+    const int64_t nvec = row_bytes / v;
+    const int64_t chunks = (nvec + kMaxZeroThreads - 1) / kMaxZeroThreads;
+    int64_t threads = (nvec + chunks - 1) / chunks;
+    threads = (threads + kWave - 1) / kWave * kWave;
+    grid = dim3((unsigned)rows, (unsigned)chunks, 1);
+    block = dim3((unsigned)threads, 1, 1);
+}
+
+}  // namespace
+
+hipError_t launch_zero_padding(void* rows, int64_t num_rows, int64_t row_bytes,
+                               const int32_t* input_perm, const int32_t* expert_offsets,
+                               int32_t num_experts, hipStream_t stream) {
+    if (num_rows == 0) return hipSuccess;
+    const int v = zvec_width(row_bytes, rows);
+    dim3 grid, block;
+    zero_grid(num_rows, row_bytes, v, grid, block);
+    uint8_t* p = static_cast<uint8_t*>(rows);
+    if (expert_offsets != nullptr) {
+        const dim3 egrid((unsigned)num_experts, kSlices, 1);
+        switch (v) {
+        case 16: zero_padding_expert_kernel<16><<<egrid, block, 0, stream>>>(p, num_rows, row_bytes, input_perm, expert_offsets); break;
+        case 8: zero_padding_expert_kernel<8><<<egrid, block, 0, stream>>>(p, num_rows, row_bytes, input_perm, expert_offsets); break;
+        case 4: zero_padding_expert_kernel<4><<<egrid, block, 0, stream>>>(p, num_rows, row_bytes, input_perm, expert_offsets); break;
+        case 2: zero_padding_expert_kernel<2><<<egrid, block, 0, stream>>>(p, num_rows, row_bytes, input_perm, expert_offsets); break;
+        default: zero_padding_expert_kernel<1><<<egrid, block, 0, stream>>>(p, num_rows, row_bytes, input_perm, expert_offsets); break;
+        }
+        return hipGetLastError();
+    }
+    switch (v) {
+    case 16: zero_padding_kernel<16><<<grid, block, 0, stream>>>(p, num_rows, row_bytes, input_perm, nullptr, 0); break;
+    case 8: zero_padding_kernel<8><<<grid, block, 0, stream>>>(p, num_rows, row_bytes, input_perm, nullptr, 0); break;
+    case 4: zero_padding_kernel<4><<<grid, block, 0, stream>>>(p, num_rows, row_bytes, input_perm, nullptr, 0); break;
+    case 2: zero_padding_kernel<2><<<grid, block, 0, stream>>>(p, num_rows, row_bytes, input_perm, nullptr, 0); break;
+    default: zero_padding_kernel<1><<<grid, block, 0, stream>>>(p, num_rows, row_bytes, input_perm, nullptr, 0); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_output_memset(void* out, int64_t num_tokens, int32_t topk, int64_t row_bytes,
+                                const int32_t* expanded_to_permuted, hipStream_t stream) {
+    if (num_tokens == 0) return hipSuccess;
+    const int v = zvec_width(row_bytes, out);
+    dim3 grid, block;
+    zero_grid(num_tokens, row_bytes, v, grid, block);
+    uint8_t* p = static_cast<uint8_t*>(out);
+    switch (v) {
+    case 16: output_memset_kernel<16><<<grid, block, 0, stream>>>(p, row_bytes, topk, expanded_to_permuted); break;
+    case 8: output_memset_kernel<8><<<grid, block, 0, stream>>>(p, row_bytes, topk, expanded_to_permuted); break;
+    case 4: output_memset_kernel<4><<<grid, block, 0, stream>>>(p, row_bytes, topk, expanded_to_permuted); break;
+    case 2: output_memset_kernel<2><<<grid, block, 0, stream>>>(p, row_bytes, topk, expanded_to_permuted); break;
+    default: output_memset_kernel<1><<<grid, block, 0, stream>>>(p, row_bytes, topk, expanded_to_permuted); break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace mxmoe

@@ -186,6 +186,39 @@ mx_status mx_apply_shuffle_mul_sum(const void* y, int32_t y_dtype, int64_t num_y
                                    int64_t num_tokens, int32_t topk,
                                    void* out, int32_t out_dtype, void* stream);
 
+/*
+ * moe_output_memset -- zero in place the output rows of the tokens that
+ * receive expert results (the TensorRT-LLM page "Enable CuteDSL MoE with
+ * Large EP", walkthrough and its in-place memset test: rows whose token has
+ * a permuted index >= 0 become zero, the others are left untouched):
+ *
+ *   out[t] = 0 (row_bytes zero bytes)  iff  exists j: output_permutation[t*k+j] >= 0
+ *
+ * out [T, row_bytes] any element type; output_permutation [T*k] int32.
+ * 1 <= row_bytes <= 65535 * 1024.
+ */
+mx_status mx_moe_output_memset(void* out, int64_t num_tokens, int32_t topk, int64_t row_bytes,
+                               const int32_t* output_permutation, void* stream);
+
+/*
+ * zero_padding_rows -- zero-fill the padding rows of a dispatched buffer, so
+ * a grouped GEMM that reads whole row_align tiles reads zeros there:
+ *
+ *   rows[r] = 0  iff  r < limit and input_permutation[r] < 0
+ *
+ * limit = expert_offsets[num_experts] (the padded total, read on the device)
+ * when expert_offsets is given, else num_rows; rows at or past it (unused
+ * capacity) are left untouched.  With expert_offsets (the offsets
+ * prepare_moe_input wrote: monotone, starting at 0) the work is spread per
+ * expert segment; segment bounds are clipped to [0, num_rows), so other
+ * offset values cannot cause accesses outside the arrays.  rows [num_rows,
+ * row_bytes]; input_permutation [num_rows] int32 (from prepare_moe_input).
+ * 1 <= row_bytes <= 65535 * 1024.
+ */
+mx_status mx_zero_padding_rows(void* rows, int64_t num_rows, int64_t row_bytes,
+                               const int32_t* input_permutation, const int32_t* expert_offsets,
+                               int32_t num_experts, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

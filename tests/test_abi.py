@@ -134,3 +134,24 @@ def test_binding_refuses_cpu_tensors():
         mx.prepare_moe_input(ids, r["a"], None, None, r["b"], r["c"], 2, 1, 1)
     with pytest.raises(ValueError):
         mx.shuffle_rows(torch.zeros(4, 8), torch.zeros(4, dtype=torch.int32))
+
+
+def test_zeroing_rejects(lib):
+    f = lib.mx_moe_output_memset
+    assert f(P, 10, 0, 16, P, S) == INVALID
+    assert f(P, 10, 8, 0, P, S) == INVALID
+    assert f(None, 10, 8, 16, P, S) == INVALID
+    assert f(P, 10, 8, 16, None, S) == INVALID
+    assert f(P, 10, 8, 16, P + 2, S) == MISALIGNED
+    assert f(P, 0, 8, 16, P, S) == OK
+    g = lib.mx_zero_padding_rows
+    assert g(P, 10, 0, P, None, 0, S) == INVALID
+    assert g(P, -1, 16, P, None, 0, S) == INVALID
+    assert g(None, 10, 16, P, None, 0, S) == INVALID
+    assert g(P, 10, 16, None, None, 0, S) == INVALID
+    assert g(P, 10, 16, P, P, 0, S) == INVALID          # offsets without an expert count
+    assert g(P, 10, 16, P, P, 1025, S) == INVALID
+    assert g(P, 10, 16, P + 1, None, 0, S) == MISALIGNED
+    assert g(P, 10, 16, P, P + 2, 4, S) == MISALIGNED
+    assert g(P, 0, 16, P, None, 0, S) == OK
+
