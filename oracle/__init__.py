@@ -73,6 +73,11 @@ def _declare(lib):
     lib.oracle_zero_padding_rows.restype = None
     lib.oracle_zero_padding_rows.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                              c_i32p, c_i32p, ctypes.c_int32]
+    lib.oracle_moe_sort.restype = ctypes.c_int
+    lib.oracle_moe_sort.argtypes = [
+        ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, c_i32p, c_i32p, ctypes.c_int64,
+        c_i32p, c_i32p, ctypes.c_int64, c_i32p, c_i32p]
     for name in ("oracle_f32_to_bf16", "oracle_f32_to_f16"):
         getattr(lib, name).restype = ctypes.c_uint16
         getattr(lib, name).argtypes = [ctypes.c_float]
@@ -200,6 +205,33 @@ def zero_padding_rows(rows: np.ndarray, input_permutation: np.ndarray,
     lib.oracle_zero_padding_rows(res.ctypes.data, len(res), _row_bytes(res), _i32p(inp),
                                  _i32p(eo), 0 if eo is None else eo.size - 1)
     return res
+
+
+def moe_sort(ids: np.ndarray, num_experts: int, local_expert_offset: int,
+             num_local_experts: int, tile_size: int, lib=None) -> dict:
+    """Tile-padded sort metadata for the local experts (see oracle.c)."""
+    lib = lib or load()
+    ids = np.ascontiguousarray(ids)
+    if ids.dtype not in (np.int32, np.int64) or ids.ndim != 2:
+        raise TypeError("ids must be a 2-D int32 or int64 array")
+    T, k = ids.shape
+    cap = T * k + num_local_experts * (tile_size - 1)
+    max_tiles = -(-cap // tile_size)
+    e2p = np.zeros(T * k, np.int32)
+    p2e = np.zeros(cap, np.int32)
+    tg = np.zeros(max_tiles, np.int32)
+    tl = np.zeros(max_tiles, np.int32)
+    total = np.zeros(1, np.int32)
+    ntiles = np.zeros(1, np.int32)
+    rc = lib.oracle_moe_sort(ids.ctypes.data, ids.dtype.itemsize, T, k, num_experts,
+                             local_expert_offset, num_local_experts, tile_size, _i32p(e2p),
+                             _i32p(p2e), cap, _i32p(tg), _i32p(tl), max_tiles, _i32p(total),
+                             _i32p(ntiles))
+    if rc != 0:
+        raise ValueError(f"oracle_moe_sort failed with {rc}")
+    return {"expanded_idx_to_permuted_idx": e2p, "permuted_idx_to_expanded_idx": p2e,
+            "tile_idx_to_group_idx": tg, "tile_idx_to_mn_limit": tl,
+            "total_num_padded_tokens": int(total[0]), "num_non_exiting_tiles": int(ntiles[0])}
 
 
 def f32_to_bf16(x: np.ndarray, lib=None) -> np.ndarray:

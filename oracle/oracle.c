@@ -273,3 +273,72 @@ void oracle_zero_padding_rows(uint8_t* rows, int64_t n_rows, int64_t row_bytes,
     for (int64_t r = 0; r < limit; ++r)
         if (input_perm[r] < 0) memset(rows + r * row_bytes, 0, (size_t)row_bytes);
 }
+
+/* ---------------------------------------------------------------------- */
+/* Tile-padded sort with a local-expert window (the sort of the TensorRT-LLM */
+/* page "Enable CuteDSL MoE with Large EP": its outputs                     */
+/* tile_idx_to_group_idx, tile_idx_to_mn_limit, expanded_idx_to_permuted_idx,*/
+/* permuted_idx_to_expanded_idx, total_num_padded_tokens,                   */
+/* num_non_exiting_tiles, and its num_local_experts / local_expert_offset / */
+/* tile_size parameters).                                                   */
+/*                                                                          */
+/* A pick i = t*k + j is local iff local_offset <= id < local_offset +      */
+/* num_local (and id < E); its group is g = id - local_offset.  Local picks */
+/* are sorted stably by group; group g takes ceil(count_g / tile) whole     */
+/* tiles.  permuted_to_expanded[r] is the pick i of row r, -1 for padding   */
+/* and unused rows; the tiles of group g hold g and the row limit           */
+/* first_row(g) + count_g; unused tiles hold -1.                            */
+/* Returns 0, -1 on bad arguments, -2 when capacity or max_tiles is too     */
+/* small, -3 on allocation failure.                                         */
+/* ---------------------------------------------------------------------- */
+
+int oracle_moe_sort(const void* ids, int id_bytes, int64_t T, int32_t k, int32_t E,
+                    int32_t local_offset, int32_t num_local, int32_t tile,
+                    int32_t* expanded_to_permuted, int32_t* permuted_to_expanded,
+                    int64_t capacity, int32_t* tile_group, int32_t* tile_limit,
+                    int64_t max_tiles, int32_t* total_padded, int32_t* num_tiles) {
+    if ((id_bytes != 4 && id_bytes != 8) || T < 0 || k < 1 || E < 1 || local_offset < 0 ||
+        num_local < 1 || (int64_t)local_offset + num_local > E || tile < 1)
+        return -1;
+    const int64_t n = T * (int64_t)k;
+    int64_t* count = (int64_t*)calloc((size_t)num_local, sizeof(int64_t));
+    int64_t* first = (int64_t*)malloc(sizeof(int64_t) * ((size_t)num_local + 1));
+    int64_t* next = (int64_t*)malloc(sizeof(int64_t) * (size_t)num_local);
+    if (!count || !first || !next) { free(count); free(first); free(next); return -3; }
+
+    for (int64_t i = 0; i < n; ++i) {
+        int64_t g = read_id(ids, id_bytes, i) - local_offset;
+        if (g >= 0 && g < num_local) count[g] += 1;
+    }
+    first[0] = 0;
+    for (int32_t g = 0; g < num_local; ++g)
+        first[g + 1] = first[g] + (count[g] + tile - 1) / tile * tile;
+    const int64_t total = first[num_local];
+    if (total > capacity || total / tile > max_tiles) {
+        free(count); free(first); free(next);
+        return -2;
+    }
+
+    for (int64_t r = 0; r < capacity; ++r) permuted_to_expanded[r] = -1;
+    for (int64_t q = 0; q < max_tiles; ++q) { tile_group[q] = -1; tile_limit[q] = -1; }
+    for (int32_t g = 0; g < num_local; ++g) next[g] = first[g];
+    for (int64_t i = 0; i < n; ++i) {
+        int64_t g = read_id(ids, id_bytes, i) - local_offset;
+        if (g >= 0 && g < num_local) {
+            int64_t r = next[g]++;
+            expanded_to_permuted[i] = (int32_t)r;
+            permuted_to_expanded[r] = (int32_t)i;
+        } else {
+            expanded_to_permuted[i] = -1;
+        }
+    }
+    for (int32_t g = 0; g < num_local; ++g)
+        for (int64_t q = first[g] / tile; q < first[g + 1] / tile; ++q) {
+            tile_group[q] = g;
+            tile_limit[q] = (int32_t)(first[g] + count[g]);
+        }
+    *total_padded = (int32_t)total;
+    *num_tiles = (int32_t)(total / tile);
+    free(count); free(first); free(next);
+    return 0;
+}

@@ -439,6 +439,71 @@ def pin_zeroing_vs_numpy(lib):
         np.testing.assert_array_equal(got, np.where((inp < 0)[:, None], 0, rows))
 
 
+# ---------------------------------------------------------------------------
+# tile-padded sort with a local-expert window
+# ---------------------------------------------------------------------------
+
+_SORT_KEYS = ("expanded_idx_to_permuted_idx", "permuted_idx_to_expanded_idx",
+              "tile_idx_to_group_idx", "tile_idx_to_mn_limit")
+
+
+def pin_golden_moe_sort(lib):
+    """Hand-worked tile-padded sort metadata (tests/golden/moe_sort_small.yaml)."""
+    for case in _golden("moe_sort_small.yaml"):
+        for dt in (np.int32, np.int64):
+            m = oracle.moe_sort(np.array(case["ids"], dt), case["num_experts"],
+                                case["local_expert_offset"], case["num_local_experts"],
+                                case["tile_size"], lib=lib)
+            for key in _SORT_KEYS:
+                np.testing.assert_array_equal(m[key], case[key], err_msg=f"{case['name']} {key}")
+            assert m["total_num_padded_tokens"] == case["total_num_padded_tokens"]
+            assert m["num_non_exiting_tiles"] == case["num_non_exiting_tiles"]
+
+
+def sort_reference_numpy(ids, E, L0, EL, S):
+    """The same metadata assembled from numpy library routines (stable
+    argsort, bincount, cumsum, repeat)."""
+    flat = ids.ravel().astype(np.int64)
+    g = flat - L0
+    local = (g >= 0) & (g < EL) & (flat < E)
+    counts = np.bincount(g[local], minlength=EL)
+    tiles = -(-counts // S)
+    first = np.concatenate([[0], np.cumsum(tiles * S)])
+    cap = flat.size + EL * (S - 1)
+    max_tiles = -(-cap // S)
+    li = np.nonzero(local)[0]
+    order = li[np.argsort(g[li], kind="stable")]               # local picks by group, stable
+    rank = np.arange(order.size) - np.concatenate([[0], np.cumsum(counts)])[g[order]]
+    rows = first[g[order]] + rank
+    e2p = np.full(flat.size, -1, np.int64)
+    e2p[order] = rows
+    p2e = np.full(cap, -1, np.int64)
+    p2e[rows] = order
+    tg = np.full(max_tiles, -1, np.int64)
+    tl = np.full(max_tiles, -1, np.int64)
+    ntile = int(tiles.sum())
+    tg[:ntile] = np.repeat(np.arange(EL), tiles)
+    tl[:ntile] = np.repeat(first[:-1] + counts, tiles)
+    return {"expanded_idx_to_permuted_idx": e2p, "permuted_idx_to_expanded_idx": p2e,
+            "tile_idx_to_group_idx": tg, "tile_idx_to_mn_limit": tl,
+            "total_num_padded_tokens": int(first[-1]), "num_non_exiting_tiles": ntile}
+
+
+def pin_moe_sort_vs_numpy(lib):
+    """Random routings, windows and tile sizes against the numpy assembly."""
+    rng = np.random.default_rng(22)
+    for T, E, k, L0, EL, S, mode in [(64, 16, 4, 4, 8, 8, "uniform"), (200, 256, 8, 32, 32, 128, "k_hot"),
+                                     (300, 128, 8, 0, 128, 16, "zipf"), (50, 9, 3, 2, 7, 1, "dups"),
+                                     (1, 4, 1, 3, 1, 4, "uniform"), (0, 8, 8, 0, 8, 4, "uniform")]:
+        ids = _rand_ids(rng, T, E, k, mode, invalid_frac=0.05) if T else np.zeros((0, k), np.int64)
+        m = oracle.moe_sort(ids, E, L0, EL, S, lib=lib)
+        want = sort_reference_numpy(ids, E, L0, EL, S)
+        for key in _SORT_KEYS:
+            np.testing.assert_array_equal(m[key], want[key], err_msg=key)
+        assert m["total_num_padded_tokens"] == want["total_num_padded_tokens"]
+        assert m["num_non_exiting_tiles"] == want["num_non_exiting_tiles"]
+
+
 ALL_PINS = [
     pin_golden_prepare,
     pin_prepare_vs_numpy,
@@ -455,6 +520,8 @@ ALL_PINS = [
     pin_conversions,
     pin_golden_zeroing,
     pin_zeroing_vs_numpy,
+    pin_golden_moe_sort,
+    pin_moe_sort_vs_numpy,
 ]
 
 

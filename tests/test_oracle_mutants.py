@@ -50,6 +50,14 @@ MUTANTS = {
                                    "output_perm[i] = 0;\n"),
     "memset_needs_all_picks": ("if (expanded_to_permuted[t * k + j] >= 0) any = 1;",
                                "if (expanded_to_permuted[t * k + j] >= 0) any = 1; else { any = 0; break; }"),
+    "sort_limit_is_segment_end": ("tile_limit[q] = (int32_t)(first[g] + count[g]);",
+                                  "tile_limit[q] = (int32_t)first[g + 1];"),
+    "sort_rows_hold_tokens": ("permuted_to_expanded[r] = (int32_t)i;",
+                              "permuted_to_expanded[r] = (int32_t)(i / k);"),
+    "sort_tile_count_off_by_one": ("*num_tiles = (int32_t)(total / tile);",
+                                   "*num_tiles = (int32_t)((total + tile) / tile);"),
+    "sort_window_ignores_offset": ("        int64_t g = read_id(ids, id_bytes, i) - local_offset;\n        if (g >= 0 && g < num_local) count[g] += 1;",
+                                   "        int64_t g = read_id(ids, id_bytes, i);\n        if (g >= 0 && g < num_local) count[g] += 1;"),
     "padding_ignores_total": ("int64_t limit = expert_offsets ? expert_offsets[E] : n_rows;",
                               "int64_t limit = n_rows;"),
 }
