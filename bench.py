@@ -59,7 +59,9 @@ def parse_args():
     p.add_argument("--with", dest="extras", default="",
                    help="comma-separated extra stages added to each step and reported "
                         "separately: zero_padding (zero-fill the padding rows after "
-                        "dispatch), output_memset (zero the output rows before combine)")
+                        "dispatch), output_memset (zero the output rows before combine), "
+                        "moe_sort (tile-padded sort metadata over all experts, tiles of "
+                        "row_align rows, after prepare)")
     return p.parse_args()
 
 
@@ -190,12 +192,24 @@ def main():
     def output_memset():
         mx.moe_output_memset(out, r["output_permutation"], k)
 
+    sort_tile = max(w.row_align, 1)
+    sort_out = {}
+    sort_ws = torch.empty(max(mx.prepare_workspace_size(T, k, E), 4), dtype=torch.uint8,
+                          device=dev)
+
+    def moe_sort():
+        sort_out.update(mx.moe_sort(ids, E, 0, E, sort_tile, out=sort_out or None,
+                                    workspace=sort_ws))
+
     extras = [e for e in args.extras.split(",") if e]
-    known = {"zero_padding": zero_padding, "output_memset": output_memset}
+    known = {"zero_padding": zero_padding, "output_memset": output_memset, "moe_sort": moe_sort}
     for e in extras:
         if e not in known:
             raise SystemExit(f"unknown --with stage {e!r}; known: {sorted(known)}")
-    stages = [("prepare", prepare), ("dispatch", dispatch)]
+    stages = [("prepare", prepare)]
+    if "moe_sort" in extras:
+        stages.append(("moe_sort", moe_sort))
+    stages.append(("dispatch", dispatch))
     if "zero_padding" in extras:
         stages.append(("zero_padding", zero_padding))
     if "output_memset" in extras:
@@ -247,6 +261,10 @@ def main():
     if "output_memset" in extras:
         has_pick = (r["output_permutation"].view(T, k) >= 0).any(dim=1).sum().item()
         nbytes["output_memset"] = int(has_pick) * H * out.element_size() + T * k * 4
+    if "moe_sort" in extras:
+        scap = sort_out["permuted_idx_to_expanded_idx"].numel()
+        nbytes["moe_sort"] = (T * k * ids.element_size() + T * k * 4 + scap * 4
+                              + 2 * 4 * sort_out["tile_idx_to_group_idx"].numel() + 4 * (E + 3))
     for e in extras:
         gbps = nbytes[e] / (stage_ms[e]["mean"] * 1e-3) / 1e9
         extra_report[e] = {"ms": stage_ms[e]["mean"], "algorithmic_bytes": nbytes[e],

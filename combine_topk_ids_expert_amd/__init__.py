@@ -23,7 +23,7 @@ import torch  # loads the HIP runtime this library must share; keep before CDLL
 
 __all__ = [
     "prepare_moe_input", "shuffle_rows", "dispatch_rows", "apply_shuffle_mul_sum",
-    "moe_output_memset", "zero_padding_rows",
+    "moe_output_memset", "zero_padding_rows", "moe_sort",
     "dispatch_capacity", "prepare_workspace_size", "empty_routing", "MxError",
     "library_path", "load_library", "EXPORTED_SYMBOLS",
 ]
@@ -40,7 +40,7 @@ EXPORTED_SYMBOLS = (
     "mx_status_string", "mx_last_hip_error", "mx_dispatch_capacity",
     "mx_prepare_workspace_size", "mx_prepare_moe_input", "mx_shuffle_rows",
     "mx_dispatch_rows", "mx_apply_shuffle_mul_sum", "mx_moe_output_memset",
-    "mx_zero_padding_rows",
+    "mx_zero_padding_rows", "mx_moe_sort",
 )
 
 
@@ -93,6 +93,9 @@ def load_library():
     lib.mx_moe_output_memset.argtypes = [vp, i64, i32, i64, vp, vp]
     lib.mx_zero_padding_rows.restype = ctypes.c_int
     lib.mx_zero_padding_rows.argtypes = [vp, i64, i64, vp, vp, i32, vp]
+    lib.mx_moe_sort.restype = ctypes.c_int
+    lib.mx_moe_sort.argtypes = [vp, i32, i64, i32, i32, i32, i32, i32, vp, vp, i64, vp, vp, i64,
+                                vp, vp, vp, vp, sz, vp]
     _lib = lib
     return lib
 
@@ -334,4 +337,51 @@ def zero_padding_rows(rows: torch.Tensor, input_permutation: torch.Tensor,
         _call(lib.mx_zero_padding_rows(_ptr(rows), n, _row_bytes(rows), _ptr(input_permutation),
                                        _ptr(expert_offsets), E, _stream(dev)),
               "zero_padding_rows")
+
+
+def moe_sort(topk_ids: torch.Tensor, num_experts: int, local_expert_offset: int,
+             num_local_experts: int, tile_size: int, out: dict | None = None,
+             workspace: torch.Tensor | None = None) -> dict:
+    """Tile-padded sort metadata for the experts [local_expert_offset,
+    local_expert_offset + num_local_experts) (see mx_moe_sort).  Returns a dict
+    of int32 tensors: expanded_idx_to_permuted_idx [T*k],
+    permuted_idx_to_expanded_idx [capacity], tile_idx_to_group_idx and
+    tile_idx_to_mn_limit [max_tiles], total_num_padded_tokens [1],
+    num_non_exiting_tiles [1], expert_offsets [num_local_experts + 1];
+    ``out`` may supply any of them (already allocated, written in place)."""
+    lib = load_library()
+    _check_dev("topk_ids", topk_ids)
+    dev = topk_ids.device
+    if topk_ids.dim() != 2 or topk_ids.dtype not in (torch.int32, torch.int64):
+        raise TypeError("topk_ids must be a 2-D int32 or int64 tensor")
+    T, topk = topk_ids.shape
+    cap = dispatch_capacity(T, topk, num_local_experts, tile_size)
+    max_tiles = -(-cap // tile_size)
+    sizes = {"expanded_idx_to_permuted_idx": T * topk, "permuted_idx_to_expanded_idx": cap,
+             "tile_idx_to_group_idx": max_tiles, "tile_idx_to_mn_limit": max_tiles,
+             "total_num_padded_tokens": 1, "num_non_exiting_tiles": 1,
+             "expert_offsets": num_local_experts + 1}
+    res = dict(out or {})
+    for name, numel in sizes.items():
+        if name not in res or res[name] is None:
+            res[name] = torch.empty(numel, dtype=torch.int32, device=dev)
+        _check_dev(name, res[name], dev)
+        _check_i32(name, res[name])
+        if name not in ("permuted_idx_to_expanded_idx", "tile_idx_to_group_idx",
+                        "tile_idx_to_mn_limit") and res[name].numel() != numel:
+            raise ValueError(f"{name} must have {numel} elements")
+    if workspace is None:
+        workspace = torch.empty(max(lib.mx_prepare_workspace_size(T, topk, num_local_experts), 4),
+                                dtype=torch.uint8, device=dev)
+    _check_dev("workspace", workspace, dev)
+    nt = min(res["tile_idx_to_group_idx"].numel(), res["tile_idx_to_mn_limit"].numel())
+    _call(lib.mx_moe_sort(
+        _ptr(topk_ids), MX_I64 if topk_ids.dtype == torch.int64 else MX_I32, T, topk, num_experts,
+        local_expert_offset, num_local_experts, tile_size,
+        _ptr(res["expanded_idx_to_permuted_idx"]), _ptr(res["permuted_idx_to_expanded_idx"]),
+        res["permuted_idx_to_expanded_idx"].numel(), _ptr(res["tile_idx_to_group_idx"]),
+        _ptr(res["tile_idx_to_mn_limit"]), nt, _ptr(res["total_num_padded_tokens"]),
+        _ptr(res["num_non_exiting_tiles"]), _ptr(res["expert_offsets"]),
+        _ptr(workspace), workspace.numel(), _stream(dev)), "moe_sort")
+    return res
 

@@ -101,7 +101,7 @@ mx_status mx_prepare_moe_input(const void* topk_ids, int32_t ids_dtype, int64_t 
     if (need > 0 && (workspace == nullptr || workspace_bytes < need))
         return MX_ERR_WORKSPACE_TOO_SMALL;
 
-    mxmoe::RouteArgs a;
+    mxmoe::RouteArgs a{};
     a.ids = topk_ids;
     a.ids64 = ids_dtype == MX_I64;
     a.num_picks = n;
@@ -213,6 +213,64 @@ mx_status mx_zero_padding_rows(void* rows, int64_t num_rows, int64_t row_bytes,
     return hip_status(mxmoe::launch_zero_padding(rows, num_rows, row_bytes, input_permutation,
                                                  expert_offsets, num_experts,
                                                  static_cast<hipStream_t>(stream)));
+}
+
+mx_status mx_moe_sort(const void* topk_ids, int32_t ids_dtype, int64_t num_tokens, int32_t topk,
+                      int32_t num_experts, int32_t local_expert_offset,
+                      int32_t num_local_experts, int32_t tile_size,
+                      int32_t* expanded_idx_to_permuted_idx,
+                      int32_t* permuted_idx_to_expanded_idx, int64_t permuted_capacity,
+                      int32_t* tile_idx_to_group_idx, int32_t* tile_idx_to_mn_limit,
+                      int64_t max_tiles, int32_t* total_num_padded_tokens,
+                      int32_t* num_non_exiting_tiles, int32_t* expert_offsets,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+    if (ids_dtype != MX_I32 && ids_dtype != MX_I64) return MX_ERR_UNSUPPORTED_DTYPE;
+    if (num_tokens < 0 || topk < 1 || num_experts < 1 || local_expert_offset < 0 ||
+        num_local_experts < 1 || num_local_experts > MX_MAX_EXPERTS ||
+        (int64_t)local_expert_offset + num_local_experts > num_experts || tile_size < 1)
+        return MX_ERR_INVALID_ARGUMENT;
+    const int64_t cap = mx_dispatch_capacity(num_tokens, topk, num_local_experts, tile_size);
+    if (cap < 0) return MX_ERR_INVALID_ARGUMENT;
+    const int64_t n = num_tokens * topk;
+    if ((n > 0 && (topk_ids == nullptr || expanded_idx_to_permuted_idx == nullptr)) ||
+        (permuted_capacity > 0 && permuted_idx_to_expanded_idx == nullptr) ||
+        (max_tiles > 0 && (tile_idx_to_group_idx == nullptr || tile_idx_to_mn_limit == nullptr)) ||
+        total_num_padded_tokens == nullptr || num_non_exiting_tiles == nullptr)
+        return MX_ERR_INVALID_ARGUMENT;
+    if (permuted_capacity < cap || max_tiles < (cap + tile_size - 1) / tile_size)
+        return MX_ERR_CAPACITY;
+    if (permuted_capacity > kMax31 || max_tiles > kMax31) return MX_ERR_INVALID_ARGUMENT;
+    if (!aligned(topk_ids, ids_dtype == MX_I64 ? 8 : 4) ||
+        !aligned(expanded_idx_to_permuted_idx, 4) || !aligned(permuted_idx_to_expanded_idx, 4) ||
+        !aligned(tile_idx_to_group_idx, 4) || !aligned(tile_idx_to_mn_limit, 4) ||
+        !aligned(total_num_padded_tokens, 4) || !aligned(num_non_exiting_tiles, 4) ||
+        !aligned(expert_offsets, 4) || !aligned(workspace, 4))
+        return MX_ERR_MISALIGNED;
+    const size_t need = mxmoe::route_workspace_bytes(n, num_local_experts);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+        return MX_ERR_WORKSPACE_TOO_SMALL;
+
+    mxmoe::RouteArgs a{};
+    a.ids = topk_ids;
+    a.ids64 = ids_dtype == MX_I64;
+    a.num_picks = n;
+    a.topk = topk;
+    a.num_experts = num_local_experts;
+    a.row_align = tile_size;
+    a.bs_align = 1;
+    a.expert_offsets = expert_offsets;
+    a.input_perm = permuted_idx_to_expanded_idx;
+    a.input_perm_len = permuted_capacity;
+    a.output_perm = expanded_idx_to_permuted_idx;
+    a.workspace = static_cast<int32_t*>(workspace);
+    a.id_offset = local_expert_offset;
+    a.inp_expanded = true;
+    a.tile_group = tile_idx_to_group_idx;
+    a.tile_limit = tile_idx_to_mn_limit;
+    a.max_tiles = max_tiles;
+    a.padded_total = total_num_padded_tokens;
+    a.tile_count = num_non_exiting_tiles;
+    return hip_status(mxmoe::launch_route(a, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

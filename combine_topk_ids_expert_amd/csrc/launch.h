@@ -24,6 +24,14 @@ struct RouteArgs {
     int64_t input_perm_len;
     int32_t* output_perm;     // [T*k]
     int32_t* workspace;
+    // Local-expert window and tile metadata (zero / null for prepare_moe_input):
+    int32_t id_offset;        // subtracted from every id; valid iff 0 <= id - offset < E
+    bool inp_expanded;        // input_perm holds the pick index i instead of the token i / k
+    int32_t* tile_group;      // [max_tiles] tile -> expert of its segment, -1 unused
+    int32_t* tile_limit;      // [max_tiles] tile -> first row + count of its expert, -1 unused
+    int64_t max_tiles;        // tiles are row_align rows
+    int32_t* padded_total;    // [1] padded row total, or null
+    int32_t* tile_count;      // [1] padded row total / row_align, or null
 };
 
 // Device workspace the routing kernels need for `num_picks` picks.

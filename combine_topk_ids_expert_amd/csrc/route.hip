@@ -56,15 +56,18 @@ __host__ __device__ inline int64_t tile_picks(int64_t n) {
 struct Shape {
     int64_t n;        // picks
     int E, nbits, k;
+    int32_t id_offset;
+    bool expanded;    // input_perm holds i instead of i / k
 };
 
 __device__ __forceinline__ int round_up_i(int v, int a) { return (v + a - 1) / a * a; }
 
 template <typename IdT>
-__device__ __forceinline__ int load_key(const IdT* ids, int64_t i, int64_t end, int E) {
+__device__ __forceinline__ int load_key(const IdT* ids, int64_t i, int64_t end, int E,
+                                        int32_t id_offset) {
     if (i >= end) return -1;
-    const IdT v = ids[i];
-    return (v >= 0 && v < (IdT)E) ? (int)v : -1;
+    const int64_t v = (int64_t)ids[i] - id_offset;
+    return (v >= 0 && v < E) ? (int)v : -1;
 }
 
 // This wave's stretch [w0, w1) of the tile [t0, t1): equal stretches of a
@@ -80,10 +83,10 @@ __device__ __forceinline__ void wave_stretch(int64_t t0, int64_t t1, int wave, i
 // One round of up to kBatch 64-pick groups starting at g0, keys loaded.
 template <typename IdT>
 __device__ __forceinline__ void load_keys(const IdT* ids, int64_t g0, int64_t w1, int E,
-                                          int (&key)[kBatch]) {
+                                          int32_t id_offset, int (&key)[kBatch]) {
     const int lane = lane_id();
 #pragma unroll
-    for (int b = 0; b < kBatch; ++b) key[b] = load_key(ids, g0 + b * kWave + lane, w1, E);
+    for (int b = 0; b < kBatch; ++b) key[b] = load_key(ids, g0 + b * kWave + lane, w1, E, id_offset);
 }
 
 // Count a round of keys per expert into this wave's LDS row.
@@ -109,7 +112,7 @@ __device__ __forceinline__ void scatter_keys(const int (&key)[kBatch], int64_t g
         if (key[b] >= 0) {
             const int r = row[key[b]] + rank;   // every lane reads before the update below
             outp[i] = r;
-            if (r < inp_len) inp[r] = (int32_t)((uint32_t)i / (uint32_t)s.k);
+            if (r < inp_len) inp[r] = s.expanded ? (int32_t)i : (int32_t)((uint32_t)i / (uint32_t)s.k);
         } else if (i < w1) {
             outp[i] = -1;
         }
@@ -123,7 +126,7 @@ __device__ void count_stretch(const IdT* ids, int64_t w0, int64_t w1, const Shap
                               int* row) {
     for (int64_t g0 = w0; g0 < w1; g0 += kBatch * kWave) {
         int key[kBatch];
-        load_keys(ids, g0, w1, s.E, key);
+        load_keys(ids, g0, w1, s.E, s.id_offset, key);
         count_keys(key, s, row);
     }
 }
@@ -134,7 +137,7 @@ __device__ void scatter_stretch(const IdT* ids, int64_t w0, int64_t w1, const Sh
                                 int* row, int32_t* outp, int32_t* inp, int64_t inp_len) {
     for (int64_t g0 = w0; g0 < w1; g0 += kBatch * kWave) {
         int key[kBatch];
-        load_keys(ids, g0, w1, s.E, key);
+        load_keys(ids, g0, w1, s.E, s.id_offset, key);
         scatter_keys(key, g0, w1, s, row, outp, inp, inp_len);
     }
 }
@@ -175,7 +178,7 @@ __device__ int scan_experts(const RouteArgs& a, const int* cnt, int* off, int* t
         return tmp[128];
     }
     if (tid == 0) {
-        a.expert_offsets[0] = 0;
+        if (a.expert_offsets) a.expert_offsets[0] = 0;
         if (a.blockscale_offsets) a.blockscale_offsets[0] = 0;
     }
     for (int e = e0; e < e1; ++e) {
@@ -183,7 +186,7 @@ __device__ int scan_experts(const RouteArgs& a, const int* cnt, int* off, int* t
         off[e] = xr;
         xr += round_up_i(c, a.row_align);
         xb += round_up_i(c, a.bs_align);
-        a.expert_offsets[e + 1] = xr;
+        if (a.expert_offsets) a.expert_offsets[e + 1] = xr;
         if (a.blockscale_offsets) a.blockscale_offsets[e + 1] = xb;
         if (a.problem_sizes1) {
             a.problem_sizes1[3 * e] = c;
@@ -212,6 +215,34 @@ __device__ void fill_unused_rows(const RouteArgs& a, const int* cnt, const int* 
     }
     for (int64_t r = R + first_thread; r < a.input_perm_len; r += thread_stride)
         a.input_perm[r] = -1;
+}
+
+// Tile maps of the tile-padded sort: the tiles [off[e], off[e] + padded
+// count) / row_align of every expert handled by this wave get the expert and
+// its row limit off[e] + cnt[e]; tiles past R / row_align get -1; the first
+// thread of the grid writes the totals.
+__device__ void fill_tiles(const RouteArgs& a, const int* cnt, const int* off, int R,
+                           int first_wave, int wave_stride, int64_t first_thread,
+                           int64_t thread_stride) {
+    if (a.tile_group == nullptr) return;
+    const int lane = lane_id();
+    const int S = a.row_align;
+    for (int e = first_wave; e < a.num_experts; e += wave_stride) {
+        const int c = cnt[e];
+        const int64_t q0 = off[e] / S, q1 = q0 + (c + S - 1) / S;
+        for (int64_t q = q0 + lane; q < q1; q += kWave) {
+            a.tile_group[q] = e;
+            a.tile_limit[q] = off[e] + c;
+        }
+    }
+    for (int64_t q = R / S + first_thread; q < a.max_tiles; q += thread_stride) {
+        a.tile_group[q] = -1;
+        a.tile_limit[q] = -1;
+    }
+    if (first_thread == 0) {
+        if (a.padded_total) a.padded_total[0] = R;
+        if (a.tile_count) a.tile_count[0] = R / S;
+    }
 }
 
 // ---- single workgroup: count, scan and scatter in one launch -----------------
@@ -253,6 +284,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_fused_kernel(RouteArgs a,
     scatter_stretch<IdT>(ids, w0, w1, s, rows[wave], a.output_perm, a.input_perm,
                          a.input_perm_len);
     fill_unused_rows(a, cnt, off, R, wave, kRouteWaves, tid, kRouteThreads);
+    fill_tiles(a, cnt, off, R, wave, kRouteWaves, tid, kRouteThreads);
 }
 
 // ---- two-launch path -------------------------------------------------------
@@ -301,7 +333,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(RouteArgs 
     // passes; they are requested first so their latency overlaps the table.
     const bool one_round = w1 - w0 <= kBatch * kWave;
     int key[kBatch];
-    if (one_round) load_keys(ids, w0, w1, s.E, key);
+    if (one_round) load_keys(ids, w0, w1, s.E, s.id_offset, key);
 
     // Expert totals over all tiles and this tile's prefix: a thread per expert
     // reads the expert's row of the count table with 16-byte loads, issued
@@ -354,13 +386,16 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(RouteArgs 
                              a.input_perm_len);
     fill_unused_rows(a, cnt, off, R, b * kRouteWaves + wave, tiles * kRouteWaves,
                      (int64_t)b * kRouteThreads + tid, (int64_t)tiles * kRouteThreads);
+    fill_tiles(a, cnt, off, R, b * kRouteWaves + wave, tiles * kRouteWaves,
+               (int64_t)b * kRouteThreads + tid, (int64_t)tiles * kRouteThreads);
 }
 
 int id_bits(int E) { return E <= 1 ? 0 : 32 - __builtin_clz((unsigned)(E - 1)); }
 
 template <typename IdT>
 hipError_t launch_typed(const RouteArgs& a, hipStream_t stream) {
-    Shape s{a.num_picks, a.num_experts, id_bits(a.num_experts), a.topk};
+    Shape s{a.num_picks, a.num_experts, id_bits(a.num_experts), a.topk, a.id_offset,
+            a.inp_expanded};
     if (a.num_picks <= kFusedMax) {
         route_fused_kernel<IdT><<<1, kRouteThreads, 0, stream>>>(a, s);
         return hipGetLastError();

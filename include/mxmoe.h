@@ -187,6 +187,48 @@ mx_status mx_apply_shuffle_mul_sum(const void* y, int32_t y_dtype, int64_t num_y
                                    void* out, int32_t out_dtype, void* stream);
 
 /*
+ * moe_sort -- tile-padded sort metadata for one rank's window of experts
+ * (the TensorRT-LLM page "Enable CuteDSL MoE with Large EP": the sort that
+ * returns tile_idx_to_group_idx, tile_idx_to_mn_limit,
+ * expanded_idx_to_permuted_idx, permuted_idx_to_expanded_idx,
+ * total_num_padded_tokens and num_non_exiting_tiles for a grouped GEMM over
+ * num_local_experts experts starting at local_expert_offset, in tiles of
+ * tile_size rows).
+ *
+ * Pick i = t*k + j is local iff local_expert_offset <= id <
+ * local_expert_offset + num_local_experts; its group is g = id -
+ * local_expert_offset.  Local picks are sorted stably by group (ascending i
+ * within a group); group g takes ceil(count_g / tile_size) whole tiles,
+ * groups in order from row 0.
+ *
+ *   expanded_idx_to_permuted_idx[i] = row of pick i, -1 if not local
+ *   permuted_idx_to_expanded_idx[r] = pick i held by row r, -1 for padding
+ *                                     rows and rows past the last group
+ *   tile_idx_to_group_idx[q]        = group of tile q, -1 past the last group
+ *   tile_idx_to_mn_limit[q]         = first row of that group + count_g (end of
+ *                                     the group's valid rows), -1 past the last
+ *   total_num_padded_tokens[0]      = sum_g ceil(count_g / tile_size) * tile_size
+ *   num_non_exiting_tiles[0]        = total_num_padded_tokens / tile_size
+ *   expert_offsets[g] (optional)    = first row of group g, [num_local_experts+1]
+ *
+ * permuted_capacity >= mx_dispatch_capacity(T, k, num_local_experts,
+ * tile_size) and max_tiles >= ceil(that capacity / tile_size), else
+ * MX_ERR_CAPACITY; every entry of both arrays is written.  0 <=
+ * local_expert_offset, local_expert_offset + num_local_experts <=
+ * num_experts, num_local_experts <= MX_MAX_EXPERTS, tile_size >= 1.
+ * workspace: mx_prepare_workspace_size(T, k, num_local_experts) bytes.
+ */
+mx_status mx_moe_sort(const void* topk_ids, int32_t ids_dtype, int64_t num_tokens, int32_t topk,
+                      int32_t num_experts, int32_t local_expert_offset,
+                      int32_t num_local_experts, int32_t tile_size,
+                      int32_t* expanded_idx_to_permuted_idx,
+                      int32_t* permuted_idx_to_expanded_idx, int64_t permuted_capacity,
+                      int32_t* tile_idx_to_group_idx, int32_t* tile_idx_to_mn_limit,
+                      int64_t max_tiles, int32_t* total_num_padded_tokens,
+                      int32_t* num_non_exiting_tiles, int32_t* expert_offsets,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * moe_output_memset -- zero in place the output rows of the tokens that
  * receive expert results (the TensorRT-LLM page "Enable CuteDSL MoE with
  * Large EP", walkthrough and its in-place memset test: rows whose token has

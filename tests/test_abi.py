@@ -155,3 +155,33 @@ def test_zeroing_rejects(lib):
     assert g(P, 10, 16, P, P + 2, 4, S) == MISALIGNED
     assert g(P, 0, 16, P, None, 0, S) == OK
 
+
+def _sort(lib, **kw):
+    a = dict(ids=P, dt=I64, T=64, k=8, E=256, L0=32, EL=32, S=128, e2p=P, p2e=P,
+             cap=64 * 8 + 32 * 127, tg=P, tl=P, mt=(64 * 8 + 32 * 127 + 127) // 128, tot=P, nt=P,
+             eo=None, ws=P, wsb=1 << 20)
+    a.update(kw)
+    return lib.mx_moe_sort(a["ids"], a["dt"], a["T"], a["k"], a["E"], a["L0"], a["EL"], a["S"],
+                           a["e2p"], a["p2e"], a["cap"], a["tg"], a["tl"], a["mt"], a["tot"],
+                           a["nt"], a["eo"], a["ws"], a["wsb"], S)
+
+
+def test_moe_sort_rejects(lib):
+    assert _sort(lib, dt=F16) == DTYPE
+    assert _sort(lib, L0=-1) == INVALID
+    assert _sort(lib, EL=0) == INVALID
+    assert _sort(lib, L0=250, EL=32) == INVALID          # window past the expert count
+    assert _sort(lib, EL=1025, E=2000, L0=0) == INVALID
+    assert _sort(lib, S=0) == INVALID
+    assert _sort(lib, e2p=None) == INVALID
+    assert _sort(lib, p2e=None) == INVALID
+    assert _sort(lib, tg=None) == INVALID
+    assert _sort(lib, tot=None) == INVALID
+    assert _sort(lib, nt=None) == INVALID
+    assert _sort(lib, cap=64 * 8) == CAPACITY
+    assert _sort(lib, mt=3) == CAPACITY
+    assert _sort(lib, ids=P + 4) == MISALIGNED
+    assert _sort(lib, tl=P + 2) == MISALIGNED
+    assert _sort(lib, T=65536, cap=65536 * 8 + 32 * 127, mt=(65536 * 8 + 32 * 127) // 128 + 1,
+                 ws=None) == WORKSPACE
+
