@@ -78,6 +78,11 @@ def _declare(lib):
         ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, c_i32p, c_i32p, ctypes.c_int64,
         c_i32p, c_i32p, ctypes.c_int64, c_i32p, c_i32p]
+    lib.oracle_f32_to_e4m3.restype = ctypes.c_uint8
+    lib.oracle_f32_to_e4m3.argtypes = [ctypes.c_float]
+    lib.oracle_quantize_fp8_rows.restype = None
+    lib.oracle_quantize_fp8_rows.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                             ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
     for name in ("oracle_f32_to_bf16", "oracle_f32_to_f16"):
         getattr(lib, name).restype = ctypes.c_uint16
         getattr(lib, name).argtypes = [ctypes.c_float]
@@ -232,6 +237,25 @@ def moe_sort(ids: np.ndarray, num_experts: int, local_expert_offset: int,
     return {"expanded_idx_to_permuted_idx": e2p, "permuted_idx_to_expanded_idx": p2e,
             "tile_idx_to_group_idx": tg, "tile_idx_to_mn_limit": tl,
             "total_num_padded_tokens": int(total[0]), "num_non_exiting_tiles": int(ntiles[0])}
+
+
+def f32_to_e4m3(x: np.ndarray, lib=None) -> np.ndarray:
+    lib = lib or load()
+    return np.array([lib.oracle_f32_to_e4m3(float(v)) for v in np.asarray(x, np.float32).ravel()],
+                    dtype=np.uint8)
+
+
+def quantize_fp8_rows(x_bf16_bits: np.ndarray, block: int = 128, lib=None):
+    """bf16 rows (uint16 patterns [T, H]) -> (e4m3fn bytes uint8 [T, H],
+    float32 scales [T, H / block])."""
+    lib = lib or load()
+    x = np.ascontiguousarray(x_bf16_bits).view(np.uint16)
+    T, H = x.shape
+    assert H % block == 0
+    q = np.zeros((T, H), np.uint8)
+    sc = np.zeros((T, H // block), np.float32)
+    lib.oracle_quantize_fp8_rows(x.ctypes.data, T, H, block, q.ctypes.data, sc.ctypes.data)
+    return q, sc
 
 
 def f32_to_bf16(x: np.ndarray, lib=None) -> np.ndarray:

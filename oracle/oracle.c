@@ -342,3 +342,56 @@ int oracle_moe_sort(const void* ids, int id_bytes, int64_t T, int32_t k, int32_t
     free(count); free(first); free(next);
     return 0;
 }
+
+/* ---------------------------------------------------------------------- */
+/* FP8 quantization of a row in 1 x block groups (the quantize_input step of */
+/* the TensorRT-LLM large-EP page, and the FP8 block-scale layout of the    */
+/* sglang page's blockscale offsets).  Reading: per group of `block`         */
+/* consecutive elements, amax = max |x|, scale = amax / 448 (1 when amax is */
+/* 0), q = e4m3fn(x / scale) rounded to nearest even and saturated at 448;  */
+/* all float arithmetic in fp32 (correctly rounded division).               */
+/* ---------------------------------------------------------------------- */
+
+/* binary32 -> OCP e4m3fn (1 sign, 4 exponent bits with bias 7, 3 fraction
+ * bits; largest finite 448 = 1.75 * 2^8; no infinities), round to nearest
+ * even, magnitudes beyond 448 saturate to 448.  NaN maps to 0x7f. */
+static uint8_t f32_to_e4m3(float f) {
+    uint8_t sign = signbit(f) ? 0x80 : 0;
+    if (isnan(f)) return 0x7f;
+    float a = fabsf(f);
+    if (a >= 448.0f) return sign | 0x7e;
+    if (a < 0x1p-6f) {                           /* subnormal range: units of 2^-9 */
+        float q = rintf(a * 0x1p9f);             /* 8 becomes the smallest normal  */
+        return sign | (uint8_t)q;
+    }
+    int e2;
+    frexpf(a, &e2);
+    int ex = e2 - 1;                             /* a in [2^ex, 2^(ex+1)), ex >= -6 */
+    float q = rintf(ldexpf(a, 3 - ex));          /* significand in units of 2^-3 */
+    if (q == 16.0f) { q = 8.0f; ex += 1; }
+    uint8_t code = (uint8_t)(((ex + 7) << 3) | ((int)q - 8));
+    return sign | (code > 0x7e ? 0x7e : code);
+}
+
+uint8_t oracle_f32_to_e4m3(float f) { return f32_to_e4m3(f); }
+
+/* x [T][H] bf16 -> q [T][H] e4m3fn bytes and scales [T][H / block] fp32;
+ * H must be a multiple of block. */
+void oracle_quantize_fp8_rows(const uint16_t* x, int64_t T, int64_t H, int32_t block,
+                              uint8_t* q, float* scales) {
+    const int64_t groups = H / block;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t g = 0; g < groups; ++g) {
+            const uint16_t* xs = x + t * H + g * block;
+            float amax = 0.0f;
+            for (int32_t e = 0; e < block; ++e) {
+                float v = fabsf(bf16_to_f32(xs[e]));
+                if (v > amax) amax = v;
+            }
+            float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
+            scales[t * groups + g] = scale;
+            for (int32_t e = 0; e < block; ++e)
+                q[t * H + g * block + e] = f32_to_e4m3(bf16_to_f32(xs[e]) / scale);
+        }
+    }
+}

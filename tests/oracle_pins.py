@@ -504,6 +504,58 @@ def pin_moe_sort_vs_numpy(lib):
         assert m["num_non_exiting_tiles"] == want["num_non_exiting_tiles"]
 
 
+# ---------------------------------------------------------------------------
+# FP8 quantization
+# ---------------------------------------------------------------------------
+
+def _e4m3_torch(v: np.ndarray) -> np.ndarray:
+    """float32 -> e4m3fn bytes by torch's conversion (round to nearest even),
+    after clamping to the finite range so torch does not produce NaN."""
+    t = torch.from_numpy(np.clip(np.asarray(v, np.float32), -448.0, 448.0))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def pin_e4m3_conversion(lib):
+    """The oracle's fp32 -> e4m3fn rounding against torch's on every e4m3
+    value, every midpoint between neighbours (ties to even), random values
+    over the whole range, subnormals, and values past 448 (saturation)."""
+    codes = np.arange(256, dtype=np.uint8)
+    vals = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy()
+    finite = np.isfinite(vals)
+    v = np.unique(vals[finite])
+    mids = ((v[1:].astype(np.float64) + v[:-1]) / 2).astype(np.float32)   # exact in fp32
+    rng = np.random.default_rng(23)
+    rand = (rng.standard_normal(4000) * 10.0 ** rng.uniform(-4, 2.7, 4000)).astype(np.float32)
+    tiny = (rng.random(500) * 2.0 ** -6).astype(np.float32)
+    test = np.concatenate([v, mids, -mids, rand, tiny, -tiny,
+                           np.array([0.0, -0.0, 448.0, 449.0, 463.9, 464.0, 1e9, -1e9], np.float32)])
+    np.testing.assert_array_equal(oracle.f32_to_e4m3(test, lib=lib), _e4m3_torch(test))
+    assert oracle.f32_to_e4m3(np.array([np.nan], np.float32), lib=lib)[0] == 0x7f
+
+
+def pin_quantize_rows(lib):
+    """Per 1x128 group: the scale is amax / 448 in fp32 and the codes are the
+    e4m3 rounding of x / scale (torch's conversion of numpy's fp32 quotient);
+    dequantized values are within half an e4m3 ulp (relative 2^-4) of x;
+    an all-zero group gets scale 1 and zero codes."""
+    rng = np.random.default_rng(24)
+    T, H = 17, 512
+    x = rng.standard_normal((T, H)).astype(np.float32) * 10.0 ** rng.uniform(-3, 3, (T, 1))
+    x[3, 128:256] = 0.0
+    xb = _bf16_bits(x)
+    xf = _bits_to_f32_torch(xb, "bf16").reshape(T, H // 128, 128)
+    q, sc = oracle.quantize_fp8_rows(xb, lib=lib)
+    amax = np.abs(xf).max(axis=2)
+    want_sc = np.where(amax > 0, (amax / np.float32(448.0)).astype(np.float32), np.float32(1.0))
+    np.testing.assert_array_equal(sc, want_sc)
+    quot = (xf / want_sc[:, :, None]).astype(np.float32)
+    np.testing.assert_array_equal(q, _e4m3_torch(quot).reshape(T, H))
+    deq = torch.from_numpy(q).view(torch.float8_e4m3fn).float().numpy().reshape(T, H // 128, 128)
+    deq = deq * sc[:, :, None]
+    assert np.all(np.abs(deq - xf) <= np.abs(xf) * 2.0 ** -4 + sc[:, :, None] * 2.0 ** -10)
+    assert np.all(q[3, 128:256] == 0) and sc[3, 1] == 1.0
+
+
 ALL_PINS = [
     pin_golden_prepare,
     pin_prepare_vs_numpy,
@@ -522,6 +574,8 @@ ALL_PINS = [
     pin_zeroing_vs_numpy,
     pin_golden_moe_sort,
     pin_moe_sort_vs_numpy,
+    pin_e4m3_conversion,
+    pin_quantize_rows,
 ]
 
 

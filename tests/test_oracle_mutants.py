@@ -58,6 +58,13 @@ MUTANTS = {
                                    "*num_tiles = (int32_t)((total + tile) / tile);"),
     "sort_window_ignores_offset": ("        int64_t g = read_id(ids, id_bytes, i) - local_offset;\n        if (g >= 0 && g < num_local) count[g] += 1;",
                                    "        int64_t g = read_id(ids, id_bytes, i);\n        if (g >= 0 && g < num_local) count[g] += 1;"),
+    "e4m3_bias_off_by_one": ("uint8_t code = (uint8_t)(((ex + 7) << 3) | ((int)q - 8));",
+                             "uint8_t code = (uint8_t)(((ex + 8) << 3) | ((int)q - 8));"),
+    "e4m3_subnormal_scale": ("float q = rintf(a * 0x1p9f);", "float q = rintf(a * 0x1p8f);"),
+    "fp8_scale_uses_240": ("float scale = amax > 0.0f ? amax / 448.0f : 1.0f;",
+                           "float scale = amax > 0.0f ? amax / 240.0f : 1.0f;"),
+    "fp8_group_amax_first_only": ("                if (v > amax) amax = v;",
+                                  "                if (e == 0) amax = v;"),
     "padding_ignores_total": ("int64_t limit = expert_offsets ? expert_offsets[E] : n_rows;",
                               "int64_t limit = n_rows;"),
 }
