@@ -61,7 +61,9 @@ def parse_args():
                         "separately: zero_padding (zero-fill the padding rows after "
                         "dispatch), output_memset (zero the output rows before combine), "
                         "moe_sort (tile-padded sort metadata over all experts, tiles of "
-                        "row_align rows, after prepare)")
+                        "row_align rows, after prepare), quantize_dispatch (bf16 rows "
+                        "quantized to fp8 e4m3 with 1x128 scales and dispatched, after "
+                        "dispatch)")
     return p.parse_args()
 
 
@@ -202,7 +204,18 @@ def main():
                                     workspace=sort_ws))
 
     extras = [e for e in args.extras.split(",") if e]
-    known = {"zero_padding": zero_padding, "output_memset": output_memset, "moe_sort": moe_sort}
+    xq = sq = None
+    if "quantize_dispatch" in extras:
+        if x.dtype != torch.bfloat16 or H % 128:
+            raise SystemExit("quantize_dispatch needs a bf16 workload with hidden % 128 == 0")
+        xq = torch.empty((cap, H), dtype=torch.float8_e4m3fn, device=dev)
+        sq = torch.empty((cap, H // 128), dtype=torch.float32, device=dev)
+
+    def quantize_dispatch():
+        mx.dispatch_rows_fp8(x, r["output_permutation"], k, xq, sq)
+
+    known = {"zero_padding": zero_padding, "output_memset": output_memset, "moe_sort": moe_sort,
+             "quantize_dispatch": quantize_dispatch}
     for e in extras:
         if e not in known:
             raise SystemExit(f"unknown --with stage {e!r}; known: {sorted(known)}")
@@ -210,6 +223,8 @@ def main():
     if "moe_sort" in extras:
         stages.append(("moe_sort", moe_sort))
     stages.append(("dispatch", dispatch))
+    if "quantize_dispatch" in extras:
+        stages.append(("quantize_dispatch", quantize_dispatch))
     if "zero_padding" in extras:
         stages.append(("zero_padding", zero_padding))
     if "output_memset" in extras:
@@ -261,6 +276,8 @@ def main():
     if "output_memset" in extras:
         has_pick = (r["output_permutation"].view(T, k) >= 0).any(dim=1).sum().item()
         nbytes["output_memset"] = int(has_pick) * H * out.element_size() + T * k * 4
+    if "quantize_dispatch" in extras:
+        nbytes["quantize_dispatch"] = T * H * 2 + n_valid * (H + H // 128 * 4) + T * k * 4
     if "moe_sort" in extras:
         scap = sort_out["permuted_idx_to_expanded_idx"].numel()
         nbytes["moe_sort"] = (T * k * ids.element_size() + T * k * 4 + scap * 4

@@ -23,7 +23,7 @@ import torch  # loads the HIP runtime this library must share; keep before CDLL
 
 __all__ = [
     "prepare_moe_input", "shuffle_rows", "dispatch_rows", "apply_shuffle_mul_sum",
-    "moe_output_memset", "zero_padding_rows", "moe_sort",
+    "moe_output_memset", "zero_padding_rows", "moe_sort", "dispatch_rows_fp8",
     "dispatch_capacity", "prepare_workspace_size", "empty_routing", "MxError",
     "library_path", "load_library", "EXPORTED_SYMBOLS",
 ]
@@ -40,7 +40,7 @@ EXPORTED_SYMBOLS = (
     "mx_status_string", "mx_last_hip_error", "mx_dispatch_capacity",
     "mx_prepare_workspace_size", "mx_prepare_moe_input", "mx_shuffle_rows",
     "mx_dispatch_rows", "mx_apply_shuffle_mul_sum", "mx_moe_output_memset",
-    "mx_zero_padding_rows", "mx_moe_sort",
+    "mx_zero_padding_rows", "mx_moe_sort", "mx_dispatch_rows_fp8",
 )
 
 
@@ -93,6 +93,8 @@ def load_library():
     lib.mx_moe_output_memset.argtypes = [vp, i64, i32, i64, vp, vp]
     lib.mx_zero_padding_rows.restype = ctypes.c_int
     lib.mx_zero_padding_rows.argtypes = [vp, i64, i64, vp, vp, i32, vp]
+    lib.mx_dispatch_rows_fp8.restype = ctypes.c_int
+    lib.mx_dispatch_rows_fp8.argtypes = [vp, i32, i64, i32, i64, vp, vp, vp, i64, vp]
     lib.mx_moe_sort.restype = ctypes.c_int
     lib.mx_moe_sort.argtypes = [vp, i32, i64, i32, i32, i32, i32, i32, vp, vp, i64, vp, vp, i64,
                                 vp, vp, vp, vp, sz, vp]
@@ -384,4 +386,29 @@ def moe_sort(topk_ids: torch.Tensor, num_experts: int, local_expert_offset: int,
         _ptr(res["num_non_exiting_tiles"]), _ptr(res["expert_offsets"]),
         _ptr(workspace), workspace.numel(), _stream(dev)), "moe_sort")
     return res
+
+
+def dispatch_rows_fp8(input: torch.Tensor, output_permutation: torch.Tensor, topk: int,
+                      output: torch.Tensor, output_scales: torch.Tensor) -> None:
+    """Quantize bf16 token rows to e4m3fn in 1x128 groups (scale = amax / 448)
+    and write codes and scales to each token's k dispatched rows, in place.
+    output: [rows, hidden] torch.float8_e4m3fn (or uint8); output_scales:
+    [rows, hidden / 128] float32."""
+    lib = load_library()
+    _check_dev("input", input)
+    dev = input.device
+    if input.dtype != torch.bfloat16 or input.dim() != 2:
+        raise TypeError("input must be a 2-D bfloat16 tensor")
+    T, H = input.shape
+    _check_dev("output_permutation", output_permutation, dev)
+    _check_i32("output_permutation", output_permutation, T * topk)
+    _check_dev("output", output, dev)
+    _check_dev("output_scales", output_scales, dev)
+    if output.element_size() != 1 or output.dim() != 2 or output.shape[1] != H:
+        raise ValueError("output must be [rows, hidden] of a 1-byte dtype")
+    if output_scales.dtype != torch.float32 or tuple(output_scales.shape) != (output.shape[0], H // 128):
+        raise ValueError("output_scales must be float32 [rows, hidden / 128]")
+    _call(lib.mx_dispatch_rows_fp8(_ptr(input), MX_BF16, T, topk, H, _ptr(output_permutation),
+                                   _ptr(output), _ptr(output_scales), output.shape[0],
+                                   _stream(dev)), "dispatch_rows_fp8")
 

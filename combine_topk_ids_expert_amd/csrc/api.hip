@@ -273,4 +273,26 @@ mx_status mx_moe_sort(const void* topk_ids, int32_t ids_dtype, int64_t num_token
     return hip_status(mxmoe::launch_route(a, static_cast<hipStream_t>(stream)));
 }
 
+mx_status mx_dispatch_rows_fp8(const void* src, int32_t src_dtype, int64_t num_tokens,
+                               int32_t topk, int64_t hidden, const int32_t* output_permutation,
+                               void* dst_q, float* dst_scales, int64_t num_dst_rows,
+                               void* stream) {
+    if (src_dtype != MX_BF16) return MX_ERR_UNSUPPORTED_DTYPE;
+    if (num_tokens < 0 || topk < 1 || num_tokens > kMax31 / topk || hidden < 128 ||
+        hidden % 128 != 0 || hidden > (int64_t)65535 * 1024 * 8 || num_dst_rows < 0 ||
+        num_dst_rows > kMax31)
+        return MX_ERR_INVALID_ARGUMENT;
+    if (num_tokens > 0 && (src == nullptr || output_permutation == nullptr ||
+                           (num_dst_rows > 0 && (dst_q == nullptr || dst_scales == nullptr))))
+        return MX_ERR_INVALID_ARGUMENT;
+    if (!aligned(src, 16) || !aligned(dst_q, 16) || !aligned(dst_scales, 4) ||
+        !aligned(output_permutation, 4))
+        return MX_ERR_MISALIGNED;
+    if (num_tokens == 0 || num_dst_rows == 0) return MX_OK;
+    return hip_status(mxmoe::launch_dispatch_quant_fp8(src, num_tokens, topk, hidden,
+                                                       output_permutation, dst_q, dst_scales,
+                                                       num_dst_rows,
+                                                       static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

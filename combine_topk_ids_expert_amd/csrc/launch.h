@@ -61,4 +61,9 @@ hipError_t launch_zero_padding(void* rows, int64_t num_rows, int64_t row_bytes,
 hipError_t launch_output_memset(void* out, int64_t num_tokens, int32_t topk, int64_t row_bytes,
                                 const int32_t* expanded_to_permuted, hipStream_t stream);
 
+hipError_t launch_dispatch_quant_fp8(const void* src, int64_t num_tokens, int32_t topk,
+                                     int64_t hidden, const int32_t* output_perm, void* dst_q,
+                                     float* dst_scales, int64_t num_dst_rows,
+                                     hipStream_t stream);
+
 }  // namespace mxmoe

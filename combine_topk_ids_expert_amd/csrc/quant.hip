@@ -1,0 +1,130 @@
+// Dispatch with FP8 quantization on the way: every bf16 token row is cut into
+// 1 x 128 groups, each group quantized to OCP e4m3fn with one fp32 scale,
+// and the codes and scales are written to the token's k dispatched rows (the
+// input quantization the TensorRT-LLM page "Enable CuteDSL MoE with Large EP"
+// runs before its MoE, fused into the row scatter; the 1 x 128 block scales
+// of the sglang prepare_moe_input page's FP8 path).
+//
+// Per group: amax = max |x|, scale = amax / 448 (1 for an all-zero group),
+// code = e4m3fn(x / scale) rounded to nearest even and saturated at 448.
+// The division is the IEEE one (hipcc's default correctly rounded fp32
+// division), so the codes do not depend on launch shapes.
+//
+// A workgroup holds one token (or a chunk of a long row); each thread owns 16
+// consecutive elements (two 16-byte loads, one 16-byte store of codes per
+// destination) and 8 threads form a group, whose amax is reduced with lane
+// shuffles inside the wave.  A wave covers 8 groups; their scales are
+// gathered into lanes 0..7 so each destination gets one contiguous 32-byte
+// scale store per wave.
+#include "device_common.h"
+#include "launch.h"
+
+namespace mxmoe {
+namespace {
+
+constexpr int kGroupElems = 128;
+constexpr int kElemsPerThread = 16;
+constexpr int kThreadsPerGroup = kGroupElems / kElemsPerThread;   // 8
+constexpr int kGroupsPerWave = kWave / kThreadsPerGroup;          // 8
+constexpr int kMaxQuantThreads = 1024;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// binary32 -> OCP e4m3fn by integer rounding of the significand: keep 3
+// fraction bits (normal range, exponent >= -6) or units of 2^-9 (subnormal
+// range), round to nearest even, saturate at 448 (0x7e); NaN -> 0x7f.
+__device__ __forceinline__ uint32_t e4m3_code(float f) {
+    const uint32_t u = __float_as_uint(f);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7fffffffu;
+    if (a > 0x7f800000u) return 0x7fu;
+    if (a >= 0x43e00000u) return sign | 0x7eu;          // |f| >= 448
+    const int ex = (int)(a >> 23) - 127;
+    if (ex < -10) return sign;                          // below 2^-10: rounds to zero
+    const uint32_t full = (a & 0x7fffffu) | 0x800000u;
+    const int shift = ex >= -6 ? 20 : 14 - ex;          // 20..24
+    uint32_t q = full >> shift;
+    const uint32_t rem = full & ((1u << shift) - 1u);
+    const uint32_t half = 1u << (shift - 1);
+    if (rem > half || (rem == half && (q & 1u))) q += 1u;
+    if (ex < -6) return sign | q;                       // q == 8 is the smallest normal
+    const uint32_t code = ((uint32_t)(ex + 7) << 3) + (q - 8u);
+    return sign | (code > 0x7eu ? 0x7eu : code);
+}
+
+// Token blockIdx.x, elements [(blockIdx.y * blockDim.x + tid) * 16, +16).
+__global__ __launch_bounds__(kMaxQuantThreads) void dispatch_quant_fp8_kernel(
+    const uint16_t* __restrict__ src, int64_t hidden, int32_t topk,
+    const int32_t* __restrict__ output_perm, uint8_t* __restrict__ dst_q,
+    float* __restrict__ dst_scales, int64_t num_dst_rows) {
+    const int64_t t = blockIdx.x;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t col = ((int64_t)blockIdx.y * blockDim.x + threadIdx.x) * kElemsPerThread;
+    const bool live = col < hidden;                    // whole groups: a group is live or not
+    u32x4 v0 = {0u, 0u, 0u, 0u}, v1 = {0u, 0u, 0u, 0u};
+    if (live) {
+        const u32x4* p = reinterpret_cast<const u32x4*>(src + t * hidden + col);
+        v0 = __builtin_nontemporal_load(p);
+        v1 = __builtin_nontemporal_load(p + 1);
+    }
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[2 * i] = __uint_as_float(v0[i] << 16);
+        x[2 * i + 1] = __uint_as_float(v0[i] & 0xffff0000u);
+        x[8 + 2 * i] = __uint_as_float(v1[i] << 16);
+        x[8 + 2 * i + 1] = __uint_as_float(v1[i] & 0xffff0000u);
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[i]));
+#pragma unroll
+    for (int d = 1; d < kThreadsPerGroup; d <<= 1) amax = fmaxf(amax, __shfl_xor(amax, d, kWave));
+    const float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
+    u32x4 codes;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+        codes[w] = e4m3_code(x[4 * w] / scale) | (e4m3_code(x[4 * w + 1] / scale) << 8) |
+                   (e4m3_code(x[4 * w + 2] / scale) << 16) |
+                   (e4m3_code(x[4 * w + 3] / scale) << 24);
+    // Lanes 0..7 take the scales of this wave's 8 groups, in group order.
+    const float wave_scale = __shfl(scale, (lane & (kGroupsPerWave - 1)) * kThreadsPerGroup, kWave);
+    const int64_t groups = hidden / kGroupElems;
+    const int64_t wave_group0 = (col - (int64_t)lane * kElemsPerThread) / kGroupElems;
+    const bool scale_lane = lane < kGroupsPerWave && wave_group0 + lane < groups;
+    const int32_t* rows = output_perm + t * topk;
+    for (int j0 = 0; j0 < topk; j0 += kWave) {         // wave-uniform
+        const int nj = topk - j0 < kWave ? topk - j0 : kWave;
+        int my_r = lane < nj ? rows[j0 + lane] : -1;
+        if (my_r >= num_dst_rows) my_r = -1;
+        for (int j = 0; j < nj; ++j) {
+            const int32_t r = __builtin_amdgcn_readlane(my_r, j);
+            if (r < 0) continue;
+            if (live)
+                __builtin_nontemporal_store(codes, reinterpret_cast<u32x4*>(dst_q + (int64_t)r * hidden + col));
+            if (scale_lane)
+                __builtin_nontemporal_store(wave_scale, dst_scales + (int64_t)r * groups + wave_group0 + lane);
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_dispatch_quant_fp8(const void* src, int64_t num_tokens, int32_t topk,
+                                     int64_t hidden, const int32_t* output_perm, void* dst_q,
+                                     float* dst_scales, int64_t num_dst_rows,
+                                     hipStream_t stream) {
+    if (num_tokens == 0 || num_dst_rows == 0) return hipSuccess;
+    const int64_t threads_needed = hidden / kElemsPerThread;
+    const int64_t chunks = (threads_needed + kMaxQuantThreads - 1) / kMaxQuantThreads;
+    int64_t threads = (threads_needed + chunks - 1) / chunks;
+    threads = (threads + kWave - 1) / kWave * kWave;
+    const dim3 grid((unsigned)num_tokens, (unsigned)chunks, 1);
+    dispatch_quant_fp8_kernel<<<grid, (unsigned)threads, 0, stream>>>(
+        static_cast<const uint16_t*>(src), hidden, topk, output_perm,
+        static_cast<uint8_t*>(dst_q), dst_scales, num_dst_rows);
+    return hipGetLastError();
+}
+
+}  // namespace mxmoe

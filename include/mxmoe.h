@@ -164,6 +164,30 @@ mx_status mx_dispatch_rows(const void* src, int64_t num_tokens, int32_t topk, in
                            void* stream);
 
 /*
+ * dispatch_rows_fp8 -- dispatch with FP8 quantization fused in: every token
+ * row is quantized in 1 x 128 groups to OCP e4m3fn codes with one fp32 scale
+ * per group (the input quantization the TensorRT-LLM page "Enable CuteDSL
+ * MoE with Large EP" performs before its MoE; the 1 x 128 block scales of
+ * the sglang page's FP8 path), and the codes and scales go to the token's k
+ * dispatched rows:
+ *
+ *   per group G of 128 elements of src[t]:
+ *     amax  = max |x|,  scale = amax / 448 (1 when amax == 0)
+ *     code  = e4m3fn(x / scale), round to nearest even, saturate at 448
+ *   dst_q[output_permutation[t*k+j]][h]      = code(src[t][h])
+ *   dst_scales[output_permutation[t*k+j]][G] = scale(G)
+ *
+ * fp32 arithmetic with IEEE division.  Destinations outside [0,
+ * num_dst_rows) are skipped.  src [T, hidden] MX_BF16 (finite values),
+ * 16-byte aligned; dst_q [num_dst_rows, hidden] bytes, 16-byte aligned;
+ * dst_scales [num_dst_rows, hidden / 128] fp32; hidden a multiple of 128.
+ */
+mx_status mx_dispatch_rows_fp8(const void* src, int32_t src_dtype, int64_t num_tokens,
+                               int32_t topk, int64_t hidden, const int32_t* output_permutation,
+                               void* dst_q, float* dst_scales, int64_t num_dst_rows,
+                               void* stream);
+
+/*
  * apply_shuffle_mul_sum -- gather, scale, reduce (sglang page, "Changes"
  * item 3: FP32 accumulation, fp16 / bf16 / fp32):
  *

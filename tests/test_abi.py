@@ -185,3 +185,18 @@ def test_moe_sort_rejects(lib):
     assert _sort(lib, T=65536, cap=65536 * 8 + 32 * 127, mt=(65536 * 8 + 32 * 127) // 128 + 1,
                  ws=None) == WORKSPACE
 
+
+def test_dispatch_fp8_rejects(lib):
+    f = lib.mx_dispatch_rows_fp8
+    assert f(P, F16, 10, 8, 4096, P, P, P, 80, S) == DTYPE
+    assert f(P, BF16, 10, 0, 4096, P, P, P, 80, S) == INVALID
+    assert f(P, BF16, 10, 8, 100, P, P, P, 80, S) == INVALID       # not a multiple of 128
+    assert f(P, BF16, 10, 8, 0, P, P, P, 80, S) == INVALID
+    assert f(None, BF16, 10, 8, 4096, P, P, P, 80, S) == INVALID
+    assert f(P, BF16, 10, 8, 4096, P, None, P, 80, S) == INVALID
+    assert f(P, BF16, 10, 8, 4096, P, P, None, 80, S) == INVALID
+    assert f(P + 8, BF16, 10, 8, 4096, P, P, P, 80, S) == MISALIGNED
+    assert f(P, BF16, 10, 8, 4096, P, P + 8, P, 80, S) == MISALIGNED
+    assert f(P, BF16, 10, 8, 4096, P + 2, P, P, 80, S) == MISALIGNED
+    assert f(P, BF16, 0, 8, 4096, P, P, P, 80, S) == OK
+
