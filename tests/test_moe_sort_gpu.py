@@ -47,6 +47,7 @@ def _check(ids, E, L0, EL, S, ids_dtype=torch.int64):
     (4000, 128, 8, 100, 28, 1, "zipf"),           # tile of one row
     (700, 40, 70, 5, 30, 16, "dups"),             # topk > 64
     (2000, 1024, 8, 512, 512, 32, "uniform"),
+    (9000, 256, 8, 32, 64, 128, "uniform"),      # tiles longer than 512 picks
 ])
 @pytest.mark.parametrize("ids_dtype", [torch.int32, torch.int64])
 def test_moe_sort_matches_oracle(T, E, k, L0, EL, S, mode, ids_dtype):

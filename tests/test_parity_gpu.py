@@ -40,6 +40,11 @@ def _print_case(*args):
     (1000, 256, 8, 128, "uniform", 0.0),        # one-launch path, padded
     (1024, 256, 8, 1, "uniform", 0.0),          # exactly 8192 picks
     (1025, 256, 8, 1, "uniform", 0.0),          # first multi-tile size
+    (8192, 256, 8, 1, "uniform", 0.0),          # 65536 picks: 128 tiles of 512
+    (8193, 256, 8, 128, "uniform", 0.02),       # tiles grow past 512 picks
+    (3000, 1000, 8, 4, "uniform", 0.05),        # E not a power of two, invalid ids
+    (2000, 100, 8, 8, "k_hot", 0.0),
+    (4000, 8, 4, 1, "dups", 0.0),               # few experts, many duplicates
     (3001, 256, 8, 128, "uniform", 0.05),       # several tiles, ragged tail, invalid ids
     (4096, 256, 8, 128, "uniform", 0.0),
     (5000, 256, 8, 1, "k_hot", 0.0),
