@@ -31,14 +31,42 @@ __device__ __forceinline__ uint64_t match_key(int key, int nbits) {
     return key >= 0 ? m : 0ull;
 }
 
-// Inclusive prefix sum across the wave.
+// ---- lane arithmetic with DPP ----------------------------------------------
+// Data-parallel-primitive operand modifiers move values between lanes in
+// registers (no LDS round trip, unlike ds_bpermute behind __shfl*).  Control
+// codes (GFX9 DPP): quad_perm is 0x00-0xff (two bits per lane of a quad),
+// row_shr:n is 0x110 + n, row_mirror 0x140, row_half_mirror 0x141,
+// row_bcast:15 0x142, row_bcast:31 0x143.  With old = 0 a lane whose source
+// lies outside its row, or whose row is masked off, adds 0.
+template <int Ctrl, int RowMask = 0xf>
+__device__ __forceinline__ int dpp(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, Ctrl, RowMask, 0xf, false);
+}
+
+// Inclusive prefix sum across the wave: Hillis-Steele inside each row of 16
+// lanes (row_shr 1, 2, 4, 8), then row 1 and row 3 add the last lane of the
+// row before them (row_bcast:15), then rows 2 and 3 add lane 31
+// (row_bcast:31).
 __device__ __forceinline__ int wave_inclusive_sum(int v) {
-    const int lane = lane_id();
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const int o = __shfl_up(v, d, kWave);
-        if (lane >= d) v += o;
-    }
+    v += dpp<0x111>(v);
+    v += dpp<0x112>(v);
+    v += dpp<0x114>(v);
+    v += dpp<0x118>(v);
+    v += dpp<0x142, 0xa>(v);
+    v += dpp<0x143, 0xc>(v);
+    return v;
+}
+
+// Sum over aligned groups of L lanes (L a power of two, 1..16, wave-uniform);
+// every lane of a group gets the group's sum.  Butterfly: lane ^ 1 and
+// lane ^ 2 by quad_perm [1,0,3,2] and [2,3,0,1], then the two quads of a
+// half-row swap (row_half_mirror) and the two half-rows of a row swap
+// (row_mirror).
+__device__ __forceinline__ int group_sum(int v, int L) {
+    if (L >= 2) v += dpp<0xb1>(v);
+    if (L >= 4) v += dpp<0x4e>(v);
+    if (L >= 8) v += dpp<0x141>(v);
+    if (L >= 16) v += dpp<0x140>(v);
     return v;
 }
 

@@ -32,7 +32,7 @@ constexpr int kRouteThreads = 512;
 constexpr int kRouteWaves = kRouteThreads / kWave;
 constexpr int kBatch = 8;                 // 64-pick groups loaded per round
 constexpr int kMaxE = 1024;
-constexpr int kTableBatch = 8;            // 16-byte count-table loads in flight per thread
+constexpr int kTableBatch = 16;           // 16-byte count-table loads in flight per thread
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #ifndef MXMOE_FUSED_MAX
@@ -62,14 +62,6 @@ struct Shape {
 
 __device__ __forceinline__ int round_up_i(int v, int a) { return (v + a - 1) / a * a; }
 
-template <typename IdT>
-__device__ __forceinline__ int load_key(const IdT* ids, int64_t i, int64_t end, int E,
-                                        int32_t id_offset) {
-    if (i >= end) return -1;
-    const int64_t v = (int64_t)ids[i] - id_offset;
-    return (v >= 0 && v < E) ? (int)v : -1;
-}
-
 // This wave's stretch [w0, w1) of the tile [t0, t1): equal stretches of a
 // multiple of 64 picks, in wave order.
 __device__ __forceinline__ void wave_stretch(int64_t t0, int64_t t1, int wave, int64_t& w0,
@@ -81,31 +73,69 @@ __device__ __forceinline__ void wave_stretch(int64_t t0, int64_t t1, int wave, i
 }
 
 // One round of up to kBatch 64-pick groups starting at g0, keys loaded.
+// Groups wholly past w1 are skipped (a wave-uniform test).  Inside a group,
+// lanes past w1 load the stretch's last id instead of branching around the
+// load, so all loads are issued before the first wait (a load under a
+// per-lane branch gets its own wait and the round would cost kBatch
+// latencies); their keys are then set to -1.
+//
+// Split in two so a caller can issue the loads early and convert later:
+// load_raw issues the loads, raw_to_keys turns the ids into keys (a key is
+// the id minus id_offset, or -1 past w1 and outside [0, E)).
+template <typename IdT>
+__device__ __forceinline__ void load_raw(const IdT* ids, int64_t g0, int64_t w1,
+                                         IdT (&v)[kBatch]) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+        const int64_t i = g0 + b * kWave + lane;
+        v[b] = g0 + b * kWave < w1 ? ids[i < w1 ? i : w1 - 1] : IdT(0);
+    }
+}
+
+template <typename IdT>
+__device__ __forceinline__ void raw_to_keys(const IdT (&v)[kBatch], int64_t g0, int64_t w1, int E,
+                                            int32_t id_offset, int (&key)[kBatch]) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+        const int64_t i = g0 + b * kWave + lane;
+        const int64_t x = (int64_t)v[b] - id_offset;
+        key[b] = (i < w1 && x >= 0 && x < E) ? (int)x : -1;
+    }
+}
+
 template <typename IdT>
 __device__ __forceinline__ void load_keys(const IdT* ids, int64_t g0, int64_t w1, int E,
                                           int32_t id_offset, int (&key)[kBatch]) {
-    const int lane = lane_id();
-#pragma unroll
-    for (int b = 0; b < kBatch; ++b) key[b] = load_key(ids, g0 + b * kWave + lane, w1, E, id_offset);
+    IdT v[kBatch];
+    load_raw(ids, g0, w1, v);
+    raw_to_keys(v, g0, w1, E, id_offset, key);
 }
 
-// Count a round of keys per expert into this wave's LDS row.
-__device__ __forceinline__ void count_keys(const int (&key)[kBatch], const Shape& s, int* row) {
+// Count a round of keys per expert into this wave's LDS row.  Groups wholly
+// past w1 hold no keys and are skipped: a stretch is often a single group,
+// and matching an empty group costs as much as a full one.
+__device__ __forceinline__ void count_keys(const int (&key)[kBatch], int64_t g0, int64_t w1,
+                                           const Shape& s, int* row) {
 #pragma unroll
     for (int b = 0; b < kBatch; ++b) {
+        if (g0 + b * kWave >= w1) break;                // wave-uniform
         const uint64_t m = match_key(key[b], s.nbits);
         if (key[b] >= 0 && lanes_below(m) == 0) row[key[b]] += __popcll(m);
     }
 }
 
 // Place a round of keys: row[e] holds the next free dispatched row of expert
-// e for this wave on entry and is advanced as picks are placed.
+// e for this wave on entry and is advanced as picks are placed (groups past
+// w1 skipped as in count_keys).
 __device__ __forceinline__ void scatter_keys(const int (&key)[kBatch], int64_t g0, int64_t w1,
                                              const Shape& s, int* row, int32_t* outp,
                                              int32_t* inp, int64_t inp_len) {
     const int lane = lane_id();
 #pragma unroll
     for (int b = 0; b < kBatch; ++b) {
+        if (g0 + b * kWave >= w1) break;                // wave-uniform
         const int64_t i = g0 + b * kWave + lane;
         const uint64_t m = match_key(key[b], s.nbits);
         const int rank = lanes_below(m);
@@ -127,7 +157,7 @@ __device__ void count_stretch(const IdT* ids, int64_t w0, int64_t w1, const Shap
     for (int64_t g0 = w0; g0 < w1; g0 += kBatch * kWave) {
         int key[kBatch];
         load_keys(ids, g0, w1, s.E, s.id_offset, key);
-        count_keys(key, s, row);
+        count_keys(key, g0, w1, s, row);
     }
 }
 
@@ -332,42 +362,67 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(RouteArgs 
     // A stretch of at most one round keeps its keys in registers for both
     // passes; they are requested first so their latency overlaps the table.
     const bool one_round = w1 - w0 <= kBatch * kWave;
-    int key[kBatch];
-    if (one_round) load_keys(ids, w0, w1, s.E, s.id_offset, key);
+    IdT raw[kBatch];
+    if (one_round) load_raw(ids, w0, w1, raw);
 
-    // Expert totals over all tiles and this tile's prefix: a thread per expert
-    // reads the expert's row of the count table with 16-byte loads, issued
-    // together (the row stride is a multiple of 4 tiles).
+    // Expert totals over all tiles and this tile's prefix.  A row of the count
+    // table is q = stride / 4 16-byte vectors (at most 32, since tiles <= 128).
+    // L lanes share a row (q rounded up to a power of two, at most 16), each
+    // taking vectors sub and sub + L, so one load instruction of a wave reads
+    // whole cache lines of 64 / L consecutive rows, where a row per lane would
+    // touch 64 lines per instruction.  The loads of a batch are issued
+    // together; each row's L partial sums are then added with DPP.
     const int stride = round_up_i(tiles, 4);
-    for (int e = tid; e < s.E; e += kRouteThreads) {
-        const u32x4* row = reinterpret_cast<const u32x4*>(a.workspace + (int64_t)e * stride);
-        int tot = 0, before = 0;
-        for (int q0 = 0; q0 < stride / 4; q0 += kTableBatch) {
-            u32x4 v[kTableBatch];
+    const int q = stride / 4;
+    int L = 1;
+    while (L < q && L < 16) L <<= 1;
+    const bool two = q > L;                           // wave-uniform
+    const int rpi = kWave / L;                        // rows per wave instruction
+    const int lane = tid & (kWave - 1), sub = lane & (L - 1), slot = lane / L;
+    const int iters = (s.E + kRouteWaves * rpi - 1) / (kRouteWaves * rpi);
+    const int sub0 = sub < q ? sub : q - 1, sub1 = sub + L < q ? sub + L : q - 1;
+    constexpr int kRowBatch = kTableBatch / 2;        // two vectors per row at most
+    for (int it0 = 0; it0 < iters; it0 += kRowBatch) {
+        u32x4 v0[kRowBatch], v1[kRowBatch];
 #pragma unroll
-            for (int u = 0; u < kTableBatch; ++u)
-                if (q0 + u < stride / 4) v[u] = row[q0 + u];
+        for (int u = 0; u < kRowBatch; ++u) {
+            const int e = ((it0 + u) * kRouteWaves + wave) * rpi + slot;
+            const u32x4* row = reinterpret_cast<const u32x4*>(
+                a.workspace + (int64_t)(e < s.E ? e : s.E - 1) * stride);
+            const bool live = it0 + u < iters;           // wave-uniform
+            v0[u] = live ? row[sub0] : u32x4{0u, 0u, 0u, 0u};
+            v1[u] = live && two ? row[sub1] : u32x4{0u, 0u, 0u, 0u};
+        }
 #pragma unroll
-            for (int u = 0; u < kTableBatch; ++u) {
+        for (int u = 0; u < kRowBatch; ++u) {
+            if (it0 + u >= iters) break;                 // wave-uniform
+            const int e = ((it0 + u) * kRouteWaves + wave) * rpi + slot;
+            int tot = 0, before = 0;
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const int g = (q0 + u) * 4 + c;
-                    const int x = g < tiles ? (int)v[u][c] : 0;
-                    tot += x;
-                    before += g < b ? x : 0;
-                }
+            for (int c = 0; c < 8; ++c) {
+                const int g = c < 4 ? sub * 4 + c : (sub + L) * 4 + c - 4;
+                const int x = g < tiles ? (int)(c < 4 ? v0[u][c] : v1[u][c - 4]) : 0;
+                tot += x;
+                before += g < b ? x : 0;
+            }
+            tot = group_sum(tot, L);
+            before = group_sum(before, L);
+            if (sub == 0 && e < s.E) {
+                cnt[e] = tot;
+                pre[e] = before;
             }
         }
-        cnt[e] = tot;
-        pre[e] = before;
     }
     for (int e = tid; e < s.E; e += kRouteThreads)
 #pragma unroll
         for (int w = 0; w < kRouteWaves; ++w) rows[w][e] = 0;
     __syncthreads();
     const int R = scan_experts(a, cnt, off, tmp, b == 0);
-    if (one_round) count_keys(key, s, rows[wave]);
-    else count_stretch<IdT>(ids, w0, w1, s, rows[wave]);
+    int key[kBatch];
+    if (one_round) {
+        raw_to_keys(raw, w0, w1, s.E, s.id_offset, key);
+        count_keys(key, w0, w1, s, rows[wave]);
+    } else count_stretch<IdT>(ids, w0, w1, s, rows[wave]);
     __syncthreads();
     for (int e = tid; e < s.E; e += kRouteThreads) {
         int run = off[e] + pre[e];
