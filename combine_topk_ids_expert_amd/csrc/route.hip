@@ -277,6 +277,13 @@ __device__ void fill_tiles(const RouteArgs& a, const int* cnt, const int* off, i
 
 // ---- single workgroup: count, scan and scatter in one launch -----------------
 
+// A wave's stretch is at most kFusedRounds rounds of picks, so its ids are
+// loaded once, all at the start, and kept in registers for both passes.
+constexpr int kFusedRounds = 2;
+constexpr int64_t kRoundPicks = (int64_t)kBatch * kWave;
+static_assert(kFusedMax <= kFusedRounds * kRoundPicks * kRouteWaves,
+              "single-launch routing keeps at most kFusedRounds rounds per wave");
+
 template <typename IdT>
 __global__ __launch_bounds__(kRouteThreads) void route_fused_kernel(RouteArgs a, Shape s) {
     __shared__ int rows[kRouteWaves][kMaxE];
@@ -285,14 +292,22 @@ __global__ __launch_bounds__(kRouteThreads) void route_fused_kernel(RouteArgs a,
     __shared__ int tmp[160];
     const int tid = threadIdx.x, wave = tid / kWave;
     const IdT* ids = static_cast<const IdT*>(a.ids);
+    int64_t w0, w1;
+    wave_stretch(0, s.n, wave, w0, w1);
+    IdT raw[kFusedRounds][kBatch];
+#pragma unroll
+    for (int r = 0; r < kFusedRounds; ++r) load_raw(ids, w0 + r * kRoundPicks, w1, raw[r]);
 
     for (int e = tid; e < s.E; e += kRouteThreads)
 #pragma unroll
         for (int w = 0; w < kRouteWaves; ++w) rows[w][e] = 0;
     __syncthreads();
-    int64_t w0, w1;
-    wave_stretch(0, s.n, wave, w0, w1);
-    count_stretch<IdT>(ids, w0, w1, s, rows[wave]);
+    int key[kFusedRounds][kBatch];
+#pragma unroll
+    for (int r = 0; r < kFusedRounds; ++r) {
+        raw_to_keys(raw[r], w0 + r * kRoundPicks, w1, s.E, s.id_offset, key[r]);
+        count_keys(key[r], w0 + r * kRoundPicks, w1, s, rows[wave]);
+    }
     __syncthreads();
     for (int e = tid; e < s.E; e += kRouteThreads) {
         int run = 0;
@@ -311,8 +326,10 @@ __global__ __launch_bounds__(kRouteThreads) void route_fused_kernel(RouteArgs a,
 #pragma unroll
         for (int w = 0; w < kRouteWaves; ++w) rows[w][e] += off[e];
     __syncthreads();
-    scatter_stretch<IdT>(ids, w0, w1, s, rows[wave], a.output_perm, a.input_perm,
-                         a.input_perm_len);
+#pragma unroll
+    for (int r = 0; r < kFusedRounds; ++r)
+        scatter_keys(key[r], w0 + r * kRoundPicks, w1, s, rows[wave], a.output_perm,
+                     a.input_perm, a.input_perm_len);
     fill_unused_rows(a, cnt, off, R, wave, kRouteWaves, tid, kRouteThreads);
     fill_tiles(a, cnt, off, R, wave, kRouteWaves, tid, kRouteThreads);
 }
