@@ -4,7 +4,7 @@ Metadata, permutations and dispatched rows must match bit for bit; the
 combine must be within rtol 1.6e-2 / atol 1e-2 (16-bit output) or rtol 1e-5
 (fp32 output), and is also expected to match bit for bit because both sides
 take the same fused multiply-add order.  Sizes span several routing tiles
-(4096 picks each) with ragged tails, rows wider than one workgroup chunk,
+(512 to 4096 picks each) with ragged tails, rows wider than one workgroup chunk,
 and every workload's real shape at a reduced token count; the full-size
 workloads are checked on sampled outputs and whole-array properties.
 """
@@ -125,6 +125,28 @@ def test_dispatch_misaligned_base():
     x = big[1:].view(T, H)                               # 2-byte offset
     assert x.data_ptr() % 16 != 0
     gu.check_dispatch(x, meta, k)
+
+
+def test_calls_follow_the_current_stream():
+    """The binding launches on torch's current stream: inside a side-stream
+    context the raw handle it passes is that stream's, and prepare, dispatch
+    and combine queued there (with the poisoning fills of their outputs on
+    the same stream) still match the oracle."""
+    _print_case("side stream")
+    dev = torch.device(DEV)
+    assert mx._stream(dev) == torch.cuda.current_stream(dev).cuda_stream
+    side = torch.cuda.Stream(device=dev)
+    rng = np.random.default_rng(77)
+    T, E, k, H = 3001, 256, 8, 1024
+    ids = routing.uniform_topk(rng, T, E, k)
+    with torch.cuda.stream(side):
+        assert mx._stream(dev) == side.cuda_stream
+        assert side.cuda_stream != torch.cuda.default_stream(dev).cuda_stream
+        meta = gu.check_prepare(ids, E, 128)
+        gu.check_dispatch(routing.normal_rows(T, H, "bf16", seed=5, device=DEV), meta, k)
+        y = routing.normal_rows(meta["input_permutation"].size, H, "bf16", seed=6, device=DEV)
+        f = torch.from_numpy(routing.softmax_weights(rng, T, k)).to(DEV)
+        gu.check_combine(y, meta["_t"]["output_permutation"], f, torch.bfloat16, T)
 
 
 def test_dispatch_fp8_with_scale_rows():
