@@ -198,6 +198,44 @@ def test_combine_shapes(T, H, k, R):
     gu.check_combine(y, perm, f, torch.float32, T)
 
 
+@pytest.mark.parametrize("ydt,odt", [
+    (torch.bfloat16, torch.bfloat16), (torch.bfloat16, torch.float16),
+    (torch.float32, torch.float32), (torch.float16, torch.bfloat16),
+])
+def test_combine_non_finite(ydt, odt):
+    """NaN stays NaN and infinities propagate: y rows holding NaN, +inf and
+    -inf (so some sums are inf - inf), and finite values large enough that
+    the weighted sum overflows the output format to +-inf.  NaN payloads are
+    not unique (the hardware conversion may pick another quiet NaN), so the
+    NaN positions must agree and every other output must match bit for bit."""
+    _print_case("combine non-finite", ydt, odt)
+    T, H, k, R = 40, 256, 4, 60
+    rng = np.random.default_rng(31)
+    big = {torch.float16: 6e4, torch.bfloat16: 3e38, torch.float32: 3e38}[ydt]
+    yh = rng.standard_normal((R, H)).astype(np.float32)
+    yh[rng.random((R, H)) < 0.03] = np.nan
+    yh[rng.random((R, H)) < 0.03] = np.inf
+    yh[rng.random((R, H)) < 0.03] = -np.inf
+    yh[rng.random((R, H)) < 0.05] = big
+    y = torch.from_numpy(yh).to(ydt).to(DEV)
+    perm = torch.from_numpy(rng.integers(0, R, T * k).astype(np.int32)).to(DEV)
+    f = torch.from_numpy(rng.uniform(0.5, 2.0, (T, k)).astype(np.float32)).to(DEV)
+    out = torch.zeros(T, H, dtype=odt, device=DEV)
+    mx.apply_shuffle_mul_sum(y, out, perm, f)
+    torch.cuda.synchronize()
+    want = oracle.apply_shuffle_mul_sum(gu.bits(y), gu.code(ydt), gu.bits(perm), gu.bits(f), "f32",
+                                        T, k, gu.code(odt))
+    got = gu.bits(out)
+    got_nan = torch.isnan(out.float()).cpu().numpy()
+    if odt == torch.float32:
+        want_nan = np.isnan(want)
+    else:
+        want_nan = torch.isnan(torch.from_numpy(want.view(np.int16)).view(odt).float()).numpy()
+    assert want_nan.any() and np.isinf(out.float().cpu().numpy()).any()
+    np.testing.assert_array_equal(got_nan, want_nan)
+    np.testing.assert_array_equal(got[~got_nan], want[~want_nan])
+
+
 def test_combine_misaligned_base():
     _print_case("combine misaligned")
     T, H, k, R = 16, 256, 4, 64

@@ -75,6 +75,23 @@ def test_fp8_dispatch_edge_groups():
     _check(_bf16(x), ids, 3, 1)
 
 
+def test_fp8_dispatch_nan_and_inf():
+    """Non-finite inputs, same reading on both sides: amax skips NaN, a NaN
+    element codes to 0x7f; an infinite element makes the group's scale
+    infinite, so its finite elements code to signed zero and the infinite
+    ones (inf / inf) to 0x7f; a group of NaN only has amax 0 and scale 1."""
+    print("case: fp8 dispatch nan/inf", flush=True)
+    H = 128 * 5
+    x = np.linspace(-3, 3, 2 * H, dtype=np.float32).reshape(2, H)
+    x[0, 5] = np.nan                              # group 0: NaN among normals
+    x[0, 130] = np.inf                            # group 1: +inf
+    x[0, 260] = -np.inf                           # group 2: -inf
+    x[0, 300] = np.nan
+    x[1, 384:512] = np.nan                        # group 3 of row 1: NaN only
+    ids = np.array([[0, 2], [1, 0]], np.int64)
+    _check(_bf16(x), ids, 3, 1)
+
+
 def test_fp8_dispatch_full_size_zipf_bf16():
     """The Zipf workload's shape at full size (T = 16384, H = 4096, E = 128,
     top-8) with bf16 activations quantized on the way; every dispatched row's
