@@ -177,10 +177,13 @@ mx_status mx_dispatch_rows(const void* src, int64_t num_tokens, int32_t topk, in
  *   dst_q[output_permutation[t*k+j]][h]      = code(src[t][h])
  *   dst_scales[output_permutation[t*k+j]][G] = scale(G)
  *
- * fp32 arithmetic with IEEE division.  Destinations outside [0,
- * num_dst_rows) are skipped.  src [T, hidden] MX_BF16 (finite values),
- * 16-byte aligned; dst_q [num_dst_rows, hidden] bytes, 16-byte aligned;
- * dst_scales [num_dst_rows, hidden / 128] fp32; hidden a multiple of 128.
+ * fp32 arithmetic with IEEE division.  Non-finite inputs: amax skips NaN
+ * and a NaN codes to 0x7f; an infinity makes its group's scale infinite, so
+ * the group's finite values code to signed zero and its infinities to 0x7f.
+ * Destinations outside [0, num_dst_rows) are skipped.  src [T, hidden]
+ * MX_BF16, 16-byte aligned; dst_q [num_dst_rows, hidden] bytes, 16-byte
+ * aligned; dst_scales [num_dst_rows, hidden / 128] fp32; hidden a multiple
+ * of 128.
  */
 mx_status mx_dispatch_rows_fp8(const void* src, int32_t src_dtype, int64_t num_tokens,
                                int32_t topk, int64_t hidden, const int32_t* output_permutation,
