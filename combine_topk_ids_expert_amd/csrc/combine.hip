@@ -24,7 +24,6 @@ constexpr int kGroup = 8;      // columns per thread in the vector path
 constexpr int kPickBatch = 8;  // picks whose loads are issued together
 constexpr int kMaxThreads = 1024;
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // 8 consecutive elements of a row, moved with 16-byte accesses.  Expert
 // output rows are read exactly once, so the loads carry the non-temporal

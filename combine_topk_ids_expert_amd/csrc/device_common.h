@@ -8,6 +8,24 @@ namespace mxmoe {
 
 constexpr int kWave = 64;
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// 16-byte store of vector v at byte offset `off` of a row that starts at
+// `row` (the row base wave-uniform, the offset per lane), through a raw
+// buffer store whose cache policy is non-temporal and system-coherent
+// (sc0 nt sc1, policy bits 1 | 2 | 16 on gfx950).  For the scattered
+// write-once destination rows of dispatch this measured 1.5-2% faster on
+// MI355X than a plain non-temporal global store.  The buffer's extent is the
+// row, so a store past row_bytes would be dropped by the hardware; callers
+// only store inside it.  0x00020000 is the gfx9 raw-buffer format word.
+__device__ __forceinline__ void store16_stream(u32x4 v, uint8_t* row, int64_t row_bytes,
+                                               int64_t off) {
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(row, (short)0, (int)row_bytes, 0x00020000);
+    __builtin_amdgcn_raw_buffer_store_b128(v, rs, (int)off, 0, 1 | 2 | 16);
+}
+
 // Number of lanes below this one whose bit is set in `mask`.
 __device__ __forceinline__ int lanes_below(uint64_t mask) {
     return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),

@@ -34,7 +34,6 @@ constexpr int kBatch = 8;                 // 64-pick groups loaded per round
 constexpr int kMaxE = 1024;
 constexpr int kTableBatch = 16;           // 16-byte count-table loads in flight per thread
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #ifndef MXMOE_FUSED_MAX
 #define MXMOE_FUSED_MAX 8192
 #endif

@@ -20,8 +20,6 @@ namespace {
 
 constexpr int kMaxRowThreads = 1024;
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 template <int V> struct Vec;
 template <> struct Vec<16> { using T = u32x4; };
@@ -36,7 +34,8 @@ template <> struct Vec<1> { using T = uint8_t; };
 // part in the wave-uniform destination loop but access nothing.  The
 // destination indices sit one per lane and are broadcast with readlane;
 // destination rows are written once and not read again by this pass, so the
-// stores carry the non-temporal hint.
+// stores carry the non-temporal hint (16-byte ones through store16_stream,
+// which adds the system-coherent bits).
 template <typename T>
 __device__ __forceinline__ void copy_vector_to(const T* __restrict__ in, int64_t c, int64_t nvec,
                                                uint8_t* __restrict__ dst, int64_t row_bytes,
@@ -52,8 +51,12 @@ __device__ __forceinline__ void copy_vector_to(const T* __restrict__ in, int64_t
         if (my_r >= num_dst_rows) my_r = -1;
         for (int j = 0; j < nj; ++j) {
             const int32_t r = __builtin_amdgcn_readlane(my_r, j);
-            if (r < 0) continue;
-            if (live) __builtin_nontemporal_store(v, reinterpret_cast<T*>(dst + (int64_t)r * row_bytes) + c);
+            if (r < 0 || !live) continue;
+            uint8_t* row = dst + (int64_t)r * row_bytes;
+            if constexpr (sizeof(T) == 16)
+                store16_stream(v, row, row_bytes, c * 16);
+            else
+                __builtin_nontemporal_store(v, reinterpret_cast<T*>(row) + c);
         }
     }
 }

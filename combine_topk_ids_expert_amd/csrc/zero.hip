@@ -16,8 +16,6 @@ namespace {
 
 constexpr int kMaxZeroThreads = 1024;
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 template <int V> struct ZVec;
 template <> struct ZVec<16> { using T = u32x4; };
