@@ -23,6 +23,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -38,11 +39,19 @@ METRIC = "dispatch+combine tokens/s; achieved HBM GB/s vs MI355X peak"
 KERNEL_SOURCES = ("route.hip", "rows.hip", "combine.hip", "device_common.h")
 
 
+def _code_only(text: str) -> str:
+    """C++ source with comments removed and whitespace runs collapsed, so the
+    hash changes with the code, not with its comments."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return re.sub(r"\s+", " ", text).strip()
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "combine_topk_ids_expert_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "combine_topk_ids_expert_amd", "csrc", name)) as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -8,10 +8,12 @@
 // chunk of at most 1024 vectors of one row) and each thread moves exactly one
 // 16-byte vector: one load, then one store per destination.  Short-lived
 // workgroups with one access per thread sustained the highest write rate on
-// MI355X (several accesses per thread, or looping workgroups, wrote slower),
-// and the write-once destination rows are stored with the non-temporal hint.  Rows
-// whose byte width or base pointers are not multiples of 16 fall back to the
-// widest access width that divides them.
+// MI355X (several accesses per thread, or looping workgroups, wrote slower).
+// The write-once destination rows are stored non-temporal and system-coherent
+// (store16_stream), the source rows are loaded with the default policy: both
+// measured fastest of the cache policies tried.  Rows whose byte width or base
+// pointers are not multiples of 16 fall back to the widest access width that
+// divides them.
 #include "device_common.h"
 #include "launch.h"
 
