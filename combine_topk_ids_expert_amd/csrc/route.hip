@@ -13,7 +13,9 @@
 // stretches, the 64-pick groups and the lanes are each walked in ascending
 // pick order, base(wave, expert) + rank is the stable position.
 //
-//   small inputs: one workgroup counts, scans and scatters (one launch);
+//   small inputs (up to 1024 picks, or 2048 with little padding, where it
+//                measured faster): one workgroup counts, scans and scatters
+//                (one launch);
 //   larger inputs, two launches:
 //     count   -- one workgroup per tile writes the tile's count of every
 //                expert to the workspace, expert-major ([E][tiles]);
@@ -35,12 +37,19 @@ constexpr int kMaxE = 1024;
 constexpr int kTableBatch = 16;           // 16-byte count-table loads in flight per thread
 
 #ifndef MXMOE_FUSED_MAX
-#define MXMOE_FUSED_MAX 8192
+#define MXMOE_FUSED_MAX 2048
+#endif
+#ifndef MXMOE_FUSED_ALWAYS
+#define MXMOE_FUSED_ALWAYS 1024
 #endif
 #ifndef MXMOE_MAX_TILES
 #define MXMOE_MAX_TILES 128
 #endif
-constexpr int64_t kFusedMax = MXMOE_FUSED_MAX;  // single-launch path up to this many picks
+// Single-launch path: always up to kFusedAlways picks; up to kFusedMax when
+// input_permutation is at most twice the picks (little padding), since the
+// one workgroup also writes every padding and unused entry.
+constexpr int64_t kFusedMax = MXMOE_FUSED_MAX;
+constexpr int64_t kFusedAlways = MXMOE_FUSED_ALWAYS < MXMOE_FUSED_MAX ? MXMOE_FUSED_ALWAYS : MXMOE_FUSED_MAX;
 constexpr int64_t kMaxTiles = MXMOE_MAX_TILES;  // tiles of the two-launch path (at most)
 constexpr int64_t kTileQuantum = kRouteThreads; // tile sizes are multiples of this
 
@@ -233,14 +242,29 @@ __device__ int scan_experts(const RouteArgs& a, const int* cnt, int* off, int* t
 
 // -1 into the padding rows of every expert handled by this wave and into
 // the rows past the last segment, [R, inp_len), strided over all threads.
+// The wave's experts are first_wave, first_wave + wave_stride, ...; 64 of
+// them at a time go one per lane (one LDS read covers them all, where a
+// loop with a dependent LDS read per expert cost microseconds), and the
+// padding rows of those that have any are written 64 rows per store.
 __device__ void fill_unused_rows(const RouteArgs& a, const int* cnt, const int* off, int R,
                                  int first_wave, int wave_stride, int64_t first_thread,
                                  int64_t thread_stride) {
     const int lane = lane_id();
-    for (int e = first_wave; e < a.num_experts; e += wave_stride) {
-        const int c = cnt[e];
-        const int64_t r0 = (int64_t)off[e] + c, r1 = (int64_t)off[e] + round_up_i(c, a.row_align);
-        for (int64_t r = r0 + lane; r < r1; r += kWave) a.input_perm[r] = -1;
+    for (int j0 = 0; first_wave + j0 * wave_stride < a.num_experts; j0 += kWave) {
+        const int e = first_wave + (j0 + lane) * wave_stride;
+        int r0 = 0, n = 0;
+        if (e < a.num_experts) {
+            const int c = cnt[e];
+            r0 = off[e] + c;
+            n = round_up_i(c, a.row_align) - c;
+        }
+        uint64_t todo = __ballot(n > 0);
+        while (todo != 0ull) {                               // wave-uniform
+            const int l = __builtin_ctzll(todo);
+            todo &= todo - 1;
+            const int p0 = __builtin_amdgcn_readlane(r0, l), pn = __builtin_amdgcn_readlane(n, l);
+            for (int q = lane; q < pn; q += kWave) a.input_perm[(int64_t)p0 + q] = -1;
+        }
     }
     for (int64_t r = R + first_thread; r < a.input_perm_len; r += thread_stride)
         a.input_perm[r] = -1;
@@ -249,19 +273,34 @@ __device__ void fill_unused_rows(const RouteArgs& a, const int* cnt, const int* 
 // Tile maps of the tile-padded sort: the tiles [off[e], off[e] + padded
 // count) / row_align of every expert handled by this wave get the expert and
 // its row limit off[e] + cnt[e]; tiles past R / row_align get -1; the first
-// thread of the grid writes the totals.
+// thread of the grid writes the totals.  A wave's experts are taken 64 at a
+// time, one per lane, as in fill_unused_rows.
 __device__ void fill_tiles(const RouteArgs& a, const int* cnt, const int* off, int R,
                            int first_wave, int wave_stride, int64_t first_thread,
                            int64_t thread_stride) {
     if (a.tile_group == nullptr) return;
     const int lane = lane_id();
     const int S = a.row_align;
-    for (int e = first_wave; e < a.num_experts; e += wave_stride) {
-        const int c = cnt[e];
-        const int64_t q0 = off[e] / S, q1 = q0 + (c + S - 1) / S;
-        for (int64_t q = q0 + lane; q < q1; q += kWave) {
-            a.tile_group[q] = e;
-            a.tile_limit[q] = off[e] + c;
+    for (int j0 = 0; first_wave + j0 * wave_stride < a.num_experts; j0 += kWave) {
+        const int e = first_wave + (j0 + lane) * wave_stride;
+        int q0 = 0, nq = 0, lim = 0;
+        if (e < a.num_experts) {
+            const int c = cnt[e];
+            q0 = off[e] / S;
+            nq = (c + S - 1) / S;
+            lim = off[e] + c;
+        }
+        uint64_t todo = __ballot(nq > 0);
+        while (todo != 0ull) {                               // wave-uniform
+            const int l = __builtin_ctzll(todo);
+            todo &= todo - 1;
+            const int p0 = __builtin_amdgcn_readlane(q0, l), pn = __builtin_amdgcn_readlane(nq, l);
+            const int pl = __builtin_amdgcn_readlane(lim, l);
+            const int pe = first_wave + (j0 + l) * wave_stride;
+            for (int q = lane; q < pn; q += kWave) {
+                a.tile_group[(int64_t)p0 + q] = pe;
+                a.tile_limit[(int64_t)p0 + q] = pl;
+            }
         }
     }
     for (int64_t q = R / S + first_thread; q < a.max_tiles; q += thread_stride) {
@@ -278,8 +317,11 @@ __device__ void fill_tiles(const RouteArgs& a, const int* cnt, const int* off, i
 
 // A wave's stretch is at most kFusedRounds rounds of picks, so its ids are
 // loaded once, all at the start, and kept in registers for both passes.
-constexpr int kFusedRounds = 2;
 constexpr int64_t kRoundPicks = (int64_t)kBatch * kWave;
+constexpr int kFusedRounds =
+    kFusedMax > kRoundPicks * kRouteWaves
+        ? (int)((kFusedMax + kRoundPicks * kRouteWaves - 1) / (kRoundPicks * kRouteWaves))
+        : 1;
 static_assert(kFusedMax <= kFusedRounds * kRoundPicks * kRouteWaves,
               "single-launch routing keeps at most kFusedRounds rounds per wave");
 
@@ -467,7 +509,8 @@ template <typename IdT>
 hipError_t launch_typed(const RouteArgs& a, hipStream_t stream) {
     Shape s{a.num_picks, a.num_experts, id_bits(a.num_experts), a.topk, a.id_offset,
             a.inp_expanded};
-    if (a.num_picks <= kFusedMax) {
+    if (a.num_picks <= kFusedAlways ||
+        (a.num_picks <= kFusedMax && a.input_perm_len <= 2 * a.num_picks)) {
         route_fused_kernel<IdT><<<1, kRouteThreads, 0, stream>>>(a, s);
         return hipGetLastError();
     }
@@ -483,7 +526,7 @@ hipError_t launch_typed(const RouteArgs& a, hipStream_t stream) {
 }  // namespace
 
 size_t route_workspace_bytes(int64_t num_picks, int32_t num_experts) {
-    if (num_picks <= kFusedMax) return 0;
+    if (num_picks <= kFusedAlways) return 0;
     const int64_t tile = tile_picks(num_picks);
     const int64_t tiles = (num_picks + tile - 1) / tile;
     return (size_t)((tiles + 3) / 4 * 4 * (int64_t)num_experts * (int64_t)sizeof(int32_t));

@@ -40,7 +40,10 @@ def _check(ids, E, L0, EL, S, ids_dtype=torch.int64):
     (0, 8, 8, 0, 8, 4, "uniform"),
     (4, 4, 2, 1, 2, 2, "dups"),
     (100, 64, 8, 16, 16, 8, "uniform"),
-    (1024, 256, 8, 0, 256, 128, "uniform"),       # one-launch path, exactly 8192 picks
+    (128, 256, 8, 0, 256, 128, "uniform"),        # one launch: 1024 picks
+    (256, 64, 8, 0, 64, 1, "uniform"),            # one launch, unpadded: 2048 picks
+    (257, 64, 8, 0, 64, 1, "uniform"),            # two launches: 2056 picks
+    (1024, 256, 8, 0, 256, 128, "uniform"),       # two-launch path, 16 tiles
     (3001, 256, 8, 64, 32, 128, "uniform"),       # several tiles, ragged tail
     (5000, 256, 8, 0, 16, 64, "k_hot"),           # window holds the hot experts
     (5000, 256, 8, 128, 128, 256, "k_hot"),       # window holds only cold experts

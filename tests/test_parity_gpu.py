@@ -37,9 +37,12 @@ def _print_case(*args):
     (1, 256, 8, 1, "uniform", 0.0),
     (7, 5, 3, 4, "dups", 0.2),
     (32, 256, 8, 1, "uniform", 0.0),
-    (1000, 256, 8, 128, "uniform", 0.0),        # one-launch path, padded
-    (1024, 256, 8, 1, "uniform", 0.0),          # exactly 8192 picks
-    (1025, 256, 8, 1, "uniform", 0.0),          # first multi-tile size
+    (128, 256, 8, 128, "uniform", 0.0),         # one launch, padded: 1024 picks
+    (129, 256, 8, 128, "uniform", 0.0),         # two launches, padded: 1032 picks, 3 tiles
+    (256, 256, 8, 1, "uniform", 0.0),           # one launch, unpadded: 2048 picks
+    (257, 256, 8, 1, "uniform", 0.0),           # two launches: 2056 picks, 5 tiles
+    (1000, 256, 8, 128, "uniform", 0.0),        # 16 tiles, padded
+    (1025, 256, 8, 1, "uniform", 0.0),          # ragged last tile
     (8192, 256, 8, 1, "uniform", 0.0),          # 65536 picks: 128 tiles of 512
     (8193, 256, 8, 128, "uniform", 0.02),       # tiles grow past 512 picks
     (3000, 1000, 8, 4, "uniform", 0.05),        # E not a power of two, invalid ids
