@@ -121,16 +121,18 @@ __device__ __forceinline__ void load_keys(const IdT* ids, int64_t g0, int64_t w1
     raw_to_keys(v, g0, w1, E, id_offset, key);
 }
 
-// Count a round of keys per expert into this wave's LDS row.  Groups wholly
-// past w1 hold no keys and are skipped: a stretch is often a single group,
-// and matching an empty group costs as much as a full one.
+// Count a round of keys per expert into this wave's LDS row.  Counting
+// needs no ranks, so every lane adds 1 with an LDS atomic (the row is the
+// wave's own; the atomic only resolves lanes of one instruction that hold
+// the same key): one instruction per 64 picks where matching needs a
+// ballot per id bit.  Groups wholly past w1 hold no keys and are skipped.
 __device__ __forceinline__ void count_keys(const int (&key)[kBatch], int64_t g0, int64_t w1,
                                            const Shape& s, int* row) {
+    (void)s;
 #pragma unroll
     for (int b = 0; b < kBatch; ++b) {
         if (g0 + b * kWave >= w1) break;                // wave-uniform
-        const uint64_t m = match_key(key[b], s.nbits);
-        if (key[b] >= 0 && lanes_below(m) == 0) row[key[b]] += __popcll(m);
+        if (key[b] >= 0) atomicAdd(&row[key[b]], 1);
     }
 }
 
