@@ -556,6 +556,35 @@ def pin_quantize_rows(lib):
     assert np.all(q[3, 128:256] == 0) and sc[3, 1] == 1.0
 
 
+def pin_quantize_non_finite(lib):
+    """Non-finite inputs (the pages are silent; the reading taken): amax is
+    numpy's fmax reduction from 0 (IEEE maxNum, which skips NaN), an
+    infinite element makes the scale infinite, the codes are torch's
+    conversion of numpy's fp32 quotient with every NaN coded 0x7f, and a
+    group of NaN only gets scale 1."""
+    T, H = 2, 128 * 5
+    x = np.linspace(-3, 3, T * H, dtype=np.float32).reshape(T, H)
+    x[0, 5] = np.nan                       # group 0: NaN among normals
+    x[0, 130] = np.inf                     # group 1: +inf
+    x[0, 260] = -np.inf                    # group 2: -inf and a NaN
+    x[0, 300] = np.nan
+    x[1, 384:512] = np.nan                 # row 1 group 3: NaN only
+    xb = _bf16_bits(x)
+    G = H // 128
+    xf = _bits_to_f32_torch(xb, "bf16").reshape(T, G, 128)
+    q, sc = oracle.quantize_fp8_rows(xb, lib=lib)
+    amax = np.fmax.reduce(np.concatenate([np.zeros((T, G, 1), np.float32), np.abs(xf)], axis=2),
+                          axis=2)
+    want_sc = np.where(amax > 0, (amax / np.float32(448.0)).astype(np.float32), np.float32(1.0))
+    np.testing.assert_array_equal(sc, want_sc)
+    assert np.isinf(sc[0, 1]) and np.isinf(sc[0, 2]) and sc[1, 3] == 1.0
+    with np.errstate(invalid="ignore"):
+        quot = (xf / want_sc[:, :, None]).astype(np.float32)
+    want_q = _e4m3_torch(quot)
+    want_q[np.isnan(quot)] = 0x7f
+    np.testing.assert_array_equal(q, want_q.reshape(T, H))
+
+
 ALL_PINS = [
     pin_golden_prepare,
     pin_prepare_vs_numpy,
@@ -576,6 +605,7 @@ ALL_PINS = [
     pin_moe_sort_vs_numpy,
     pin_e4m3_conversion,
     pin_quantize_rows,
+    pin_quantize_non_finite,
 ]
 
 

@@ -63,6 +63,8 @@ MUTANTS = {
     "e4m3_subnormal_scale": ("float q = rintf(a * 0x1p9f);", "float q = rintf(a * 0x1p8f);"),
     "fp8_scale_uses_240": ("float scale = amax > 0.0f ? amax / 448.0f : 1.0f;",
                            "float scale = amax > 0.0f ? amax / 240.0f : 1.0f;"),
+    "fp8_amax_keeps_nan": ("                if (v > amax) amax = v;",
+                           "                if (!(v <= amax)) amax = v;"),
     "fp8_group_amax_first_only": ("                if (v > amax) amax = v;",
                                   "                if (e == 0) amax = v;"),
     "padding_ignores_total": ("int64_t limit = expert_offsets ? expert_offsets[E] : n_rows;",
