@@ -345,3 +345,68 @@ def test_workload_full_size_sampled(name):
                                         w.out_dtype)
     got = gu.bits(out[torch.from_numpy(toks).to(DEV)])
     np.testing.assert_array_equal(got, want)
+
+
+def test_graph_capture_replays_match_eager():
+    """The calls enqueue kernels only (no allocation, no memset), so a HIP
+    graph can capture prepare, dispatch and combine.  The graph is replayed
+    three times on new inputs copied into its static tensors, with eager work
+    and synchronisations between replays; every replay must equal the eager
+    calls on the same inputs, bit for bit."""
+    _print_case("graph capture")
+    dev = torch.device(DEV)
+    T, E, k, H, A = 1500, 64, 8, 1024, 16
+    r = mx.empty_routing(T, k, E, dev, row_align=A)
+    cap = r["input_permutation"].numel()
+    ids = torch.empty(T, k, dtype=torch.int64, device=dev)
+    x = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    y = torch.empty(cap, H, dtype=torch.bfloat16, device=dev)
+    w = torch.empty(T, k, dtype=torch.float32, device=dev)
+    xd = torch.zeros(cap, H, dtype=torch.bfloat16, device=dev)
+    out = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+
+    def step():
+        mx.prepare_moe_input(ids, r["expert_offsets"], r["problem_sizes1"], r["problem_sizes2"],
+                             r["input_permutation"], r["output_permutation"], E, 64, 32,
+                             row_align=A, workspace=r["workspace"])
+        mx.dispatch_rows(x, r["output_permutation"], k, xd)
+        mx.apply_shuffle_mul_sum(y, out, r["output_permutation"], w)
+
+    def load(seed):
+        rng = np.random.default_rng(seed)
+        ids.copy_(torch.from_numpy(routing.uniform_topk(rng, T, E, k)))
+        x.copy_(routing.normal_rows(T, H, "bf16", seed=seed, device=DEV))
+        y.copy_(routing.normal_rows(cap, H, "bf16", seed=seed + 1, device=DEV))
+        w.copy_(torch.from_numpy(routing.softmax_weights(rng, T, k)))
+
+    def snapshot():
+        used = r["input_permutation"] >= 0
+        return [r["expert_offsets"].clone(), r["input_permutation"].clone(),
+                r["output_permutation"].clone(), xd[used].clone(), out.clone()]
+
+    load(100)
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        step()                                         # warm-up off the default stream
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for seed in (101, 102, 103):
+        load(seed)
+        torch.cuda.synchronize()
+        step()                                         # eager on these inputs
+        torch.cuda.synchronize()
+        want = snapshot()
+        xd.zero_()
+        out.fill_(float("nan"))
+        r["input_permutation"].fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = snapshot()
+        for a, b in zip(got, want):
+            assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                               b.view(torch.int16) if b.dtype == torch.bfloat16 else b), seed
