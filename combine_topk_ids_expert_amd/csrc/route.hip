@@ -5,13 +5,14 @@
 //
 // The permutations are a stable counting sort of the flat picks i = t*k + j
 // by expert id.  The picks are cut into tiles; each tile is one workgroup of
-// 8 waves, and each wave owns a contiguous stretch of the tile.  Inside a
-// wave, 64 picks at a time, lanes holding the same expert find each other
-// with one ballot per id bit (match_key); the lowest such lane updates that
-// wave's private LDS counter for the expert, and every lane's rank among
-// equal ids is the popcount of matching lanes below it.  Since the wave
-// stretches, the 64-pick groups and the lanes are each walked in ascending
-// pick order, base(wave, expert) + rank is the stable position.
+// 8 waves, and each wave owns a contiguous stretch of the tile.  A wave
+// counts its picks per expert into its private LDS row with an LDS atomic
+// per pick.  To place them, 64 picks at a time, lanes holding the same
+// expert find each other with one ballot per id bit (match_key); every
+// lane's rank among equal ids is the popcount of matching lanes below it,
+// and the lowest such lane advances the wave's cursor for the expert.  Since
+// the wave stretches, the 64-pick groups and the lanes are each walked in
+// ascending pick order, base(wave, expert) + rank is the stable position.
 //
 //   small inputs (up to 1024 picks, or 2048 with little padding, where it
 //                measured faster): one workgroup counts, scans and scatters
@@ -19,11 +20,12 @@
 //   larger inputs, two launches:
 //     count   -- one workgroup per tile writes the tile's count of every
 //                expert to the workspace, expert-major ([E][tiles]);
-//     scatter -- every workgroup reads the whole count table (a thread sums
-//                one expert's row with 16-byte loads issued together), scans
-//                the padded totals over experts itself, takes its tile's base
-//                per expert, recounts its tile per wave and writes both
-//                permutations; workgroup 0 writes the offsets and sizes.
+//     scatter -- every workgroup reads the whole count table (a few lanes
+//                per expert row, 16-byte loads issued together, partial sums
+//                added with DPP), scans the padded totals over experts
+//                itself, takes its tile's base per expert, recounts its tile
+//                per wave and writes both permutations; workgroup 0 writes
+//                the offsets and sizes.
 #include "device_common.h"
 #include "launch.h"
 
@@ -34,7 +36,7 @@ constexpr int kRouteThreads = 512;
 constexpr int kRouteWaves = kRouteThreads / kWave;
 constexpr int kBatch = 8;                 // 64-pick groups loaded per round
 constexpr int kMaxE = 1024;
-constexpr int kTableBatch = 16;           // 16-byte count-table loads in flight per thread
+constexpr int kTableBatch = 16;           // 16-byte count-table loads in flight per lane
 
 #ifndef MXMOE_FUSED_MAX
 #define MXMOE_FUSED_MAX 2048
@@ -51,6 +53,8 @@ constexpr int kTableBatch = 16;           // 16-byte count-table loads in flight
 constexpr int64_t kFusedMax = MXMOE_FUSED_MAX;
 constexpr int64_t kFusedAlways = MXMOE_FUSED_ALWAYS < MXMOE_FUSED_MAX ? MXMOE_FUSED_ALWAYS : MXMOE_FUSED_MAX;
 constexpr int64_t kMaxTiles = MXMOE_MAX_TILES;  // tiles of the two-launch path (at most)
+static_assert(kMaxTiles >= 1 && kMaxTiles <= 128,
+              "the count-table read covers rows of at most 32 16-byte vectors");
 constexpr int64_t kTileQuantum = kRouteThreads; // tile sizes are multiples of this
 
 // Tile size of the two-launch path: the smallest multiple of kTileQuantum
