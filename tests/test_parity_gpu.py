@@ -410,3 +410,43 @@ def test_graph_capture_replays_match_eager():
         for a, b in zip(got, want):
             assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
                                b.view(torch.int16) if b.dtype == torch.bfloat16 else b), seed
+
+
+@pytest.mark.parametrize("name", ["uniform_T4096_H7168_E256_k8_pad128", "khot8_T8192_H7168_E256_k8"])
+def test_repeat_runs_identical(name):
+    """Determinism at full size: the whole step (prepare, dispatch, combine)
+    run twice on the same inputs, with every output poisoned in between,
+    gives identical bits; the K-hot workload puts most picks on 8 experts,
+    so many lanes of a wave count into the same LDS counters."""
+    w = WORKLOADS[name]
+    _print_case("repeat runs", name)
+    dev = torch.device(DEV)
+    inp = build_inputs(w, DEV)
+    T, k, E, H = w.T, w.k, w.E, w.H
+    r = mx.empty_routing(T, k, E, dev, row_align=w.row_align, blockscale=True)
+    cap = r["input_permutation"].numel()
+    ids = torch.from_numpy(inp["ids"]).to(dev)
+    wts = torch.from_numpy(inp["weights"]).to(dev)
+    y = expert_output(w, cap, dev)
+    xd = torch.empty(cap, H, dtype=inp["x"].dtype, device=dev)
+    out = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    runs = []
+    for _ in range(2):
+        for key in ("expert_offsets", "problem_sizes1", "problem_sizes2", "input_permutation",
+                    "output_permutation", "blockscale_offsets"):
+            r[key].fill_(-7)
+        xd.view(torch.uint8).fill_(0xA5)
+        out.fill_(float("nan"))
+        mx.prepare_moe_input(ids, r["expert_offsets"], r["problem_sizes1"], r["problem_sizes2"],
+                             r["input_permutation"], r["output_permutation"], E, 2048, H,
+                             r["blockscale_offsets"], row_align=w.row_align,
+                             workspace=r["workspace"])
+        mx.dispatch_rows(inp["x"], r["output_permutation"], k, xd)
+        mx.apply_shuffle_mul_sum(y, out, r["output_permutation"], wts)
+        torch.cuda.synchronize()
+        runs.append([r[key].clone() for key in ("expert_offsets", "problem_sizes1",
+                                                "problem_sizes2", "input_permutation",
+                                                "output_permutation", "blockscale_offsets")]
+                    + [xd.view(torch.uint8).clone(), out.view(torch.int16).clone()])
+    for a, b in zip(*runs):
+        assert torch.equal(a, b)
