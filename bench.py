@@ -23,9 +23,9 @@ from __future__ import annotations
 
 import argparse
 import hashlib
-import re
 import json
 import os
+import re
 import sys
 import time
 
