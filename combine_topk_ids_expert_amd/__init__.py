@@ -143,6 +143,16 @@ def _stream(device: torch.device):
     return torch.cuda.current_stream(device).cuda_stream
 
 
+def _on(device: torch.device, fn, *args):
+    """Call the C entry point ``fn(*args, stream)`` with the tensors' device
+    current: HIP launches on the current device, so a call on tensors of
+    another device switches to it for the launch (and back)."""
+    if device.index is not None and device.index != torch.cuda.current_device():
+        with torch.cuda.device(device):
+            return fn(*args, _stream(device))
+    return fn(*args, _stream(device))
+
+
 def _call(status: int, what: str):
     if status != 0:
         raise MxError(status, what)
@@ -216,13 +226,14 @@ def prepare_moe_input(topk_ids: torch.Tensor, expert_offsets: torch.Tensor,
         workspace = torch.empty(max(lib.mx_prepare_workspace_size(T, topk, E), 4),
                                 dtype=torch.uint8, device=dev)
     _check_dev("workspace", workspace, dev)
-    _call(lib.mx_prepare_moe_input(
+    _call(_on(
+        dev, lib.mx_prepare_moe_input,
         _ptr(topk_ids), MX_I64 if topk_ids.dtype == torch.int64 else MX_I32, T, topk, E,
         2 * n, k, k, n, row_align,
         _ptr(expert_offsets), _ptr(problem_sizes1), _ptr(problem_sizes2),
         _ptr(input_permutation), input_permutation.numel(), _ptr(output_permutation),
         _ptr(blockscale_offsets), blockscale_align,
-        _ptr(workspace), workspace.numel(), _stream(dev)), "prepare_moe_input")
+        _ptr(workspace), workspace.numel()), "prepare_moe_input")
 
 
 def shuffle_rows(input: torch.Tensor, dst2src_map: torch.Tensor,
@@ -242,8 +253,8 @@ def shuffle_rows(input: torch.Tensor, dst2src_map: torch.Tensor,
         raise ValueError("output must be [len(dst2src_map), *input.shape[1:]] of input's dtype")
     row_bytes = _row_bytes(input)
     if n_dst:
-        _call(lib.mx_shuffle_rows(_ptr(input), input.shape[0], row_bytes, _ptr(dst2src_map),
-                                  n_dst, _ptr(output), _stream(dev)), "shuffle_rows")
+        _call(_on(dev, lib.mx_shuffle_rows, _ptr(input), input.shape[0], row_bytes,
+                  _ptr(dst2src_map), n_dst, _ptr(output)), "shuffle_rows")
     return output
 
 
@@ -273,10 +284,9 @@ def dispatch_rows(input: torch.Tensor, output_permutation: torch.Tensor, topk: i
         side_rb = _row_bytes(side_input)
     T = input.shape[0]
     if T and output.shape[0]:
-        _call(lib.mx_dispatch_rows(_ptr(input), T, topk, _row_bytes(input),
-                                   _ptr(output_permutation), _ptr(output), output.shape[0],
-                                   _ptr(side_input), side_rb, _ptr(side_output), _stream(dev)),
-              "dispatch_rows")
+        _call(_on(dev, lib.mx_dispatch_rows, _ptr(input), T, topk, _row_bytes(input),
+                  _ptr(output_permutation), _ptr(output), output.shape[0],
+                  _ptr(side_input), side_rb, _ptr(side_output)), "dispatch_rows")
     return output
 
 
@@ -306,9 +316,10 @@ def apply_shuffle_mul_sum(input: torch.Tensor, output: torch.Tensor,
         if factors.dtype not in _FLOAT_CODES or factors.numel() != T * topk:
             raise ValueError("factors must be [tokens, topk] float32 / float16 / bfloat16")
         fcode = _FLOAT_CODES[factors.dtype]
-    _call(lib.mx_apply_shuffle_mul_sum(
+    _call(_on(
+        dev, lib.mx_apply_shuffle_mul_sum,
         _ptr(input), _FLOAT_CODES[input.dtype], input.shape[0], H, _ptr(permutation),
-        _ptr(factors), fcode, T, topk, _ptr(output), _FLOAT_CODES[output.dtype], _stream(dev)),
+        _ptr(factors), fcode, T, topk, _ptr(output), _FLOAT_CODES[output.dtype]),
         "apply_shuffle_mul_sum")
 
 
@@ -322,9 +333,8 @@ def moe_output_memset(output: torch.Tensor, output_permutation: torch.Tensor, to
     _check_dev("output_permutation", output_permutation, dev)
     _check_i32("output_permutation", output_permutation, T * topk)
     if T:
-        _call(lib.mx_moe_output_memset(_ptr(output), T, topk, _row_bytes(output),
-                                       _ptr(output_permutation), _stream(dev)),
-              "moe_output_memset")
+        _call(_on(dev, lib.mx_moe_output_memset, _ptr(output), T, topk, _row_bytes(output),
+                  _ptr(output_permutation)), "moe_output_memset")
 
 
 def zero_padding_rows(rows: torch.Tensor, input_permutation: torch.Tensor,
@@ -345,9 +355,8 @@ def zero_padding_rows(rows: torch.Tensor, input_permutation: torch.Tensor,
         _check_i32("expert_offsets", expert_offsets)
         E = expert_offsets.numel() - 1
     if n:
-        _call(lib.mx_zero_padding_rows(_ptr(rows), n, _row_bytes(rows), _ptr(input_permutation),
-                                       _ptr(expert_offsets), E, _stream(dev)),
-              "zero_padding_rows")
+        _call(_on(dev, lib.mx_zero_padding_rows, _ptr(rows), n, _row_bytes(rows),
+                  _ptr(input_permutation), _ptr(expert_offsets), E), "zero_padding_rows")
 
 
 def moe_sort(topk_ids: torch.Tensor, num_experts: int, local_expert_offset: int,
@@ -386,14 +395,15 @@ def moe_sort(topk_ids: torch.Tensor, num_experts: int, local_expert_offset: int,
                                 dtype=torch.uint8, device=dev)
     _check_dev("workspace", workspace, dev)
     nt = min(res["tile_idx_to_group_idx"].numel(), res["tile_idx_to_mn_limit"].numel())
-    _call(lib.mx_moe_sort(
+    _call(_on(
+        dev, lib.mx_moe_sort,
         _ptr(topk_ids), MX_I64 if topk_ids.dtype == torch.int64 else MX_I32, T, topk, num_experts,
         local_expert_offset, num_local_experts, tile_size,
         _ptr(res["expanded_idx_to_permuted_idx"]), _ptr(res["permuted_idx_to_expanded_idx"]),
         res["permuted_idx_to_expanded_idx"].numel(), _ptr(res["tile_idx_to_group_idx"]),
         _ptr(res["tile_idx_to_mn_limit"]), nt, _ptr(res["total_num_padded_tokens"]),
         _ptr(res["num_non_exiting_tiles"]), _ptr(res["expert_offsets"]),
-        _ptr(workspace), workspace.numel(), _stream(dev)), "moe_sort")
+        _ptr(workspace), workspace.numel()), "moe_sort")
     return res
 
 
@@ -417,7 +427,7 @@ def dispatch_rows_fp8(input: torch.Tensor, output_permutation: torch.Tensor, top
         raise ValueError("output must be [rows, hidden] of a 1-byte dtype")
     if output_scales.dtype != torch.float32 or tuple(output_scales.shape) != (output.shape[0], H // 128):
         raise ValueError("output_scales must be float32 [rows, hidden / 128]")
-    _call(lib.mx_dispatch_rows_fp8(_ptr(input), MX_BF16, T, topk, H, _ptr(output_permutation),
-                                   _ptr(output), _ptr(output_scales), output.shape[0],
-                                   _stream(dev)), "dispatch_rows_fp8")
+    _call(_on(dev, lib.mx_dispatch_rows_fp8, _ptr(input), MX_BF16, T, topk, H,
+              _ptr(output_permutation), _ptr(output), _ptr(output_scales), output.shape[0]),
+          "dispatch_rows_fp8")
 

@@ -13,8 +13,10 @@
  *   - Every array argument is a DEVICE pointer to memory the caller owns,
  *     laid out row-major and contiguous.  The library allocates and frees
  *     nothing, keeps no state between calls and never synchronises.
- *   - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream).
- *     Outputs are written in place when the stream reaches the work.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream)
+ *     and launched on the current HIP device, which must own the stream and
+ *     the arrays.  Outputs are written in place when the stream reaches the
+ *     work.
  *   - Argument errors (null pointers, sizes out of range, unsupported dtypes,
  *     misaligned index arrays, short buffers) are detected on the host before
  *     any HIP call and returned as a status; nothing is enqueued then.  After
