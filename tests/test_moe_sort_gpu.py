@@ -91,3 +91,28 @@ def test_moe_sort_one_rank_of_288_slots():
     print("case: moe_sort rank share", w.name, flush=True)
     ids = routing_ids(w, np.random.default_rng(w.seed))
     _check(ids, w.E, 72, 36, 128)
+
+
+def test_moe_sort_then_dispatch_is_the_permute():
+    """The sort's outputs drive the row kernels: dispatch_rows with
+    expanded_idx_to_permuted_idx writes row r = x[p2e[r] / k] for every row
+    with p2e[r] >= 0 (the permute of the TensorRT-LLM page's MoE, in
+    token-major form) and leaves padding and unused rows untouched; checked
+    against the oracle's sort and gather, bit for bit."""
+    print("case: moe_sort then dispatch", flush=True)
+    rng = np.random.default_rng(57)
+    T, E, k, L0, EL, S, H = 3000, 256, 8, 64, 32, 128, 2048
+    ids = routing.uniform_topk(rng, T, E, k)
+    got = mx.moe_sort(torch.from_numpy(ids).to(DEV), E, L0, EL, S)
+    want = oracle.moe_sort(ids.astype(np.int64), E, L0, EL, S)
+    p2e = want["permuted_idx_to_expanded_idx"]
+    x = routing.normal_rows(T, H, "bf16", seed=58, device=DEV)
+    rows = got["permuted_idx_to_expanded_idx"].numel()
+    xd = torch.empty(rows, H, dtype=torch.bfloat16, device=DEV)
+    xd.view(torch.uint8).fill_(gu.SENTINEL)
+    mx.dispatch_rows(x, got["expanded_idx_to_permuted_idx"], k, xd)
+    torch.cuda.synchronize()
+    src = np.where(p2e >= 0, p2e // k, -1).astype(np.int32)
+    used = src >= 0
+    np.testing.assert_array_equal(gu.bits(xd)[used], oracle.shuffle_rows(gu.bits(x), src)[used])
+    assert np.all(xd.view(torch.uint8).cpu().numpy()[~used] == gu.SENTINEL)
