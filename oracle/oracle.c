@@ -33,6 +33,20 @@
  *   - the combine sums j = 0..k-1 in ascending order as
  *     acc = fmaf(y, w, acc) from +0.0f, then rounds to nearest-even.
  *
+ * Beyond those three calls it defines, from the TensorRT-LLM page "Enable
+ * CuteDSL MoE with Large EP": the in-place output memset (rows of tokens
+ * with a permuted index >= 0 become zero), the tile-padded sort over a
+ * window of local experts (moe_sort), and the 1 x 128 FP8 e4m3fn input
+ * quantization; and the zero-fill of padding rows (padding rows are those
+ * with input_permutation < 0 below the padded total).
+ *
+ * Parity unpinned (the pages do not fix these; each is pinned to its own
+ * definition by hand-worked cases and library routines, not to the pages'
+ * implementations): the N / K columns of the problem sizes, the 128-row
+ * rounding of block-scale offsets, the meaning of moe_sort's tile limit and
+ * row maps (TensorRT-LLM's kernel source is not available), and the FP8
+ * handling of NaN and infinities.
+ *
  * Built with gcc -O2 -ffp-contract=off so the compiler neither fuses nor
  * reorders the float arithmetic written here.
  */
