@@ -450,3 +450,55 @@ def test_repeat_runs_identical(name):
                     + [xd.view(torch.uint8).clone(), out.view(torch.int16).clone()])
     for a, b in zip(*runs):
         assert torch.equal(a, b)
+
+
+def test_out_of_range_indices_are_skipped():
+    """Index data is never trusted: destinations of dispatch_rows and
+    dispatch_rows_fp8 outside [0, rows) and sources of shuffle_rows outside
+    [0, T) are skipped, rows nobody targets keep their contents, and every
+    in-range row matches the oracle's gather bit for bit."""
+    _print_case("out-of-range indices")
+    rng = np.random.default_rng(71)
+    T, k, H, rows = 300, 4, 1024, 1500
+    x = routing.normal_rows(T, H, "bf16", seed=72, device=DEV)
+    perm = rng.permutation(rows)[:T * k].astype(np.int64)       # distinct rows
+    bad = rng.random(T * k)
+    perm[bad < 0.05] = -1
+    perm[(bad >= 0.05) & (bad < 0.10)] = rows
+    perm[(bad >= 0.10) & (bad < 0.15)] = rows + 5
+    perm[(bad >= 0.15) & (bad < 0.17)] = 2**31 - 1
+    perm = perm.astype(np.int32)
+    src = np.full(rows, -1, np.int32)                            # the gather map it implies
+    ok = (perm >= 0) & (perm < rows)
+    src[perm[ok]] = (np.nonzero(ok)[0] // k).astype(np.int32)
+    used = src >= 0
+    t_perm = torch.from_numpy(perm).to(DEV)
+    # scatter form
+    xd = torch.empty(rows, H, dtype=torch.bfloat16, device=DEV)
+    xd.view(torch.uint8).fill_(gu.SENTINEL)
+    mx.dispatch_rows(x, t_perm, k, xd)
+    torch.cuda.synchronize()
+    want = oracle.shuffle_rows(gu.bits(x), src)
+    np.testing.assert_array_equal(gu.bits(xd)[used], want[used])
+    assert np.all(xd.view(torch.uint8).cpu().numpy()[~used] == gu.SENTINEL)
+    # gather form with sources out of range
+    src_bad = src.copy()
+    src_bad[rng.random(rows) < 0.1] = T
+    src_bad[rng.random(rows) < 0.05] = T + 9
+    used_g = (src_bad >= 0) & (src_bad < T)
+    xg = torch.empty(rows, H, dtype=torch.bfloat16, device=DEV)
+    xg.view(torch.uint8).fill_(gu.SENTINEL)
+    mx.shuffle_rows(x, torch.from_numpy(src_bad).to(DEV), xg)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(gu.bits(xg)[used_g],
+                                  oracle.shuffle_rows(gu.bits(x), src_bad)[used_g])
+    assert np.all(xg.view(torch.uint8).cpu().numpy()[~used_g] == gu.SENTINEL)
+    # FP8 dispatch: codes and scales of in-range rows, others untouched
+    q = torch.full((rows, H), 0x55, dtype=torch.uint8, device=DEV)
+    sc = torch.full((rows, H // 128), -3.0, dtype=torch.float32, device=DEV)
+    mx.dispatch_rows_fp8(x, t_perm, k, q, sc)
+    torch.cuda.synchronize()
+    xq, xs = oracle.quantize_fp8_rows(gu.bits(x))
+    np.testing.assert_array_equal(q.cpu().numpy()[used], oracle.shuffle_rows(xq, src)[used])
+    np.testing.assert_array_equal(sc.cpu().numpy()[used], oracle.shuffle_rows(xs, src)[used])
+    assert np.all(q.cpu().numpy()[~used] == 0x55) and np.all(sc.cpu().numpy()[~used] == -3.0)
