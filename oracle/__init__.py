@@ -79,15 +79,17 @@ def _declare(lib):
         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, c_i32p, c_i32p, ctypes.c_int64,
         c_i32p, c_i32p, ctypes.c_int64, c_i32p, c_i32p]
     lib.oracle_f32_to_e4m3.restype = ctypes.c_uint8
-    lib.oracle_f32_to_e4m3.argtypes = [ctypes.c_float]
+    lib.oracle_f32_to_e4m3.argtypes = [ctypes.c_uint32]
     lib.oracle_quantize_fp8_rows.restype = None
     lib.oracle_quantize_fp8_rows.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                              ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    # scalar conversions take and return fp32 bit patterns (no trip through a
+    # double, which would quiet signalling NaNs)
     for name in ("oracle_f32_to_bf16", "oracle_f32_to_f16"):
         getattr(lib, name).restype = ctypes.c_uint16
-        getattr(lib, name).argtypes = [ctypes.c_float]
+        getattr(lib, name).argtypes = [ctypes.c_uint32]
     for name in ("oracle_bf16_to_f32", "oracle_f16_to_f32"):
-        getattr(lib, name).restype = ctypes.c_float
+        getattr(lib, name).restype = ctypes.c_uint32
         getattr(lib, name).argtypes = [ctypes.c_uint16]
     return lib
 
@@ -241,8 +243,8 @@ def moe_sort(ids: np.ndarray, num_experts: int, local_expert_offset: int,
 
 def f32_to_e4m3(x: np.ndarray, lib=None) -> np.ndarray:
     lib = lib or load()
-    return np.array([lib.oracle_f32_to_e4m3(float(v)) for v in np.asarray(x, np.float32).ravel()],
-                    dtype=np.uint8)
+    bits = np.asarray(x, np.float32).ravel().view(np.uint32)
+    return np.array([lib.oracle_f32_to_e4m3(int(v)) for v in bits], dtype=np.uint8)
 
 
 def quantize_fp8_rows(x_bf16_bits: np.ndarray, block: int = 128, lib=None):
@@ -260,23 +262,23 @@ def quantize_fp8_rows(x_bf16_bits: np.ndarray, block: int = 128, lib=None):
 
 def f32_to_bf16(x: np.ndarray, lib=None) -> np.ndarray:
     lib = lib or load()
-    return np.array([lib.oracle_f32_to_bf16(float(v)) for v in np.asarray(x, np.float32).ravel()],
-                    dtype=np.uint16)
+    bits = np.asarray(x, np.float32).ravel().view(np.uint32)
+    return np.array([lib.oracle_f32_to_bf16(int(v)) for v in bits], dtype=np.uint16)
 
 
 def f32_to_f16(x: np.ndarray, lib=None) -> np.ndarray:
     lib = lib or load()
-    return np.array([lib.oracle_f32_to_f16(float(v)) for v in np.asarray(x, np.float32).ravel()],
-                    dtype=np.uint16)
+    bits = np.asarray(x, np.float32).ravel().view(np.uint32)
+    return np.array([lib.oracle_f32_to_f16(int(v)) for v in bits], dtype=np.uint16)
 
 
 def bf16_to_f32(h: np.ndarray, lib=None) -> np.ndarray:
     lib = lib or load()
     return np.array([lib.oracle_bf16_to_f32(int(v)) for v in np.asarray(h, np.uint16).ravel()],
-                    dtype=np.float32)
+                    dtype=np.uint32).view(np.float32)
 
 
 def f16_to_f32(h: np.ndarray, lib=None) -> np.ndarray:
     lib = lib or load()
     return np.array([lib.oracle_f16_to_f32(int(v)) for v in np.asarray(h, np.uint16).ravel()],
-                    dtype=np.float32)
+                    dtype=np.uint32).view(np.float32)

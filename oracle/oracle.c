@@ -136,11 +136,16 @@ static void store_elem(void* base, int dtype, int64_t idx, float v) {
     }
 }
 
-/* Exported for the tests that pin the conversions against library routines. */
-uint16_t oracle_f32_to_bf16(float f) { return f32_to_bf16(f); }
-uint16_t oracle_f32_to_f16(float f) { return f32_to_f16(f); }
-float oracle_bf16_to_f32(uint16_t h) { return bf16_to_f32(h); }
-float oracle_f16_to_f32(uint16_t h) { return f16_to_f32(h); }
+/* Exported for the tests that pin the conversions against library routines.
+ * Values cross the interface as bit patterns: a float passed through a
+ * double (as Python floats are) would have its signalling NaNs quieted
+ * before the conversion sees them. */
+static float f32_from_bits(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
+static uint32_t f32_bits(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
+uint16_t oracle_f32_to_bf16(uint32_t bits) { return f32_to_bf16(f32_from_bits(bits)); }
+uint16_t oracle_f32_to_f16(uint32_t bits) { return f32_to_f16(f32_from_bits(bits)); }
+uint32_t oracle_bf16_to_f32(uint16_t h) { return f32_bits(bf16_to_f32(h)); }
+uint32_t oracle_f16_to_f32(uint16_t h) { return f32_bits(f16_to_f32(h)); }
 
 /* ---------------------------------------------------------------------- */
 /* prepare_moe_input                                                        */
@@ -387,7 +392,7 @@ static uint8_t f32_to_e4m3(float f) {
     return sign | (code > 0x7e ? 0x7e : code);
 }
 
-uint8_t oracle_f32_to_e4m3(float f) { return f32_to_e4m3(f); }
+uint8_t oracle_f32_to_e4m3(uint32_t bits) { return f32_to_e4m3(f32_from_bits(bits)); }
 
 /* x [T][H] bf16 -> q [T][H] e4m3fn bytes and scales [T][H / block] fp32;
  * H must be a multiple of block. */

@@ -378,15 +378,26 @@ def pin_conversions(lib):
     with np.errstate(over="ignore"):
         want16 = vals.astype(np.float16).view(np.uint16)
     np.testing.assert_array_equal(oracle.f32_to_f16(vals, lib=lib), want16)
-    nan_b = oracle.f32_to_bf16(np.array([np.nan], np.float32), lib=lib)
-    assert np.isnan(_bits_to_f32_torch(nan_b, "bf16")).all()
+    # NaN stays NaN (a reading: payloads are not unique).  Patterns whose
+    # payload lies only in the low 16 bits would become infinities if the
+    # narrowing merely truncated, so they are included with the random NaNs.
+    nans = np.concatenate([
+        np.array([0x7fc00000, 0xffc00000, 0x7f800001, 0xff800001, 0x7f80ffff, 0x7f810000,
+                  0x7fbfffff, 0xffffffff], np.uint32).view(np.float32),
+        rng.integers(0, 2**32, 20000, dtype=np.uint64).astype(np.uint32).view(np.float32)])
+    nans = nans[np.isnan(nans)]
+    assert nans.size > 8
+    assert np.isnan(_bits_to_f32_torch(oracle.f32_to_bf16(nans, lib=lib), "bf16")).all()
+    assert np.isnan(oracle.f32_to_f16(nans, lib=lib).view(np.float16)).all()
     all16 = np.arange(2**16, dtype=np.uint32).astype(np.uint16)
     fin = ~np.isnan(all16.view(np.float16))
     np.testing.assert_array_equal(oracle.f16_to_f32(all16, lib=lib)[fin],
                                   all16.view(np.float16).astype(np.float32)[fin])
+    assert np.isnan(oracle.f16_to_f32(all16, lib=lib)[~fin]).all()
     bf_ref = _bits_to_f32_torch(all16, "bf16")
     finb = ~np.isnan(bf_ref)
     np.testing.assert_array_equal(oracle.bf16_to_f32(all16, lib=lib)[finb], bf_ref[finb])
+    assert np.isnan(oracle.bf16_to_f32(all16, lib=lib)[~finb]).all()
 
 
 # ---------------------------------------------------------------------------

@@ -40,6 +40,8 @@ MUTANTS = {
     "bf16_ties_away_from_zero": ("if (rest > 0x8000u || (rest == 0x8000u && (t & 1u)))",
                                  "if (rest >= 0x8000u)"),
     "bf16_truncates": ("t += 1;", "t += 0;"),
+    "bf16_nan_not_quieted": ("if (isnan(f)) return (uint16_t)((u >> 16) | 0x0040);",
+                             "if (isnan(f)) return (uint16_t)(u >> 16);"),
     "f16_subnormal_scale": ("float q = rintf(a * 0x1p24f);", "float q = rintf(a * 0x1p23f);"),
     "f16_bias_off_by_one": ("(((ex + 15) << 10)", "(((ex + 14) << 10)"),
     "f16_widen_bias": ("v = ldexpf((float)(1024 + fr), ex - 25);",
