@@ -177,9 +177,12 @@ def pin_blockscale_and_problem_sizes(lib):
     (numpy cumsum).  Problem sizes: (count, N, K) per expert with the given
     N, K; the counts are numpy's bincount."""
     rng = np.random.default_rng(14)
-    for T, E, k, B in [(300, 128, 8, 128), (50, 7, 3, 16), (5, 4, 2, 1)]:
+    # with row_align > 1 the block-scale sum must still round the raw counts,
+    # not the row-padded ones (they differ when the padding crosses a B step)
+    for T, E, k, B, A in [(300, 128, 8, 128, 1), (50, 7, 3, 16, 1), (5, 4, 2, 1, 1),
+                          (300, 16, 8, 4, 3), (1000, 64, 8, 128, 64), (40, 5, 3, 2, 7)]:
         ids = _rand_ids(rng, T, E, k, "zipf" if E >= 8 else "dups", invalid_frac=0.05)
-        m = oracle.prepare_moe_input(ids, E, row_align=1, blockscale_align=B,
+        m = oracle.prepare_moe_input(ids, E, row_align=A, blockscale_align=B,
                                      gemm=(2 * 512, 256, 256, 512), lib=lib)
         flat = ids.ravel()
         counts = np.bincount(flat[(flat >= 0) & (flat < E)], minlength=E)

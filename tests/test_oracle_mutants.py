@@ -69,6 +69,23 @@ MUTANTS = {
                            "                if (!(v <= amax)) amax = v;"),
     "fp8_group_amax_first_only": ("                if (v > amax) amax = v;",
                                   "                if (e == 0) amax = v;"),
+    "blockscale_from_padded_counts": ("bs += round_up(count[e], bs_align);",
+                                      "bs += round_up(round_up(count[e], row_align), bs_align);"),
+    "problem_size_is_padded": ("ps1[3 * e] = (int32_t)count[e];",
+                               "ps1[3 * e] = (int32_t)round_up(count[e], row_align);"),
+    "combine_starts_from_negative_zero": ("float acc = 0.0f;", "float acc = -0.0f;"),
+    "combine_reverse_pick_order": (
+        "            for (int32_t j = 0; j < k; ++j) {\n                int64_t r = perm[t * k + j];",
+        "            for (int32_t j = k - 1; j >= 0; --j) {\n                int64_t r = perm[t * k + j];"),
+    "f16_ties_away_from_zero": ("float q = rintf(ldexpf(a, 10 - ex));",
+                                "float q = roundf(ldexpf(a, 10 - ex));"),
+    "e4m3_ties_away_from_zero": ("float q = rintf(ldexpf(a, 3 - ex));",
+                                 "float q = roundf(ldexpf(a, 3 - ex));"),
+    "fp8_multiplies_by_reciprocal": (
+        "q[t * H + g * block + e] = f32_to_e4m3(bf16_to_f32(xs[e]) / scale);",
+        "q[t * H + g * block + e] = f32_to_e4m3(bf16_to_f32(xs[e]) * (1.0f / scale));"),
+    "padding_zeroes_rows_of_token0": ("if (input_perm[r] < 0) memset(",
+                                      "if (input_perm[r] <= 0) memset("),
     "padding_ignores_total": ("int64_t limit = expert_offsets ? expert_offsets[E] : n_rows;",
                               "int64_t limit = n_rows;"),
 }
