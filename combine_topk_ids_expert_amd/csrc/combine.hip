@@ -9,11 +9,11 @@
 // skipped.  The ascending-j chain of fused multiply-adds is the only order
 // used, so the result does not depend on launch shapes.
 //
-// One workgroup per token (and column chunk).  A thread owns 8 consecutive
-// columns and issues the 16-byte loads of up to 8 picks before the first
-// multiply-add, so each wave keeps 8 KiB (16-bit y) of reads in flight; the
-// row indices and weights are loaded one per lane and broadcast with
-// readlane.
+// One workgroup per token and column chunk of at most 128 threads (the chunks
+// of a token are neighbours in the grid).  A thread owns 8 columns and
+// issues the loads of up to 8 picks before the first multiply-add, so each
+// wave keeps 8 KiB (16-bit y) of reads in flight; the row indices and weights
+// are loaded one per lane and broadcast with readlane.
 #include "device_common.h"
 #include "launch.h"
 
@@ -22,47 +22,62 @@ namespace {
 
 constexpr int kGroup = 8;      // columns per thread in the vector path
 constexpr int kPickBatch = 8;  // picks whose loads are issued together
-constexpr int kMaxThreads = 1024;
+constexpr int kCombineThreads = 128;  // workgroup width; longer rows are cut into chunks
 
 
-// 8 consecutive elements of a row, moved with 16-byte accesses.  Expert
-// output rows are read exactly once, so the loads carry the non-temporal
-// hint; so do the stores of the write-once output rows.
-template <typename TY> struct Pack;
-template <> struct Pack<BF16> { u32x4 q; __device__ float at(int e) const { const uint32_t w = q[e >> 1]; return to_f32(BF16{}, (uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu))); } };
-template <> struct Pack<F16> { u32x4 q; __device__ float at(int e) const { const uint32_t w = q[e >> 1]; return to_f32(F16{}, (uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu))); } };
-template <> struct Pack<F32> { u32x4 q[2]; __device__ float at(int e) const { return __uint_as_float(q[e >> 2][e & 3]); } };
+// N consecutive elements of a row, moved with one 8- or 16-byte access.
+// Expert output rows are read exactly once, so the loads carry the
+// non-temporal hint; so do the stores of the write-once output rows.
+template <typename TY, int N>
+struct Cols {
+    static constexpr int kBytes = N * (int)sizeof(typename TY::storage);
+    static_assert(kBytes == 8 || kBytes == 16, "one 8- or 16-byte access per set");
+    uint32_t w[kBytes / 4];
+    __device__ float at(int e) const {
+        if constexpr (sizeof(typename TY::storage) == 4) {
+            return __uint_as_float(w[e]);
+        } else {
+            const uint32_t x = w[e >> 1];
+            return to_f32(TY{}, (uint16_t)((e & 1) ? (x >> 16) : (x & 0xffffu)));
+        }
+    }
+};
 
-template <typename TY>
-__device__ __forceinline__ Pack<TY> load_pack(const typename TY::storage* p) {
-    Pack<TY> v;
-    const u32x4* q = reinterpret_cast<const u32x4*>(p);
-    if constexpr (sizeof(typename TY::storage) == 2) {
-        v.q = __builtin_nontemporal_load(q);
+template <typename TY, int N>
+__device__ __forceinline__ Cols<TY, N> load_cols(const typename TY::storage* p) {
+    Cols<TY, N> v;
+    if constexpr (Cols<TY, N>::kBytes == 16) {
+        const u32x4 q = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v.w[i] = q[i];
     } else {
-        v.q[0] = __builtin_nontemporal_load(q);
-        v.q[1] = __builtin_nontemporal_load(q + 1);
+        const u32x2 q = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+        v.w[0] = q[0];
+        v.w[1] = q[1];
     }
     return v;
 }
 
-template <typename TO>
-__device__ __forceinline__ void store_pack(typename TO::storage* p, const float* acc) {
-    u32x4* o = reinterpret_cast<u32x4*>(p);
+template <typename TO, int N>
+__device__ __forceinline__ void store_cols(typename TO::storage* p, const float* acc) {
+    constexpr int kBytes = N * (int)sizeof(typename TO::storage);
+    static_assert(kBytes == 8 || kBytes == 16, "one 8- or 16-byte access per set");
+    uint32_t w[kBytes / 4];
     if constexpr (sizeof(typename TO::storage) == 2) {
-        u32x4 q;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            q[i] = (uint32_t)from_f32(TO{}, acc[2 * i]) |
+        for (int i = 0; i < kBytes / 4; ++i)
+            w[i] = (uint32_t)from_f32(TO{}, acc[2 * i]) |
                    ((uint32_t)from_f32(TO{}, acc[2 * i + 1]) << 16);
-        __builtin_nontemporal_store(q, o);
     } else {
-        const u32x4 q0 = {__float_as_uint(acc[0]), __float_as_uint(acc[1]),
-                          __float_as_uint(acc[2]), __float_as_uint(acc[3])};
-        const u32x4 q1 = {__float_as_uint(acc[4]), __float_as_uint(acc[5]),
-                          __float_as_uint(acc[6]), __float_as_uint(acc[7])};
-        __builtin_nontemporal_store(q0, o);
-        __builtin_nontemporal_store(q1, o + 1);
+#pragma unroll
+        for (int i = 0; i < kBytes / 4; ++i) w[i] = __float_as_uint(acc[i]);
+    }
+    if constexpr (kBytes == 16) {
+        const u32x4 q = {w[0], w[1], w[2], w[3]};
+        __builtin_nontemporal_store(q, reinterpret_cast<u32x4*>(p));
+    } else {
+        const u32x2 q = {w[0], w[1]};
+        __builtin_nontemporal_store(q, reinterpret_cast<u32x2*>(p));
     }
 }
 
@@ -85,24 +100,41 @@ __device__ __forceinline__ float readlane_f(float v, int lane) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
-// Vector path: hidden % 8 == 0 and y / out 16-byte aligned.  Each wave loads
-// the token's row indices and weights one per lane (one vector load each) and
-// broadcasts them with readlane; every loop around a readlane is uniform, so
-// threads past the row end stay in the loops and only skip their memory
-// accesses.
+// Vector path: hidden % 8 == 0 and y / out 16-byte aligned.  A thread owns 8
+// columns.  With 16-bit y and out they are 8 consecutive columns (16-byte
+// loads and stores).  When y or out is fp32 they are two sets of 4, at
+// lane*4 and 256 + lane*4 within the wave's 512 columns, so that every
+// 16-byte access of a wave covers 1 KiB of one row: 8 consecutive fp32
+// columns per lane would leave every other 16 bytes of each load or store
+// instruction to the next one.  Each wave loads the token's row indices and
+// weights one per lane (one vector load each) and broadcasts them with
+// readlane; every loop around a readlane is uniform, so threads past the row
+// end stay in the loops and only skip their memory accesses.
 template <typename TY, typename TO, int FDT>
-__global__ __launch_bounds__(kMaxThreads) void combine_vec_kernel(
+__global__ __launch_bounds__(kCombineThreads) void combine_vec_kernel(
     const typename TY::storage* __restrict__ y, int64_t num_y_rows, int64_t hidden,
     const int32_t* __restrict__ perm, const void* __restrict__ factors, int32_t topk,
-    typename TO::storage* __restrict__ out) {
-    const int64_t t = blockIdx.x;
+    typename TO::storage* __restrict__ out, int32_t chunks) {
+    constexpr int kSets =
+        (sizeof(typename TY::storage) == 4 || sizeof(typename TO::storage) == 4) ? 2 : 1;
+    constexpr int kCols = kGroup / kSets;
+    int64_t chunk;
+    const int64_t t = chunk_row(chunks, chunk);
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t col = ((int64_t)blockIdx.y * blockDim.x + threadIdx.x) * kGroup;
-    const bool active = col < hidden;
-    const int32_t* rows = perm + t * topk;
-    float acc[kGroup];
+    const int64_t wave_col = (chunk * blockDim.x + (threadIdx.x - lane)) * kGroup;
+    int64_t col[kSets];
+    bool active[kSets];
 #pragma unroll
-    for (int e = 0; e < kGroup; ++e) acc[e] = 0.0f;
+    for (int s = 0; s < kSets; ++s) {
+        col[s] = wave_col + (int64_t)(s * kWave + lane) * kCols;
+        active[s] = col[s] < hidden;
+    }
+    const int32_t* rows = perm + t * topk;
+    float acc[kSets][kCols];
+#pragma unroll
+    for (int s = 0; s < kSets; ++s)
+#pragma unroll
+        for (int e = 0; e < kCols; ++e) acc[s][e] = 0.0f;
     for (int j0 = 0; j0 < topk; j0 += kWave) {
         const int nj = topk - j0 < kWave ? topk - j0 : kWave;
         int my_r = -1;
@@ -115,7 +147,7 @@ __global__ __launch_bounds__(kMaxThreads) void combine_vec_kernel(
         for (int jb = 0; jb < nj; jb += kPickBatch) {
             int32_t r[kPickBatch];
             float w[kPickBatch];
-            Pack<TY> v[kPickBatch];
+            Cols<TY, kCols> v[kPickBatch][kSets];
 #pragma unroll
             for (int jj = 0; jj < kPickBatch; ++jj) {
                 r[jj] = jb + jj < nj ? __builtin_amdgcn_readlane(my_r, jb + jj) : -1;
@@ -123,27 +155,35 @@ __global__ __launch_bounds__(kMaxThreads) void combine_vec_kernel(
             }
 #pragma unroll
             for (int jj = 0; jj < kPickBatch; ++jj)
-                if (r[jj] >= 0 && active) v[jj] = load_pack<TY>(y + (int64_t)r[jj] * hidden + col);
+#pragma unroll
+                for (int s = 0; s < kSets; ++s)
+                    if (r[jj] >= 0 && active[s])
+                        v[jj][s] = load_cols<TY, kCols>(y + (int64_t)r[jj] * hidden + col[s]);
 #pragma unroll
             for (int jj = 0; jj < kPickBatch; ++jj) {
                 if (r[jj] < 0) continue;
 #pragma unroll
-                for (int e = 0; e < kGroup; ++e)
-                    acc[e] = __builtin_fmaf(v[jj].at(e), w[jj], acc[e]);
+                for (int s = 0; s < kSets; ++s)
+#pragma unroll
+                    for (int e = 0; e < kCols; ++e)
+                        acc[s][e] = __builtin_fmaf(v[jj][s].at(e), w[jj], acc[s][e]);
             }
         }
     }
-    if (active) store_pack<TO>(out + t * hidden + col, acc);
+#pragma unroll
+    for (int s = 0; s < kSets; ++s)
+        if (active[s]) store_cols<TO, kCols>(out + t * hidden + col[s], acc[s]);
 }
 
 // Scalar path for any hidden size and element-aligned pointers.
 template <typename TY, typename TO, int FDT>
-__global__ __launch_bounds__(kMaxThreads) void combine_scalar_kernel(
+__global__ __launch_bounds__(kCombineThreads) void combine_scalar_kernel(
     const typename TY::storage* __restrict__ y, int64_t num_y_rows, int64_t hidden,
     const int32_t* __restrict__ perm, const void* __restrict__ factors, int32_t topk,
-    typename TO::storage* __restrict__ out) {
-    const int64_t t = blockIdx.x;
-    const int64_t h = (int64_t)blockIdx.y * blockDim.x + threadIdx.x;
+    typename TO::storage* __restrict__ out, int32_t chunks) {
+    int64_t chunk;
+    const int64_t t = chunk_row(chunks, chunk);
+    const int64_t h = chunk * blockDim.x + threadIdx.x;
     if (h >= hidden) return;
     const int32_t* rows = perm + t * topk;
     float acc = 0.0f;
@@ -163,20 +203,20 @@ hipError_t launch_typed(const void* y, int64_t num_y_rows, int64_t hidden, const
     using SY = typename TY::storage;
     using SO = typename TO::storage;
     const bool vec = hidden % kGroup == 0 && ((uintptr_t)y % 16) == 0 && ((uintptr_t)out % 16) == 0;
-    const int64_t items = vec ? hidden / kGroup : hidden;
-    int64_t threads = (items + kWave - 1) / kWave * kWave;
-    if (threads > kMaxThreads) threads = kMaxThreads;
-    const int64_t chunks = (items + threads - 1) / threads;
-    const dim3 grid((unsigned)T, (unsigned)chunks, 1);
-    if (vec)
-        combine_vec_kernel<TY, TO, FDT><<<grid, (unsigned)threads, 0, stream>>>(
-            static_cast<const SY*>(y), num_y_rows, hidden, perm, factors, topk,
-            static_cast<SO*>(out));
-    else
-        combine_scalar_kernel<TY, TO, FDT><<<grid, (unsigned)threads, 0, stream>>>(
-            static_cast<const SY*>(y), num_y_rows, hidden, perm, factors, topk,
-            static_cast<SO*>(out));
-    return hipGetLastError();
+    const RowShape sh = row_shape(vec ? hidden / kGroup : hidden, kCombineThreads);
+    const int64_t factor_bytes = FDT == 0 ? 4 : 2;
+    return for_row_batches(T, sh, [&](int64_t t0, int64_t, dim3 grid, dim3 block) {
+        const int32_t* p = perm + t0 * topk;
+        const void* f = factors ? static_cast<const char*>(factors) + t0 * topk * factor_bytes
+                                : nullptr;
+        SO* o = static_cast<SO*>(out) + t0 * hidden;
+        if (vec)
+            combine_vec_kernel<TY, TO, FDT><<<grid, block, 0, stream>>>(
+                static_cast<const SY*>(y), num_y_rows, hidden, p, f, topk, o, sh.chunks);
+        else
+            combine_scalar_kernel<TY, TO, FDT><<<grid, block, 0, stream>>>(
+                static_cast<const SY*>(y), num_y_rows, hidden, p, f, topk, o, sh.chunks);
+    });
 }
 
 template <typename TY, typename TO>

@@ -11,6 +11,50 @@ constexpr int kWave = 64;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// Launch shape of the row kernels (dispatch, combine, row shuffle, zeroing,
+// quantize-on-dispatch): one workgroup per (row, column chunk), flattened
+// into blockIdx.x with the chunk varying fastest, so the chunks of one row run
+// next to each other.  Workgroups are at most `max_threads` wide (whole
+// waves); the chunks of a row are as few as that allows, and as even.  Rows
+// are launched in batches so that no launch holds more than 2^31 work-items.
+struct RowShape {
+    int32_t threads;          // workgroup width
+    int32_t chunks;           // column chunks per row
+    int64_t rows_per_launch;  // rows of one launch
+};
+
+inline RowShape row_shape(int64_t items, int64_t max_threads) {
+    RowShape s;
+    const int64_t chunks = (items + max_threads - 1) / max_threads;
+    int64_t threads = (items + chunks - 1) / chunks;
+    threads = (threads + kWave - 1) / kWave * kWave;
+    s.threads = (int32_t)threads;
+    s.chunks = (int32_t)chunks;
+    s.rows_per_launch = ((int64_t)1 << 31) / (chunks * threads);
+    return s;
+}
+
+// Launches launch(row0, rows, grid, block) for consecutive batches of rows,
+// stopping at the first launch error.
+template <typename F>
+hipError_t for_row_batches(int64_t rows, const RowShape& s, F&& launch) {
+    for (int64_t r0 = 0; r0 < rows; r0 += s.rows_per_launch) {
+        const int64_t n = rows - r0 < s.rows_per_launch ? rows - r0 : s.rows_per_launch;
+        launch(r0, n, dim3((unsigned)(n * s.chunks), 1, 1), dim3((unsigned)s.threads, 1, 1));
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+// Row (within the launch) and column chunk of this workgroup.
+__device__ __forceinline__ int64_t chunk_row(int32_t chunks, int64_t& chunk) {
+    const uint32_t b = blockIdx.x;
+    const uint32_t r = b / (uint32_t)chunks;
+    chunk = (int64_t)(b - r * (uint32_t)chunks);
+    return (int64_t)r;
+}
+
 // 16-byte store of vector v at byte offset `off` of a row that starts at
 // `row` (the row base wave-uniform, the offset per lane), through a raw
 // buffer store whose cache policy is non-temporal and system-coherent

@@ -10,13 +10,14 @@
 // The division is the IEEE one (hipcc's default correctly rounded fp32
 // division), so the codes do not depend on launch shapes.
 //
-// A workgroup holds one token (or a chunk of a long row); each thread owns 16
-// consecutive elements (two 16-byte loads, one 16-byte store of codes per
-// destination, non-temporal and system-coherent through store16_stream: 11%
-// faster than a plain non-temporal store here on MI355X) and 8 threads form a
-// group, whose amax is reduced with lane shuffles inside the wave.  A wave covers 8 groups; their scales are
-// gathered into lanes 0..7 so each destination gets one contiguous 32-byte
-// scale store per wave.
+// A workgroup holds one token row, or a chunk of at most 1024 threads of a
+// longer one (the chunks of a row are neighbours in the grid).  Each thread
+// owns 16 consecutive elements: two 16-byte loads, and one 16-byte store of
+// codes per destination, non-temporal and system-coherent through
+// store16_stream (11% faster than a plain non-temporal store on MI355X).
+// 8 threads form a group, whose amax is reduced with lane shuffles inside the
+// wave.  A wave covers 8 groups; their scales are gathered into lanes 0..7 so
+// each destination gets one contiguous 32-byte scale store per wave.
 #include "device_common.h"
 #include "launch.h"
 
@@ -27,7 +28,10 @@ constexpr int kGroupElems = 128;
 constexpr int kElemsPerThread = 16;
 constexpr int kThreadsPerGroup = kGroupElems / kElemsPerThread;   // 8
 constexpr int kGroupsPerWave = kWave / kThreadsPerGroup;          // 8
-constexpr int kMaxQuantThreads = 1024;
+// Workgroup width limit: a row of up to 16384 elements is one workgroup (448
+// threads at 7168).  Chunks of 64 to 256 threads, which suit the plain row
+// copies, made this kernel 1-10% slower on MI355X.
+constexpr int kQuantThreads = 1024;
 
 
 // binary32 -> OCP e4m3fn by integer rounding of the significand: keep 3
@@ -52,14 +56,15 @@ __device__ __forceinline__ uint32_t e4m3_code(float f) {
     return sign | (code > 0x7eu ? 0x7eu : code);
 }
 
-// Token blockIdx.x, elements [(blockIdx.y * blockDim.x + tid) * 16, +16).
-__global__ __launch_bounds__(kMaxQuantThreads) void dispatch_quant_fp8_kernel(
+// Token t, elements [(chunk * blockDim.x + tid) * 16, +16).
+__global__ __launch_bounds__(kQuantThreads) void dispatch_quant_fp8_kernel(
     const uint16_t* __restrict__ src, int64_t hidden, int32_t topk,
     const int32_t* __restrict__ output_perm, uint8_t* __restrict__ dst_q,
-    float* __restrict__ dst_scales, int64_t num_dst_rows) {
-    const int64_t t = blockIdx.x;
+    float* __restrict__ dst_scales, int64_t num_dst_rows, int32_t chunks) {
+    int64_t chunk;
+    const int64_t t = chunk_row(chunks, chunk);
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t col = ((int64_t)blockIdx.y * blockDim.x + threadIdx.x) * kElemsPerThread;
+    const int64_t col = (chunk * blockDim.x + threadIdx.x) * kElemsPerThread;
     const bool live = col < hidden;                    // whole groups: a group is live or not
     u32x4 v0 = {0u, 0u, 0u, 0u}, v1 = {0u, 0u, 0u, 0u};
     if (live) {
@@ -115,15 +120,13 @@ hipError_t launch_dispatch_quant_fp8(const void* src, int64_t num_tokens, int32_
                                      float* dst_scales, int64_t num_dst_rows,
                                      hipStream_t stream) {
     if (num_tokens == 0 || num_dst_rows == 0) return hipSuccess;
-    const int64_t threads_needed = hidden / kElemsPerThread;
-    const int64_t chunks = (threads_needed + kMaxQuantThreads - 1) / kMaxQuantThreads;
-    int64_t threads = (threads_needed + chunks - 1) / chunks;
-    threads = (threads + kWave - 1) / kWave * kWave;
-    const dim3 grid((unsigned)num_tokens, (unsigned)chunks, 1);
-    dispatch_quant_fp8_kernel<<<grid, (unsigned)threads, 0, stream>>>(
-        static_cast<const uint16_t*>(src), hidden, topk, output_perm,
-        static_cast<uint8_t*>(dst_q), dst_scales, num_dst_rows);
-    return hipGetLastError();
+    const RowShape sh = row_shape(hidden / kElemsPerThread, kQuantThreads);
+    const uint16_t* s = static_cast<const uint16_t*>(src);
+    return for_row_batches(num_tokens, sh, [&](int64_t t0, int64_t, dim3 grid, dim3 block) {
+        dispatch_quant_fp8_kernel<<<grid, block, 0, stream>>>(
+            s + t0 * hidden, hidden, topk, output_perm + t0 * topk,
+            static_cast<uint8_t*>(dst_q), dst_scales, num_dst_rows, sh.chunks);
+    });
 }
 
 }  // namespace mxmoe

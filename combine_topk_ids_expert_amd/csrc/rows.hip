@@ -4,9 +4,10 @@
 // token-major scatter form, which reads every token row once and writes it to
 // each of its k dispatched rows.
 //
-// Both are HBM-bound byte copies.  A workgroup owns one row (or a column
-// chunk of at most 1024 vectors of one row) and each thread moves exactly one
-// 16-byte vector: one load, then one store per destination.  Short-lived
+// Both are HBM-bound byte copies.  A workgroup owns a column chunk of at most
+// 128 vectors of one row (the chunks of a row are neighbours in the grid) and
+// each thread moves exactly one 16-byte vector: one load, then one store per
+// destination.  Short-lived
 // workgroups with one access per thread sustained the highest write rate on
 // MI355X (several accesses per thread, or looping workgroups, wrote slower).
 // The write-once destination rows are stored non-temporal and system-coherent
@@ -20,7 +21,10 @@
 namespace mxmoe {
 namespace {
 
-constexpr int kMaxRowThreads = 1024;
+// Workgroup width of the row copies: rows of more than 128 vectors are cut
+// into column chunks.  Two-wave workgroups copied 1-2% faster than one
+// workgroup per 14 KiB row (896 threads).
+constexpr int kRowThreads = 128;
 
 
 template <int V> struct Vec;
@@ -63,39 +67,41 @@ __device__ __forceinline__ void copy_vector_to(const T* __restrict__ in, int64_t
     }
 }
 
-// dst[r] = src[dst2src[r]]: workgroup (blockIdx.x = r, blockIdx.y = column
-// chunk), one vector per thread.
+// dst[r] = src[dst2src[r]]: one workgroup per destination row r and column
+// chunk, one vector per thread.
 template <int V>
-__global__ __launch_bounds__(kMaxRowThreads) void shuffle_rows_kernel(
+__global__ __launch_bounds__(kRowThreads) void shuffle_rows_kernel(
     const uint8_t* __restrict__ src, int64_t num_src_rows, int64_t row_bytes,
-    const int32_t* __restrict__ dst2src, uint8_t* __restrict__ dst) {
+    const int32_t* __restrict__ dst2src, uint8_t* __restrict__ dst, int32_t chunks) {
     using T = typename Vec<V>::T;
-    const int32_t r = (int32_t)blockIdx.x;
+    int64_t chunk;
+    const int64_t r = chunk_row(chunks, chunk);
     const int32_t s = dst2src[r];
     if (s < 0 || s >= num_src_rows) return;
-    const int64_t c = (int64_t)blockIdx.y * blockDim.x + threadIdx.x;
+    const int64_t c = chunk * blockDim.x + threadIdx.x;
     const T* in = reinterpret_cast<const T*>(src + (int64_t)s * row_bytes);
-    copy_vector_to<T>(in, c, row_bytes / V, dst, row_bytes, nullptr, 1, (int64_t)r + 1, r);
+    copy_vector_to<T>(in, c, row_bytes / V, dst, row_bytes, nullptr, 1, r + 1, (int32_t)r);
 }
 
-// dst[output_perm[t*k + j]] = src[t] for every j: workgroup (blockIdx.x =
-// token t, blockIdx.y = column chunk), one vector per thread; the side row
-// (if any) goes with chunk 0.
+// dst[output_perm[t*k + j]] = src[t] for every j: one workgroup per token t
+// and column chunk, one vector per thread; the side row (if any) goes with
+// chunk 0.
 template <int V, int SV>
-__global__ __launch_bounds__(kMaxRowThreads) void dispatch_rows_kernel(
+__global__ __launch_bounds__(kRowThreads) void dispatch_rows_kernel(
     const uint8_t* __restrict__ src, int64_t row_bytes, int32_t topk,
     const int32_t* __restrict__ output_perm, uint8_t* __restrict__ dst, int64_t num_dst_rows,
     const uint8_t* __restrict__ side_src, int64_t side_row_bytes,
-    uint8_t* __restrict__ side_dst) {
+    uint8_t* __restrict__ side_dst, int32_t chunks) {
     using T = typename Vec<V>::T;
-    const int64_t t = blockIdx.x;
+    int64_t chunk;
+    const int64_t t = chunk_row(chunks, chunk);
     const int32_t* rows = output_perm + t * topk;
-    const int64_t c = (int64_t)blockIdx.y * blockDim.x + threadIdx.x;
+    const int64_t c = chunk * blockDim.x + threadIdx.x;
     copy_vector_to<T>(reinterpret_cast<const T*>(src + t * row_bytes), c, row_bytes / V, dst,
                       row_bytes, rows, topk, num_dst_rows);
     if constexpr (SV > 0) {
         using S = typename Vec<SV>::T;
-        if (blockIdx.y == 0) {
+        if (chunk == 0) {
             const int64_t ns = side_row_bytes / SV;
             for (int64_t c0 = 0; c0 < ns; c0 += blockDim.x)
                 copy_vector_to<S>(reinterpret_cast<const S*>(side_src + t * side_row_bytes),
@@ -112,30 +118,17 @@ int vec_width(int64_t row_bytes, const void* a, const void* b) {
     return 1;
 }
 
-// Launch shape: one vector per thread; a row of nvec vectors is cut into the
-// fewest column chunks of at most kMaxRowThreads vectors, and the workgroup
-// width is the chunk rounded up to whole waves.
-void row_grid(int64_t rows, int64_t row_bytes, int v, dim3& grid, dim3& block) {
-    const int64_t nvec = row_bytes / v;
-    const int64_t chunks = (nvec + kMaxRowThreads - 1) / kMaxRowThreads;
-    int64_t threads = (nvec + chunks - 1) / chunks;
-    threads = (threads + kWave - 1) / kWave * kWave;
-    grid = dim3((unsigned)rows, (unsigned)chunks, 1);
-    block = dim3((unsigned)threads, 1, 1);
-}
-
 template <int V>
-hipError_t launch_dispatch_v(dim3 grid, dim3 block, int side_vec, const uint8_t* s,
-                             int64_t row_bytes, int32_t topk, const int32_t* output_perm,
-                             uint8_t* d, int64_t num_dst_rows, const uint8_t* ss,
-                             int64_t side_row_bytes, uint8_t* sd, hipStream_t stream) {
+void launch_dispatch_v(dim3 grid, dim3 block, int32_t chunks, int side_vec, const uint8_t* s,
+                       int64_t row_bytes, int32_t topk, const int32_t* output_perm, uint8_t* d,
+                       int64_t num_dst_rows, const uint8_t* ss, int64_t side_row_bytes,
+                       uint8_t* sd, hipStream_t stream) {
     switch (side_vec) {
-    case 0: dispatch_rows_kernel<V, 0><<<grid, block, 0, stream>>>(s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd); break;
-    case 16: dispatch_rows_kernel<V, 16><<<grid, block, 0, stream>>>(s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd); break;
-    case 4: dispatch_rows_kernel<V, 4><<<grid, block, 0, stream>>>(s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd); break;
-    default: dispatch_rows_kernel<V, 1><<<grid, block, 0, stream>>>(s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd); break;
+    case 0: dispatch_rows_kernel<V, 0><<<grid, block, 0, stream>>>(s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd, chunks); break;
+    case 16: dispatch_rows_kernel<V, 16><<<grid, block, 0, stream>>>(s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd, chunks); break;
+    case 4: dispatch_rows_kernel<V, 4><<<grid, block, 0, stream>>>(s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd, chunks); break;
+    default: dispatch_rows_kernel<V, 1><<<grid, block, 0, stream>>>(s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd, chunks); break;
     }
-    return hipGetLastError();
 }
 
 }  // namespace
@@ -145,18 +138,20 @@ hipError_t launch_shuffle_rows(const void* src, int64_t num_src_rows, int64_t ro
                                hipStream_t stream) {
     if (num_dst_rows == 0) return hipSuccess;
     const int v = vec_width(row_bytes, src, dst);
-    dim3 grid, block;
-    row_grid(num_dst_rows, row_bytes, v, grid, block);
+    const RowShape sh = row_shape(row_bytes / v, kRowThreads);
     const uint8_t* s = static_cast<const uint8_t*>(src);
     uint8_t* d = static_cast<uint8_t*>(dst);
-    switch (v) {
-    case 16: shuffle_rows_kernel<16><<<grid, block, 0, stream>>>(s, num_src_rows, row_bytes, dst2src, d); break;
-    case 8: shuffle_rows_kernel<8><<<grid, block, 0, stream>>>(s, num_src_rows, row_bytes, dst2src, d); break;
-    case 4: shuffle_rows_kernel<4><<<grid, block, 0, stream>>>(s, num_src_rows, row_bytes, dst2src, d); break;
-    case 2: shuffle_rows_kernel<2><<<grid, block, 0, stream>>>(s, num_src_rows, row_bytes, dst2src, d); break;
-    default: shuffle_rows_kernel<1><<<grid, block, 0, stream>>>(s, num_src_rows, row_bytes, dst2src, d); break;
-    }
-    return hipGetLastError();
+    return for_row_batches(num_dst_rows, sh, [&](int64_t r0, int64_t, dim3 grid, dim3 block) {
+        const int32_t* m = dst2src + r0;
+        uint8_t* dr = d + r0 * row_bytes;
+        switch (v) {
+        case 16: shuffle_rows_kernel<16><<<grid, block, 0, stream>>>(s, num_src_rows, row_bytes, m, dr, sh.chunks); break;
+        case 8: shuffle_rows_kernel<8><<<grid, block, 0, stream>>>(s, num_src_rows, row_bytes, m, dr, sh.chunks); break;
+        case 4: shuffle_rows_kernel<4><<<grid, block, 0, stream>>>(s, num_src_rows, row_bytes, m, dr, sh.chunks); break;
+        case 2: shuffle_rows_kernel<2><<<grid, block, 0, stream>>>(s, num_src_rows, row_bytes, m, dr, sh.chunks); break;
+        default: shuffle_rows_kernel<1><<<grid, block, 0, stream>>>(s, num_src_rows, row_bytes, m, dr, sh.chunks); break;
+        }
+    });
 }
 
 hipError_t launch_dispatch_rows(const void* src, int64_t num_tokens, int32_t topk,
@@ -170,19 +165,23 @@ hipError_t launch_dispatch_rows(const void* src, int64_t num_tokens, int32_t top
         const int sv = vec_width(side_row_bytes, side_src, side_dst);
         side_vec = sv >= 16 ? 16 : sv >= 4 ? 4 : 1;
     }
-    dim3 grid, block;
-    row_grid(num_tokens, row_bytes, v, grid, block);
+    const RowShape sh = row_shape(row_bytes / v, kRowThreads);
     const uint8_t* s = static_cast<const uint8_t*>(src);
     uint8_t* d = static_cast<uint8_t*>(dst);
     const uint8_t* ss = static_cast<const uint8_t*>(side_src);
     uint8_t* sd = static_cast<uint8_t*>(side_dst);
-    switch (v) {
-    case 16: return launch_dispatch_v<16>(grid, block, side_vec, s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd, stream);
-    case 8: return launch_dispatch_v<8>(grid, block, side_vec, s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd, stream);
-    case 4: return launch_dispatch_v<4>(grid, block, side_vec, s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd, stream);
-    case 2: return launch_dispatch_v<2>(grid, block, side_vec, s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd, stream);
-    default: return launch_dispatch_v<1>(grid, block, side_vec, s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd, stream);
-    }
+    return for_row_batches(num_tokens, sh, [&](int64_t t0, int64_t, dim3 grid, dim3 block) {
+        const uint8_t* st = s + t0 * row_bytes;
+        const int32_t* pt = output_perm + t0 * topk;
+        const uint8_t* sst = ss ? ss + t0 * side_row_bytes : nullptr;
+        switch (v) {
+        case 16: launch_dispatch_v<16>(grid, block, sh.chunks, side_vec, st, row_bytes, topk, pt, d, num_dst_rows, sst, side_row_bytes, sd, stream); break;
+        case 8: launch_dispatch_v<8>(grid, block, sh.chunks, side_vec, st, row_bytes, topk, pt, d, num_dst_rows, sst, side_row_bytes, sd, stream); break;
+        case 4: launch_dispatch_v<4>(grid, block, sh.chunks, side_vec, st, row_bytes, topk, pt, d, num_dst_rows, sst, side_row_bytes, sd, stream); break;
+        case 2: launch_dispatch_v<2>(grid, block, sh.chunks, side_vec, st, row_bytes, topk, pt, d, num_dst_rows, sst, side_row_bytes, sd, stream); break;
+        default: launch_dispatch_v<1>(grid, block, sh.chunks, side_vec, st, row_bytes, topk, pt, d, num_dst_rows, sst, side_row_bytes, sd, stream); break;
+        }
+    });
 }
 
 }  // namespace mxmoe

@@ -14,7 +14,8 @@
 namespace mxmoe {
 namespace {
 
-constexpr int kMaxZeroThreads = 1024;
+constexpr int kZeroThreads = 128;       // workgroup width of the per-row kernels
+constexpr int kMaxZeroThreads = 1024;   // workgroup width limit of the per-segment kernel
 
 
 template <int V> struct ZVec;
@@ -30,22 +31,17 @@ __device__ __forceinline__ void zero_vector(uint8_t* row, int64_t c, int64_t nve
     if (c < nvec) __builtin_nontemporal_store(T{}, reinterpret_cast<T*>(row) + c);
 }
 
-// Without expert offsets: row blockIdx.x is zeroed iff its source index is
-// negative (every row of the buffer is considered).
+// Without expert offsets: row r is zeroed iff its source index is negative
+// (every row of the buffer is considered); one workgroup per row and column
+// chunk.
 template <int V>
-__global__ __launch_bounds__(kMaxZeroThreads) void zero_padding_kernel(
-    uint8_t* __restrict__ rows, int64_t num_rows, int64_t row_bytes,
-    const int32_t* __restrict__ input_perm, const int32_t* __restrict__ expert_offsets,
-    int32_t num_experts) {
-    const int64_t r = blockIdx.x;
-    int64_t limit = num_rows;
-    if (expert_offsets != nullptr) {
-        const int64_t total = expert_offsets[num_experts];
-        if (total < limit) limit = total;
-    }
-    if (r >= limit || input_perm[r] >= 0) return;
-    zero_vector<V>(rows + r * row_bytes, (int64_t)blockIdx.y * blockDim.x + threadIdx.x,
-                   row_bytes / V);
+__global__ __launch_bounds__(kZeroThreads) void zero_padding_kernel(
+    uint8_t* __restrict__ rows, int64_t row_bytes, const int32_t* __restrict__ input_perm,
+    int32_t chunks) {
+    int64_t chunk;
+    const int64_t r = chunk_row(chunks, chunk);
+    if (input_perm[r] >= 0) return;
+    zero_vector<V>(rows + r * row_bytes, chunk * blockDim.x + threadIdx.x, row_bytes / V);
 }
 
 // With expert offsets only the rows inside the expert segments are
@@ -84,13 +80,14 @@ __global__ __launch_bounds__(kMaxZeroThreads) void zero_padding_expert_kernel(
     }
 }
 
-// Output row blockIdx.x (token t) is zeroed iff one of its topk picks has
-// a permuted index >= 0.
+// Output row t is zeroed iff one of its topk picks has a permuted index
+// >= 0; one workgroup per row and column chunk.
 template <int V>
-__global__ __launch_bounds__(kMaxZeroThreads) void output_memset_kernel(
+__global__ __launch_bounds__(kZeroThreads) void output_memset_kernel(
     uint8_t* __restrict__ out, int64_t row_bytes, int32_t topk,
-    const int32_t* __restrict__ expanded_to_permuted) {
-    const int64_t t = blockIdx.x;
+    const int32_t* __restrict__ expanded_to_permuted, int32_t chunks) {
+    int64_t chunk;
+    const int64_t t = chunk_row(chunks, chunk);
     const int lane = threadIdx.x & (kWave - 1);
     bool any = false;
     for (int j0 = 0; j0 < topk; j0 += kWave) {       // wave-uniform
@@ -99,8 +96,7 @@ __global__ __launch_bounds__(kMaxZeroThreads) void output_memset_kernel(
         any = any || __ballot(valid) != 0ull;
     }
     if (!any) return;
-    zero_vector<V>(out + t * row_bytes, (int64_t)blockIdx.y * blockDim.x + threadIdx.x,
-                   row_bytes / V);
+    zero_vector<V>(out + t * row_bytes, chunk * blockDim.x + threadIdx.x, row_bytes / V);
 }
 
 int zvec_width(int64_t row_bytes, const void* p) {
@@ -110,14 +106,6 @@ int zvec_width(int64_t row_bytes, const void* p) {
     return 1;
 }
 
-void zero_grid(int64_t rows, int64_t row_bytes, int v, dim3& grid, dim3& block) {
-    const int64_t nvec = row_bytes / v;
-    const int64_t chunks = (nvec + kMaxZeroThreads - 1) / kMaxZeroThreads;
-    int64_t threads = (nvec + chunks - 1) / chunks;
-    threads = (threads + kWave - 1) / kWave * kWave;
-    grid = dim3((unsigned)rows, (unsigned)chunks, 1);
-    block = dim3((unsigned)threads, 1, 1);
-}
 
 }  // namespace
 
@@ -126,11 +114,13 @@ hipError_t launch_zero_padding(void* rows, int64_t num_rows, int64_t row_bytes,
                                int32_t num_experts, hipStream_t stream) {
     if (num_rows == 0) return hipSuccess;
     const int v = zvec_width(row_bytes, rows);
-    dim3 grid, block;
-    zero_grid(num_rows, row_bytes, v, grid, block);
     uint8_t* p = static_cast<uint8_t*>(rows);
     if (expert_offsets != nullptr) {
+        // The segment kernel loops over a row's vectors, one workgroup of at
+        // most kMaxZeroThreads threads per (expert, slice).
+        const RowShape sh = row_shape(row_bytes / v, kMaxZeroThreads);
         const dim3 egrid((unsigned)num_experts, kSlices, 1);
+        const dim3 block((unsigned)sh.threads, 1, 1);
         switch (v) {
         case 16: zero_padding_expert_kernel<16><<<egrid, block, 0, stream>>>(p, num_rows, row_bytes, input_perm, expert_offsets); break;
         case 8: zero_padding_expert_kernel<8><<<egrid, block, 0, stream>>>(p, num_rows, row_bytes, input_perm, expert_offsets); break;
@@ -140,31 +130,37 @@ hipError_t launch_zero_padding(void* rows, int64_t num_rows, int64_t row_bytes,
         }
         return hipGetLastError();
     }
-    switch (v) {
-    case 16: zero_padding_kernel<16><<<grid, block, 0, stream>>>(p, num_rows, row_bytes, input_perm, nullptr, 0); break;
-    case 8: zero_padding_kernel<8><<<grid, block, 0, stream>>>(p, num_rows, row_bytes, input_perm, nullptr, 0); break;
-    case 4: zero_padding_kernel<4><<<grid, block, 0, stream>>>(p, num_rows, row_bytes, input_perm, nullptr, 0); break;
-    case 2: zero_padding_kernel<2><<<grid, block, 0, stream>>>(p, num_rows, row_bytes, input_perm, nullptr, 0); break;
-    default: zero_padding_kernel<1><<<grid, block, 0, stream>>>(p, num_rows, row_bytes, input_perm, nullptr, 0); break;
-    }
-    return hipGetLastError();
+    const RowShape sh = row_shape(row_bytes / v, kZeroThreads);
+    return for_row_batches(num_rows, sh, [&](int64_t r0, int64_t, dim3 grid, dim3 block) {
+        uint8_t* pr = p + r0 * row_bytes;
+        const int32_t* m = input_perm + r0;
+        switch (v) {
+        case 16: zero_padding_kernel<16><<<grid, block, 0, stream>>>(pr, row_bytes, m, sh.chunks); break;
+        case 8: zero_padding_kernel<8><<<grid, block, 0, stream>>>(pr, row_bytes, m, sh.chunks); break;
+        case 4: zero_padding_kernel<4><<<grid, block, 0, stream>>>(pr, row_bytes, m, sh.chunks); break;
+        case 2: zero_padding_kernel<2><<<grid, block, 0, stream>>>(pr, row_bytes, m, sh.chunks); break;
+        default: zero_padding_kernel<1><<<grid, block, 0, stream>>>(pr, row_bytes, m, sh.chunks); break;
+        }
+    });
 }
 
 hipError_t launch_output_memset(void* out, int64_t num_tokens, int32_t topk, int64_t row_bytes,
                                 const int32_t* expanded_to_permuted, hipStream_t stream) {
     if (num_tokens == 0) return hipSuccess;
     const int v = zvec_width(row_bytes, out);
-    dim3 grid, block;
-    zero_grid(num_tokens, row_bytes, v, grid, block);
+    const RowShape sh = row_shape(row_bytes / v, kZeroThreads);
     uint8_t* p = static_cast<uint8_t*>(out);
-    switch (v) {
-    case 16: output_memset_kernel<16><<<grid, block, 0, stream>>>(p, row_bytes, topk, expanded_to_permuted); break;
-    case 8: output_memset_kernel<8><<<grid, block, 0, stream>>>(p, row_bytes, topk, expanded_to_permuted); break;
-    case 4: output_memset_kernel<4><<<grid, block, 0, stream>>>(p, row_bytes, topk, expanded_to_permuted); break;
-    case 2: output_memset_kernel<2><<<grid, block, 0, stream>>>(p, row_bytes, topk, expanded_to_permuted); break;
-    default: output_memset_kernel<1><<<grid, block, 0, stream>>>(p, row_bytes, topk, expanded_to_permuted); break;
-    }
-    return hipGetLastError();
+    return for_row_batches(num_tokens, sh, [&](int64_t t0, int64_t, dim3 grid, dim3 block) {
+        uint8_t* pt = p + t0 * row_bytes;
+        const int32_t* e = expanded_to_permuted + t0 * topk;
+        switch (v) {
+        case 16: output_memset_kernel<16><<<grid, block, 0, stream>>>(pt, row_bytes, topk, e, sh.chunks); break;
+        case 8: output_memset_kernel<8><<<grid, block, 0, stream>>>(pt, row_bytes, topk, e, sh.chunks); break;
+        case 4: output_memset_kernel<4><<<grid, block, 0, stream>>>(pt, row_bytes, topk, e, sh.chunks); break;
+        case 2: output_memset_kernel<2><<<grid, block, 0, stream>>>(pt, row_bytes, topk, e, sh.chunks); break;
+        default: output_memset_kernel<1><<<grid, block, 0, stream>>>(pt, row_bytes, topk, e, sh.chunks); break;
+        }
+    });
 }
 
 }  // namespace mxmoe
