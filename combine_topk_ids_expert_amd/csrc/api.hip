@@ -9,8 +9,8 @@
 namespace {
 
 constexpr int64_t kMax31 = (int64_t)0x7fffffff;
-// Rows are cut into column chunks of at most 1024 accesses (gridDim.y <= 65535);
-// with 1-byte accesses that bounds a row at 65535 * 1024 bytes.
+// Longest row accepted: just under 64 MiB, so that a row's byte offsets, its
+// buffer descriptors' extents and its column-chunk counts stay 32-bit.
 constexpr int64_t kMaxRowBytes = (int64_t)65535 * 1024;
 thread_local int g_last_hip_error = 0;
 

@@ -43,8 +43,11 @@ def _print_case(*args):
     (257, 256, 8, 1, "uniform", 0.0),           # two launches: 2056 picks, 5 tiles
     (1000, 256, 8, 128, "uniform", 0.0),        # 16 tiles, padded
     (1025, 256, 8, 1, "uniform", 0.0),          # ragged last tile
-    (8192, 256, 8, 1, "uniform", 0.0),          # 65536 picks: 128 tiles of 512
-    (8193, 256, 8, 128, "uniform", 0.02),       # tiles grow past 512 picks
+    (8192, 256, 8, 1, "uniform", 0.0),          # 65536 picks, E = 256: 64 tiles of 1024
+    (8193, 256, 8, 128, "uniform", 0.02),       # tiles grow past 1024 picks
+    (8192, 128, 8, 1, "uniform", 0.0),          # 65536 picks, E = 128: 128 tiles of 512
+    (8193, 128, 8, 1, "uniform", 0.0),          # 65 tiles of 1024: table rows of 17 vectors
+    (9000, 1024, 8, 1, "uniform", 0.01),        # tile count held up by the one-round floor
     (3000, 1000, 8, 4, "uniform", 0.05),        # E not a power of two, invalid ids
     (2000, 100, 8, 8, "k_hot", 0.0),
     (4000, 8, 4, 1, "dups", 0.0),               # few experts, many duplicates
