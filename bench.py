@@ -15,8 +15,10 @@ dominant kernel's achieved algorithmic HBM bandwidth against MI355X's
 8 TB/s, and the CPU oracle timed on a bounded sample of the same workload on
 the host.
 
---copy-probe BYTES times a plain device copy of BYTES bytes instead (the
-reference kernel whose HBM counters calibrate the traffic figures).
+--graph captures one step's launches in a HIP graph and times K replays of
+it, so the headline holds no host launch cost (the per-stage event pass stays
+eager).  --copy-probe BYTES times a plain device copy of BYTES bytes instead
+(the reference kernel whose HBM counters calibrate the traffic figures).
 """
 
 from __future__ import annotations
@@ -65,6 +67,8 @@ def parse_args():
                    help="wall-clock budget of the CPU-oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-probe", type=int, default=0, metavar="BYTES")
+    p.add_argument("--graph", action="store_true",
+                   help="time replays of a HIP graph of one step instead of eager launches")
     p.add_argument("--with", dest="extras", default="",
                    help="comma-separated extra stages added to each step and reported "
                         "separately: zero_padding (zero-fill the padding rows after "
@@ -246,12 +250,25 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
+    graph = None
+    if args.graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _, fn in stages:
+                fn()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
     # Headline: exactly K steps between two device synchronisations.
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(K):
-        for _, fn in stages:
-            fn()
+    if graph is not None:
+        for _ in range(K):
+            graph.replay()
+    else:
+        for _ in range(K):
+            for _, fn in stages:
+                fn()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
@@ -321,7 +338,8 @@ def main():
         "dtype": {"fp8": "fp8-e4m3 rows, bf16 combine"}.get(w.x_dtype, w.x_dtype),
         "data": "synthetic",
         "config": {"workload": w.name, "T": T, "H": H, "E": E, "topk": k, "routing": w.mode,
-                   "row_align": w.row_align, "x_dtype": w.x_dtype, "out_dtype": w.out_dtype},
+                   "row_align": w.row_align, "x_dtype": w.x_dtype, "out_dtype": w.out_dtype,
+                   "launch": "hip_graph" if graph is not None else "eager"},
         "roofline": {"bound": "hbm", "kernel": kernel_name, "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic["traffic_bytes"] if traffic else None,

@@ -1,0 +1,50 @@
+"""bench.py's contract on the host (no GPU): the one-GPU rule, the byte
+accounting of its roofline, and the source hash that keys the counters."""
+
+import os
+import subprocess
+import sys
+
+import pytest
+
+import bench
+from workloads import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# Algorithmic MB per step (dispatch, combine) of each workload, all ids valid:
+# dispatch reads every token row once and writes it to its k rows (+ the fp32
+# 1x128 scale rows of the fp8 workload) and reads T*k int32 row indices;
+# combine reads the T*k expert rows, writes T output rows and reads T*k
+# indices and T*k fp32 weights.  Worked out by hand from the shapes.
+EXPECTED_MB = {
+    "uniform_T32_H4096_E256_k8": (2.360, 2.361),
+    "uniform_T4096_H7168_E256_k8_pad128": (528.61, 528.74),
+    "khot8_T8192_H7168_E256_k8": (1057.23, 1057.49),
+    "zipf1.2_T16384_H4096fp8_E128_k8": (623.38, 1209.01),
+    "replica288_T65536_H7168_k8_f32out": (8457.81, 9399.44),
+}
+
+
+@pytest.mark.parametrize("name", sorted(EXPECTED_MB))
+def test_algorithmic_bytes_match_hand_count(name):
+    w = WORKLOADS[name]
+    n = w.T * w.k
+    b = bench.algorithmic_bytes(w, n, n, 8)
+    disp, comb = EXPECTED_MB[name]
+    assert b["dispatch"] / 1e6 == pytest.approx(disp, abs=0.01)
+    assert b["combine"] / 1e6 == pytest.approx(comb, abs=0.01)
+
+
+def test_more_than_one_gpu_is_refused():
+    proc = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                          capture_output=True, text=True, timeout=120)
+    assert proc.returncode == 2
+    assert "one GPU" in proc.stderr
+
+
+def test_source_hash_ignores_comments_and_whitespace():
+    a = "int f(int x) {  // add one\n    return x + 1; /* done */\n}\n"
+    b = "int f(int x)\n{\n\treturn x + 1;\n}"
+    assert bench._code_only(a) == bench._code_only(b)
+    assert bench._code_only(a) != bench._code_only(b.replace("1", "2"))
