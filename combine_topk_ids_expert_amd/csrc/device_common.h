@@ -55,19 +55,33 @@ __device__ __forceinline__ int64_t chunk_row(int32_t chunks, int64_t& chunk) {
     return (int64_t)r;
 }
 
+// Cache policies of store16 (gfx950 policy bits: sc0 = 1, nt = 2, sc1 = 16).
+//   kStream  sc0 nt sc1: non-temporal, system-coherent.
+//   kKeep    sc1: allocating in the caches, system-coherent.
+// For the scattered write-once destination rows of the row dispatch, kStream
+// measured 1.5-2% faster on MI355X than a plain non-temporal global store as
+// long as the source rows fit in the 256 MB Infinity Cache; beyond that,
+// kKeep was 1.6-2.6% faster (T = 24576 to 65536 rows of 14 KiB), and below
+// it 12-14% slower, since the allocated destination lines evict the source
+// rows.  kCacheResidentBytes is the source size up to which the row dispatch
+// uses kStream.
+enum StorePolicy : int { kStream = 1 | 2 | 16, kKeep = 16 };
+constexpr int64_t kCacheResidentBytes = (int64_t)256 << 20;
+
+inline StorePolicy dispatch_store_policy(int64_t source_bytes) {
+    return source_bytes > kCacheResidentBytes ? kKeep : kStream;
+}
+
 // 16-byte store of vector v at byte offset `off` of a row that starts at
 // `row` (the row base wave-uniform, the offset per lane), through a raw
-// buffer store whose cache policy is non-temporal and system-coherent
-// (sc0 nt sc1, policy bits 1 | 2 | 16 on gfx950).  For the scattered
-// write-once destination rows of dispatch this measured 1.5-2% faster on
-// MI355X than a plain non-temporal global store.  The buffer's extent is the
-// row, so a store past row_bytes would be dropped by the hardware; callers
-// only store inside it.  0x00020000 is the gfx9 raw-buffer format word.
-__device__ __forceinline__ void store16_stream(u32x4 v, uint8_t* row, int64_t row_bytes,
-                                               int64_t off) {
+// buffer store with cache policy P.  The buffer's extent is the row, so a
+// store past row_bytes would be dropped by the hardware; callers only store
+// inside it.  0x00020000 is the gfx9 raw-buffer format word.
+template <int P>
+__device__ __forceinline__ void store16(u32x4 v, uint8_t* row, int64_t row_bytes, int64_t off) {
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc(row, (short)0, (int)row_bytes, 0x00020000);
-    __builtin_amdgcn_raw_buffer_store_b128(v, rs, (int)off, 0, 1 | 2 | 16);
+    __builtin_amdgcn_raw_buffer_store_b128(v, rs, (int)off, 0, P);
 }
 
 // Number of lanes below this one whose bit is set in `mask`.

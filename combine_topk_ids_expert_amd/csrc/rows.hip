@@ -7,14 +7,14 @@
 // Both are HBM-bound byte copies.  A workgroup owns a column chunk of at most
 // 128 vectors of one row (the chunks of a row are neighbours in the grid) and
 // each thread moves exactly one 16-byte vector: one load, then one store per
-// destination.  Short-lived
-// workgroups with one access per thread sustained the highest write rate on
-// MI355X (several accesses per thread, or looping workgroups, wrote slower).
-// The write-once destination rows are stored non-temporal and system-coherent
-// (store16_stream), the source rows are loaded with the default policy: both
-// measured fastest of the cache policies tried.  Rows whose byte width or base
-// pointers are not multiples of 16 fall back to the widest access width that
-// divides them.
+// destination.  Short-lived workgroups with one access per thread sustained
+// the highest write rate on MI355X (several accesses per thread, or looping
+// workgroups, wrote slower).  The write-once destination rows are stored
+// system-coherent: non-temporal while the source rows fit in the Infinity
+// Cache, allocating beyond that (store16, dispatch_store_policy).  The source
+// rows are loaded with the default policy.  Each measured fastest of the
+// cache policies tried.  Rows whose byte width or base pointers are not
+// multiples of 16 fall back to the widest access width that divides them.
 #include "device_common.h"
 #include "launch.h"
 
@@ -40,9 +40,9 @@ template <> struct Vec<1> { using T = uint8_t; };
 // part in the wave-uniform destination loop but access nothing.  The
 // destination indices sit one per lane and are broadcast with readlane;
 // destination rows are written once and not read again by this pass, so the
-// stores carry the non-temporal hint (16-byte ones through store16_stream,
-// which adds the system-coherent bits).
-template <typename T>
+// narrow stores carry the non-temporal hint and the 16-byte ones go through
+// store16 with cache policy P.
+template <typename T, int P = kStream>
 __device__ __forceinline__ void copy_vector_to(const T* __restrict__ in, int64_t c, int64_t nvec,
                                                uint8_t* __restrict__ dst, int64_t row_bytes,
                                                const int32_t* __restrict__ rows, int n,
@@ -60,7 +60,7 @@ __device__ __forceinline__ void copy_vector_to(const T* __restrict__ in, int64_t
             if (r < 0 || !live) continue;
             uint8_t* row = dst + (int64_t)r * row_bytes;
             if constexpr (sizeof(T) == 16)
-                store16_stream(v, row, row_bytes, c * 16);
+                store16<P>(v, row, row_bytes, c * 16);
             else
                 __builtin_nontemporal_store(v, reinterpret_cast<T*>(row) + c);
         }
@@ -85,8 +85,8 @@ __global__ __launch_bounds__(kRowThreads) void shuffle_rows_kernel(
 
 // dst[output_perm[t*k + j]] = src[t] for every j: one workgroup per token t
 // and column chunk, one vector per thread; the side row (if any) goes with
-// chunk 0.
-template <int V, int SV>
+// chunk 0.  P is the cache policy of the 16-byte stores.
+template <int V, int SV, int P>
 __global__ __launch_bounds__(kRowThreads) void dispatch_rows_kernel(
     const uint8_t* __restrict__ src, int64_t row_bytes, int32_t topk,
     const int32_t* __restrict__ output_perm, uint8_t* __restrict__ dst, int64_t num_dst_rows,
@@ -97,16 +97,16 @@ __global__ __launch_bounds__(kRowThreads) void dispatch_rows_kernel(
     const int64_t t = chunk_row(chunks, chunk);
     const int32_t* rows = output_perm + t * topk;
     const int64_t c = chunk * blockDim.x + threadIdx.x;
-    copy_vector_to<T>(reinterpret_cast<const T*>(src + t * row_bytes), c, row_bytes / V, dst,
-                      row_bytes, rows, topk, num_dst_rows);
+    copy_vector_to<T, P>(reinterpret_cast<const T*>(src + t * row_bytes), c, row_bytes / V, dst,
+                         row_bytes, rows, topk, num_dst_rows);
     if constexpr (SV > 0) {
         using S = typename Vec<SV>::T;
         if (chunk == 0) {
             const int64_t ns = side_row_bytes / SV;
             for (int64_t c0 = 0; c0 < ns; c0 += blockDim.x)
-                copy_vector_to<S>(reinterpret_cast<const S*>(side_src + t * side_row_bytes),
-                                  c0 + threadIdx.x, ns, side_dst, side_row_bytes, rows, topk,
-                                  num_dst_rows);
+                copy_vector_to<S, P>(reinterpret_cast<const S*>(side_src + t * side_row_bytes),
+                                     c0 + threadIdx.x, ns, side_dst, side_row_bytes, rows, topk,
+                                     num_dst_rows);
         }
     }
 }
@@ -118,16 +118,16 @@ int vec_width(int64_t row_bytes, const void* a, const void* b) {
     return 1;
 }
 
-template <int V>
+template <int V, int P>
 void launch_dispatch_v(dim3 grid, dim3 block, int32_t chunks, int side_vec, const uint8_t* s,
                        int64_t row_bytes, int32_t topk, const int32_t* output_perm, uint8_t* d,
                        int64_t num_dst_rows, const uint8_t* ss, int64_t side_row_bytes,
                        uint8_t* sd, hipStream_t stream) {
     switch (side_vec) {
-    case 0: dispatch_rows_kernel<V, 0><<<grid, block, 0, stream>>>(s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd, chunks); break;
-    case 16: dispatch_rows_kernel<V, 16><<<grid, block, 0, stream>>>(s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd, chunks); break;
-    case 4: dispatch_rows_kernel<V, 4><<<grid, block, 0, stream>>>(s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd, chunks); break;
-    default: dispatch_rows_kernel<V, 1><<<grid, block, 0, stream>>>(s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd, chunks); break;
+    case 0: dispatch_rows_kernel<V, 0, P><<<grid, block, 0, stream>>>(s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd, chunks); break;
+    case 16: dispatch_rows_kernel<V, 16, P><<<grid, block, 0, stream>>>(s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd, chunks); break;
+    case 4: dispatch_rows_kernel<V, 4, P><<<grid, block, 0, stream>>>(s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd, chunks); break;
+    default: dispatch_rows_kernel<V, 1, P><<<grid, block, 0, stream>>>(s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd, chunks); break;
     }
 }
 
@@ -166,6 +166,7 @@ hipError_t launch_dispatch_rows(const void* src, int64_t num_tokens, int32_t top
         side_vec = sv >= 16 ? 16 : sv >= 4 ? 4 : 1;
     }
     const RowShape sh = row_shape(row_bytes / v, kRowThreads);
+    const bool keep = dispatch_store_policy(num_tokens * (row_bytes + side_row_bytes)) == kKeep;
     const uint8_t* s = static_cast<const uint8_t*>(src);
     uint8_t* d = static_cast<uint8_t*>(dst);
     const uint8_t* ss = static_cast<const uint8_t*>(side_src);
@@ -175,11 +176,14 @@ hipError_t launch_dispatch_rows(const void* src, int64_t num_tokens, int32_t top
         const int32_t* pt = output_perm + t0 * topk;
         const uint8_t* sst = ss ? ss + t0 * side_row_bytes : nullptr;
         switch (v) {
-        case 16: launch_dispatch_v<16>(grid, block, sh.chunks, side_vec, st, row_bytes, topk, pt, d, num_dst_rows, sst, side_row_bytes, sd, stream); break;
-        case 8: launch_dispatch_v<8>(grid, block, sh.chunks, side_vec, st, row_bytes, topk, pt, d, num_dst_rows, sst, side_row_bytes, sd, stream); break;
-        case 4: launch_dispatch_v<4>(grid, block, sh.chunks, side_vec, st, row_bytes, topk, pt, d, num_dst_rows, sst, side_row_bytes, sd, stream); break;
-        case 2: launch_dispatch_v<2>(grid, block, sh.chunks, side_vec, st, row_bytes, topk, pt, d, num_dst_rows, sst, side_row_bytes, sd, stream); break;
-        default: launch_dispatch_v<1>(grid, block, sh.chunks, side_vec, st, row_bytes, topk, pt, d, num_dst_rows, sst, side_row_bytes, sd, stream); break;
+        case 16:
+            if (keep) launch_dispatch_v<16, kKeep>(grid, block, sh.chunks, side_vec, st, row_bytes, topk, pt, d, num_dst_rows, sst, side_row_bytes, sd, stream);
+            else launch_dispatch_v<16, kStream>(grid, block, sh.chunks, side_vec, st, row_bytes, topk, pt, d, num_dst_rows, sst, side_row_bytes, sd, stream);
+            break;
+        case 8: launch_dispatch_v<8, kStream>(grid, block, sh.chunks, side_vec, st, row_bytes, topk, pt, d, num_dst_rows, sst, side_row_bytes, sd, stream); break;
+        case 4: launch_dispatch_v<4, kStream>(grid, block, sh.chunks, side_vec, st, row_bytes, topk, pt, d, num_dst_rows, sst, side_row_bytes, sd, stream); break;
+        case 2: launch_dispatch_v<2, kStream>(grid, block, sh.chunks, side_vec, st, row_bytes, topk, pt, d, num_dst_rows, sst, side_row_bytes, sd, stream); break;
+        default: launch_dispatch_v<1, kStream>(grid, block, sh.chunks, side_vec, st, row_bytes, topk, pt, d, num_dst_rows, sst, side_row_bytes, sd, stream); break;
         }
     });
 }
