@@ -37,26 +37,21 @@ constexpr int kGroupsPerWave = kWave / kThreadsPerGroup;          // 8
 constexpr int kQuantThreads = 1024;
 
 
-// binary32 -> OCP e4m3fn by integer rounding of the significand: keep 3
-// fraction bits (normal range, exponent >= -6) or units of 2^-9 (subnormal
-// range), round to nearest even, saturate at 448 (0x7e); NaN -> 0x7f.
-__device__ __forceinline__ uint32_t e4m3_code(float f) {
-    const uint32_t u = __float_as_uint(f);
-    const uint32_t sign = (u >> 24) & 0x80u;
-    const uint32_t a = u & 0x7fffffffu;
-    if (a > 0x7f800000u) return 0x7fu;
-    if (a >= 0x43e00000u) return sign | 0x7eu;          // |f| >= 448
-    const int ex = (int)(a >> 23) - 127;
-    if (ex < -10) return sign;                          // below 2^-10: rounds to zero
-    const uint32_t full = (a & 0x7fffffu) | 0x800000u;
-    const int shift = ex >= -6 ? 20 : 14 - ex;          // 20..24
-    uint32_t q = full >> shift;
-    const uint32_t rem = full & ((1u << shift) - 1u);
-    const uint32_t half = 1u << (shift - 1);
-    if (rem > half || (rem == half && (q & 1u))) q += 1u;
-    if (ex < -6) return sign | q;                       // q == 8 is the smallest normal
-    const uint32_t code = ((uint32_t)(ex + 7) << 3) + (q - 8u);
-    return sign | (code > 0x7eu ? 0x7eu : code);
+// Four binary32 values -> four OCP e4m3fn codes (byte i = value i): round to
+// nearest even, saturate at 448 (0x7e with the sign), NaN -> 0x7f.  The
+// rounding is gfx950's v_cvt_pk_fp8_f32, which gives exactly these codes for
+// every finite |v| < 464 (checked against an integer encoder over all 2^32
+// inputs on MI355X); above that it returns NaN, and NaN keeps its sign.  So
+// each value is first clamped to [-448, 448] (values in (448, 464) round to
+// 448 anyway, larger ones saturate there), and NaN inputs get 0x7f after.
+__device__ __forceinline__ uint32_t e4m3_codes4(float v0, float v1, float v2, float v3) {
+    const float c0 = fminf(fmaxf(v0, -448.0f), 448.0f), c1 = fminf(fmaxf(v1, -448.0f), 448.0f);
+    const float c2 = fminf(fmaxf(v2, -448.0f), 448.0f), c3 = fminf(fmaxf(v3, -448.0f), 448.0f);
+    uint32_t c = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c0, c1, 0, false);
+    c = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c2, c3, (int)c, true);
+    const uint32_t nan = (v0 != v0 ? 0x000000ffu : 0u) | (v1 != v1 ? 0x0000ff00u : 0u) |
+                         (v2 != v2 ? 0x00ff0000u : 0u) | (v3 != v3 ? 0xff000000u : 0u);
+    return (c & ~nan) | (0x7f7f7f7fu & nan);
 }
 
 // Token t, elements [(chunk * blockDim.x + tid) * 16, +16).
@@ -92,9 +87,8 @@ __global__ __launch_bounds__(kQuantThreads) void dispatch_quant_fp8_kernel(
     u32x4 codes;
 #pragma unroll
     for (int w = 0; w < 4; ++w)
-        codes[w] = e4m3_code(x[4 * w] / scale) | (e4m3_code(x[4 * w + 1] / scale) << 8) |
-                   (e4m3_code(x[4 * w + 2] / scale) << 16) |
-                   (e4m3_code(x[4 * w + 3] / scale) << 24);
+        codes[w] = e4m3_codes4(x[4 * w] / scale, x[4 * w + 1] / scale, x[4 * w + 2] / scale,
+                               x[4 * w + 3] / scale);
     // Lanes 0..7 take the scales of this wave's 8 groups, in group order.
     const float wave_scale = __shfl(scale, (lane & (kGroupsPerWave - 1)) * kThreadsPerGroup, kWave);
     const int64_t groups = hidden / kGroupElems;
