@@ -86,6 +86,21 @@ MUTANTS = {
         "q[t * H + g * block + e] = f32_to_e4m3(bf16_to_f32(xs[e]) * (1.0f / scale));"),
     "padding_zeroes_rows_of_token0": ("if (input_perm[r] < 0) memset(",
                                       "if (input_perm[r] <= 0) memset("),
+    "sort_tiles_round_down": ("first[g + 1] = first[g] + (count[g] + tile - 1) / tile * tile;",
+                              "first[g + 1] = first[g] + count[g] / tile * tile;"),
+    "sort_unused_tiles_group_zero": (
+        "for (int64_t q = 0; q < max_tiles; ++q) { tile_group[q] = -1; tile_limit[q] = -1; }",
+        "for (int64_t q = 0; q < max_tiles; ++q) { tile_group[q] = 0; tile_limit[q] = -1; }"),
+    "sort_first_tile_skipped": ("for (int64_t q = first[g] / tile; q < first[g + 1] / tile; ++q) {",
+                                "for (int64_t q = first[g] / tile + 1; q < first[g + 1] / tile; ++q) {"),
+    "sort_group_is_expert_id": ("tile_group[q] = g;", "tile_group[q] = g + local_offset;"),
+    "sort_unstable_within_group": ("int64_t r = next[g]++;",
+                                   "int64_t r = first[g] + count[g] - 1 - (next[g]++ - first[g]);"),
+    "memset_ignores_pick_0": ("for (int32_t j = 0; j < k; ++j)\n            if (expanded_to_permuted",
+                              "for (int32_t j = 1; j < k; ++j)\n            if (expanded_to_permuted"),
+    "padding_zeroes_valid_rows": ("if (input_perm[r] < 0) memset(", "if (input_perm[r] >= 0) memset("),
+    "fp8_zero_group_scale_zero": ("float scale = amax > 0.0f ? amax / 448.0f : 1.0f;",
+                                  "float scale = amax > 0.0f ? amax / 448.0f : 0.0f;"),
     "padding_ignores_total": ("int64_t limit = expert_offsets ? expert_offsets[E] : n_rows;",
                               "int64_t limit = n_rows;"),
 }
