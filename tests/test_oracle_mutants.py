@@ -46,6 +46,24 @@ MUTANTS = {
     "f16_bias_off_by_one": ("(((ex + 15) << 10)", "(((ex + 14) << 10)"),
     "f16_widen_bias": ("v = ldexpf((float)(1024 + fr), ex - 25);",
                        "v = ldexpf((float)(1024 + fr), ex - 24);"),
+    "problem_sizes2_swaps_n_k": ("ps2[3 * e + 1] = g2_n; ps2[3 * e + 2] = g2_k;",
+                                 "ps2[3 * e + 1] = g2_k; ps2[3 * e + 2] = g2_n;"),
+    "problem_sizes1_takes_gemm2": ("ps1[3 * e + 1] = g1_n; ps1[3 * e + 2] = g1_k;",
+                                   "ps1[3 * e + 1] = g2_n; ps1[3 * e + 2] = g2_k;"),
+    "unused_rows_zero": ("for (int64_t r = 0; r < r_max; ++r) input_perm[r] = -1;",
+                         "for (int64_t r = 0; r < r_max; ++r) input_perm[r] = 0;"),
+    "ids_shifted_by_one": (
+        "        int64_t e = read_id(ids, id_bytes, i);\n        if (e >= 0 && e < E) count[e] += 1;",
+        "        int64_t e = read_id(ids, id_bytes, i) - 1;\n        if (e >= 0 && e < E) count[e] += 1;"),
+    "f16_widen_drops_sign": ("    return sign ? -v : v;\n}", "    return sign > 1 ? -v : v;\n}"),
+    "f16_widen_subnormal_scale": ("v = ldexpf((float)fr, -24);", "v = ldexpf((float)fr, -25);"),
+    "f16_widen_inf_as_nan": ("v = fr ? NAN : INFINITY;", "v = NAN;"),
+    "weights_read_as_y_dtype": ("float w = factors ? load_elem(factors, f_dtype, t * k + j) : 1.0f;",
+                                "float w = factors ? load_elem(factors, y_dtype, t * k + j) : 1.0f;"),
+    "absent_weights_zero": ("float w = factors ? load_elem(factors, f_dtype, t * k + j) : 1.0f;",
+                            "float w = factors ? load_elem(factors, f_dtype, t * k + j) : 0.0f;"),
+    "f16_output_rounded_as_bf16": ("    case OR_F16: ((uint16_t*)base)[idx] = f32_to_f16(v); break;",
+                                   "    case OR_F16: ((uint16_t*)base)[idx] = f32_to_bf16(v); break;"),
     "shuffle_accepts_last_plus_one": ("if (s < 0 || s >= n_src) continue;",
                                       "if (s < 0 || s > n_src) continue;"),
     "invalid_id_kept_as_expert0": ("output_perm[i] = -1;\n",
