@@ -9,11 +9,12 @@ seeded synthetic routing and activations, resident in HBM before timing.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 Prints one JSON line: tokens/s over the K timed steps (wall clock between
-two device synchronisations), per-stage times from HIP events recorded on
-the launch stream around each stage in a second pass of K steps, the
-dominant kernel's achieved algorithmic HBM bandwidth against MI355X's
-8 TB/s, and the CPU oracle timed on a bounded sample of the same workload on
-the host.
+two device synchronisations); from a second pass of K steps, per-stage times
+from HIP events recorded on the launch stream around each stage, and the
+dispatch and combine kernels' own durations from HIP events recorded with
+the kernels' begin and end timestamps; the dominant kernel's achieved
+algorithmic HBM bandwidth against MI355X's 8 TB/s; and the CPU oracle timed
+on a bounded sample of the same workload on the host.
 
 --graph captures one step's launches in a HIP graph and times K replays of
 it, so the headline holds no host launch cost (the per-stage event pass stays
@@ -195,11 +196,13 @@ def main():
                              r["blockscale_offsets"], row_align=w.row_align,
                              workspace=r["workspace"])
 
-    def dispatch():
-        mx.dispatch_rows(x, r["output_permutation"], k, xd, scales, sd)
+    def dispatch(kernel_events=None):
+        mx.dispatch_rows(x, r["output_permutation"], k, xd, scales, sd,
+                         kernel_events=kernel_events)
 
-    def combine():
-        mx.apply_shuffle_mul_sum(y, out, r["output_permutation"], weights)
+    def combine(kernel_events=None):
+        mx.apply_shuffle_mul_sum(y, out, r["output_permutation"], weights,
+                                 kernel_events=kernel_events)
 
     def zero_padding():
         mx.zero_padding_rows(xd, r["input_permutation"], r["expert_offsets"])
@@ -272,18 +275,34 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    # Per-kernel durations: a second pass of K steps with HIP events recorded
-    # on the launch stream around every stage (kept out of the headline pass,
-    # since each event record adds a few microseconds between kernels).
+    # Per-stage and per-kernel durations: a second pass of K steps (kept out of
+    # the headline pass, since each event record adds a few microseconds
+    # between kernels).  HIP events are recorded on the launch stream around
+    # every stage; dispatch and combine also record a pair of events with
+    # their kernels' own begin and end timestamps (the timed entry points).
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
           for _ in range(K)]
+    kev = {name: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(K)] for name in ("dispatch", "combine")}
+    for pairs in kev.values():
+        for a, b in pairs:                  # torch creates an event's HIP handle at its first record
+            a.record(stream)
+            b.record(stream)
     torch.cuda.synchronize()
     for s in range(K):
         ev[s][0].record(stream)
-        for i, (_, fn) in enumerate(stages):
-            fn()
+        for i, (name, fn) in enumerate(stages):
+            if name in kev:
+                fn(kernel_events=kev[name][s])
+            else:
+                fn()
             ev[s][i + 1].record(stream)
     torch.cuda.synchronize()
+    kernel_ms = {}
+    for name, pairs in kev.items():
+        ts = np.array([a.elapsed_time(b) for a, b in pairs])
+        kernel_ms[name] = {"mean": float(ts.mean()), "p50": float(np.percentile(ts, 50)),
+                           "p90": float(np.percentile(ts, 90)), "min": float(ts.min())}
 
     stage_ms = {}
     for i, (name, _) in enumerate(stages):
@@ -312,9 +331,9 @@ def main():
         gbps = nbytes[e] / (stage_ms[e]["mean"] * 1e-3) / 1e9
         extra_report[e] = {"ms": stage_ms[e]["mean"], "algorithmic_bytes": nbytes[e],
                            "achieved_gbps": gbps, "frac": gbps / HBM_PEAK_GBPS}
-    dom = max(("dispatch", "combine"), key=lambda n: stage_ms[n]["mean"])
+    dom = max(("dispatch", "combine"), key=lambda n: kernel_ms[n]["mean"])
     kernel_name = {"dispatch": "dispatch_rows_kernel", "combine": "combine_vec_kernel"}[dom]
-    achieved = nbytes[dom] / (stage_ms[dom]["mean"] * 1e-3) / 1e9
+    achieved = nbytes[dom] / (kernel_ms[dom]["mean"] * 1e-3) / 1e9
     traffic = load_traffic(w.name, kernel_name)
     step_bytes = sum(nbytes.values())
     ms_per_step = elapsed / K * 1e3
@@ -344,9 +363,13 @@ def main():
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic["traffic_bytes"] if traffic else None,
                      "traffic_detail": traffic, "bytes_per_launch": nbytes[dom],
-                     "avg_launch_ms": stage_ms[dom]["mean"]},
+                     "avg_launch_ms": kernel_ms[dom]["mean"],
+                     "avg_launch_ms_source": "HIP events recorded with the kernel's own begin "
+                                             "and end timestamps (hipExtLaunchKernel)",
+                     "avg_stage_ms_events_between_launches": stage_ms[dom]["mean"]},
         "cpu_baseline": cpu,
         "stages_ms": stage_ms,
+        "kernels_ms": kernel_ms,
         "extras": extra_report or None,
         "algorithmic_bytes": nbytes,
         "step_hbm_gbps": step_bytes / (ms_per_step * 1e-3) / 1e9,

@@ -41,6 +41,7 @@ EXPORTED_SYMBOLS = (
     "mx_prepare_workspace_size", "mx_prepare_moe_input", "mx_shuffle_rows",
     "mx_dispatch_rows", "mx_apply_shuffle_mul_sum", "mx_moe_output_memset",
     "mx_zero_padding_rows", "mx_moe_sort", "mx_dispatch_rows_fp8",
+    "mx_dispatch_rows_timed", "mx_apply_shuffle_mul_sum_timed",
 )
 
 
@@ -89,6 +90,11 @@ def load_library():
     lib.mx_dispatch_rows.argtypes = [vp, i64, i32, i64, vp, vp, i64, vp, i64, vp, vp]
     lib.mx_apply_shuffle_mul_sum.restype = ctypes.c_int
     lib.mx_apply_shuffle_mul_sum.argtypes = [vp, i32, i64, i64, vp, vp, i32, i64, i32, vp, i32, vp]
+    lib.mx_dispatch_rows_timed.restype = ctypes.c_int
+    lib.mx_dispatch_rows_timed.argtypes = [vp, i64, i32, i64, vp, vp, i64, vp, i64, vp, vp, vp, vp]
+    lib.mx_apply_shuffle_mul_sum_timed.restype = ctypes.c_int
+    lib.mx_apply_shuffle_mul_sum_timed.argtypes = [vp, i32, i64, i64, vp, vp, i32, i64, i32, vp,
+                                                   i32, vp, vp, vp]
     lib.mx_moe_output_memset.restype = ctypes.c_int
     lib.mx_moe_output_memset.argtypes = [vp, i64, i32, i64, vp, vp]
     lib.mx_zero_padding_rows.restype = ctypes.c_int
@@ -156,6 +162,23 @@ def _on(device: torch.device, fn, *args):
 def _call(status: int, what: str):
     if status != 0:
         raise MxError(status, what)
+
+
+def _event_handles(kernel_events):
+    """Raw hipEvent_t handles of a (start, stop) pair of torch.cuda.Event
+    (created with enable_timing=True), for the timed entry points.  torch
+    creates an event's HIP handle at its first record, so each event must have
+    been recorded once before."""
+    start, stop = kernel_events
+    hs = []
+    for e in (start, stop):
+        if not isinstance(e, torch.cuda.Event):
+            raise TypeError("kernel_events must be two torch.cuda.Event")
+        if not e.cuda_event:
+            raise ValueError("record each kernel event once before passing it (torch creates "
+                             "the HIP event at its first record)")
+        hs.append(e.cuda_event)
+    return hs
 
 
 def dispatch_capacity(num_tokens: int, topk: int, num_experts: int, row_align: int = 1) -> int:
@@ -260,10 +283,14 @@ def shuffle_rows(input: torch.Tensor, dst2src_map: torch.Tensor,
 
 def dispatch_rows(input: torch.Tensor, output_permutation: torch.Tensor, topk: int,
                   output: torch.Tensor, side_input: torch.Tensor | None = None,
-                  side_output: torch.Tensor | None = None) -> torch.Tensor:
+                  side_output: torch.Tensor | None = None,
+                  kernel_events=None) -> torch.Tensor:
     """output[output_permutation[t*topk + j]] = input[t] for every token t and
     pick j (destinations out of range are skipped); optionally the same for
-    a side row per token (e.g. FP8 block scales)."""
+    a side row per token (e.g. FP8 block scales).
+
+    kernel_events: optional (start, stop) torch.cuda.Event pair, recorded with
+    the begin and end of the dispatch kernels themselves (mx_dispatch_rows_timed)."""
     lib = load_library()
     _check_dev("input", input)
     dev = input.device
@@ -284,16 +311,25 @@ def dispatch_rows(input: torch.Tensor, output_permutation: torch.Tensor, topk: i
         side_rb = _row_bytes(side_input)
     T = input.shape[0]
     if T and output.shape[0]:
-        _call(_on(dev, lib.mx_dispatch_rows, _ptr(input), T, topk, _row_bytes(input),
-                  _ptr(output_permutation), _ptr(output), output.shape[0],
-                  _ptr(side_input), side_rb, _ptr(side_output)), "dispatch_rows")
+        args = (_ptr(input), T, topk, _row_bytes(input), _ptr(output_permutation), _ptr(output),
+                output.shape[0], _ptr(side_input), side_rb, _ptr(side_output))
+        if kernel_events is None:
+            _call(_on(dev, lib.mx_dispatch_rows, *args), "dispatch_rows")
+        else:
+            _call(_on(dev, lib.mx_dispatch_rows_timed, *args, *_event_handles(kernel_events)),
+                  "dispatch_rows")
     return output
 
 
 def apply_shuffle_mul_sum(input: torch.Tensor, output: torch.Tensor,
-                          permutation: torch.Tensor, factors: torch.Tensor | None = None) -> None:
+                          permutation: torch.Tensor, factors: torch.Tensor | None = None,
+                          kernel_events=None) -> None:
     """output[t] = round(sum_j factors[t, j] * input[permutation[t*k + j]]) with
-    fp32 accumulation (k = permutation.numel() // output.shape[0]); in place."""
+    fp32 accumulation (k = permutation.numel() // output.shape[0]); in place.
+
+    kernel_events: optional (start, stop) torch.cuda.Event pair, recorded with
+    the begin and end of the combine kernels themselves
+    (mx_apply_shuffle_mul_sum_timed)."""
     lib = load_library()
     _check_dev("input", input)
     dev = input.device
@@ -316,11 +352,13 @@ def apply_shuffle_mul_sum(input: torch.Tensor, output: torch.Tensor,
         if factors.dtype not in _FLOAT_CODES or factors.numel() != T * topk:
             raise ValueError("factors must be [tokens, topk] float32 / float16 / bfloat16")
         fcode = _FLOAT_CODES[factors.dtype]
-    _call(_on(
-        dev, lib.mx_apply_shuffle_mul_sum,
-        _ptr(input), _FLOAT_CODES[input.dtype], input.shape[0], H, _ptr(permutation),
-        _ptr(factors), fcode, T, topk, _ptr(output), _FLOAT_CODES[output.dtype]),
-        "apply_shuffle_mul_sum")
+    args = (_ptr(input), _FLOAT_CODES[input.dtype], input.shape[0], H, _ptr(permutation),
+            _ptr(factors), fcode, T, topk, _ptr(output), _FLOAT_CODES[output.dtype])
+    if kernel_events is None:
+        _call(_on(dev, lib.mx_apply_shuffle_mul_sum, *args), "apply_shuffle_mul_sum")
+    else:
+        _call(_on(dev, lib.mx_apply_shuffle_mul_sum_timed, *args,
+                  *_event_handles(kernel_events)), "apply_shuffle_mul_sum")
 
 
 def moe_output_memset(output: torch.Tensor, output_permutation: torch.Tensor, topk: int) -> None:

@@ -33,6 +33,60 @@ int elem_bytes(int32_t dt) {
 
 }  // namespace
 
+namespace {
+
+// The row dispatch and the combine with optional start / stop events (null
+// for the plain entry points).
+mx_status dispatch_rows(const void* src, int64_t num_tokens, int32_t topk, int64_t row_bytes,
+                        const int32_t* output_permutation, void* dst, int64_t num_dst_rows,
+                        const void* side_src, int64_t side_row_bytes, void* side_dst,
+                        void* start_event, void* stop_event, void* stream) {
+    if (num_tokens < 0 || topk < 1 || row_bytes < 1 || row_bytes > kMaxRowBytes ||
+        num_dst_rows < 0 || num_dst_rows > kMax31 || num_tokens > kMax31 / topk)
+        return MX_ERR_INVALID_ARGUMENT;
+    const bool side = side_src != nullptr || side_dst != nullptr;
+    if (side && (side_src == nullptr || side_dst == nullptr || side_row_bytes < 1))
+        return MX_ERR_INVALID_ARGUMENT;
+    if (!side && side_row_bytes != 0) return MX_ERR_INVALID_ARGUMENT;
+    if (num_tokens > 0 && (src == nullptr || output_permutation == nullptr ||
+                           (num_dst_rows > 0 && dst == nullptr)))
+        return MX_ERR_INVALID_ARGUMENT;
+    if (!aligned(output_permutation, 4)) return MX_ERR_MISALIGNED;
+    if (num_tokens == 0 || num_dst_rows == 0) return MX_OK;
+    return hip_status(mxmoe::launch_dispatch_rows(
+        src, num_tokens, topk, row_bytes, output_permutation, dst, num_dst_rows,
+        side ? side_src : nullptr, side ? side_row_bytes : 0, side ? side_dst : nullptr,
+        static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(start_event),
+        static_cast<hipEvent_t>(stop_event)));
+}
+
+mx_status apply_shuffle_mul_sum(const void* y, int32_t y_dtype, int64_t num_y_rows,
+                                int64_t hidden, const int32_t* permutation,
+                                const void* factors, int32_t factors_dtype,
+                                int64_t num_tokens, int32_t topk, void* out, int32_t out_dtype,
+                                void* start_event, void* stop_event, void* stream) {
+    const int yb = elem_bytes(y_dtype), ob = elem_bytes(out_dtype);
+    if (yb == 0 || ob == 0) return MX_ERR_UNSUPPORTED_DTYPE;
+    if (factors != nullptr && elem_bytes(factors_dtype) == 0) return MX_ERR_UNSUPPORTED_DTYPE;
+    if (num_y_rows < 0 || num_y_rows > kMax31 || hidden < 0 || num_tokens < 0 || topk < 1 ||
+        num_tokens > kMax31 / topk || hidden > (int64_t)65535 * 1024 * 8)
+        return MX_ERR_INVALID_ARGUMENT;
+    if (num_tokens > 0 && hidden > 0 &&
+        (out == nullptr || permutation == nullptr || (num_y_rows > 0 && y == nullptr)))
+        return MX_ERR_INVALID_ARGUMENT;
+    if (!aligned(y, (size_t)yb) || !aligned(out, (size_t)ob) || !aligned(permutation, 4) ||
+        (factors != nullptr && !aligned(factors, (size_t)elem_bytes(factors_dtype))))
+        return MX_ERR_MISALIGNED;
+    if (num_tokens == 0 || hidden == 0) return MX_OK;
+    return hip_status(mxmoe::launch_combine(y, y_dtype, num_y_rows, hidden, permutation, factors,
+                                            factors_dtype, num_tokens, topk, out, out_dtype,
+                                            static_cast<hipStream_t>(stream),
+                                            static_cast<hipEvent_t>(start_event),
+                                            static_cast<hipEvent_t>(stop_event)));
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* mx_status_string(mx_status s) {
@@ -140,26 +194,22 @@ mx_status mx_shuffle_rows(const void* src, int64_t num_src_rows, int64_t row_byt
                                                  static_cast<hipStream_t>(stream)));
 }
 
+
 mx_status mx_dispatch_rows(const void* src, int64_t num_tokens, int32_t topk, int64_t row_bytes,
                            const int32_t* output_permutation, void* dst, int64_t num_dst_rows,
                            const void* side_src, int64_t side_row_bytes, void* side_dst,
                            void* stream) {
-    if (num_tokens < 0 || topk < 1 || row_bytes < 1 || row_bytes > kMaxRowBytes ||
-        num_dst_rows < 0 || num_dst_rows > kMax31 || num_tokens > kMax31 / topk)
-        return MX_ERR_INVALID_ARGUMENT;
-    const bool side = side_src != nullptr || side_dst != nullptr;
-    if (side && (side_src == nullptr || side_dst == nullptr || side_row_bytes < 1))
-        return MX_ERR_INVALID_ARGUMENT;
-    if (!side && side_row_bytes != 0) return MX_ERR_INVALID_ARGUMENT;
-    if (num_tokens > 0 && (src == nullptr || output_permutation == nullptr ||
-                           (num_dst_rows > 0 && dst == nullptr)))
-        return MX_ERR_INVALID_ARGUMENT;
-    if (!aligned(output_permutation, 4)) return MX_ERR_MISALIGNED;
-    if (num_tokens == 0 || num_dst_rows == 0) return MX_OK;
-    return hip_status(mxmoe::launch_dispatch_rows(
-        src, num_tokens, topk, row_bytes, output_permutation, dst, num_dst_rows,
-        side ? side_src : nullptr, side ? side_row_bytes : 0, side ? side_dst : nullptr,
-        static_cast<hipStream_t>(stream)));
+    return dispatch_rows(src, num_tokens, topk, row_bytes, output_permutation, dst, num_dst_rows,
+                         side_src, side_row_bytes, side_dst, nullptr, nullptr, stream);
+}
+
+mx_status mx_dispatch_rows_timed(const void* src, int64_t num_tokens, int32_t topk,
+                                 int64_t row_bytes, const int32_t* output_permutation, void* dst,
+                                 int64_t num_dst_rows, const void* side_src,
+                                 int64_t side_row_bytes, void* side_dst, void* start_event,
+                                 void* stop_event, void* stream) {
+    return dispatch_rows(src, num_tokens, topk, row_bytes, output_permutation, dst, num_dst_rows,
+                         side_src, side_row_bytes, side_dst, start_event, stop_event, stream);
 }
 
 mx_status mx_apply_shuffle_mul_sum(const void* y, int32_t y_dtype, int64_t num_y_rows,
@@ -167,22 +217,20 @@ mx_status mx_apply_shuffle_mul_sum(const void* y, int32_t y_dtype, int64_t num_y
                                    const void* factors, int32_t factors_dtype,
                                    int64_t num_tokens, int32_t topk,
                                    void* out, int32_t out_dtype, void* stream) {
-    const int yb = elem_bytes(y_dtype), ob = elem_bytes(out_dtype);
-    if (yb == 0 || ob == 0) return MX_ERR_UNSUPPORTED_DTYPE;
-    if (factors != nullptr && elem_bytes(factors_dtype) == 0) return MX_ERR_UNSUPPORTED_DTYPE;
-    if (num_y_rows < 0 || num_y_rows > kMax31 || hidden < 0 || num_tokens < 0 || topk < 1 ||
-        num_tokens > kMax31 / topk || hidden > (int64_t)65535 * 1024 * 8)
-        return MX_ERR_INVALID_ARGUMENT;
-    if (num_tokens > 0 && hidden > 0 &&
-        (out == nullptr || permutation == nullptr || (num_y_rows > 0 && y == nullptr)))
-        return MX_ERR_INVALID_ARGUMENT;
-    if (!aligned(y, (size_t)yb) || !aligned(out, (size_t)ob) || !aligned(permutation, 4) ||
-        (factors != nullptr && !aligned(factors, (size_t)elem_bytes(factors_dtype))))
-        return MX_ERR_MISALIGNED;
-    if (num_tokens == 0 || hidden == 0) return MX_OK;
-    return hip_status(mxmoe::launch_combine(y, y_dtype, num_y_rows, hidden, permutation, factors,
-                                            factors_dtype, num_tokens, topk, out, out_dtype,
-                                            static_cast<hipStream_t>(stream)));
+    return apply_shuffle_mul_sum(y, y_dtype, num_y_rows, hidden, permutation, factors,
+                                 factors_dtype, num_tokens, topk, out, out_dtype, nullptr,
+                                 nullptr, stream);
+}
+
+mx_status mx_apply_shuffle_mul_sum_timed(const void* y, int32_t y_dtype, int64_t num_y_rows,
+                                         int64_t hidden, const int32_t* permutation,
+                                         const void* factors, int32_t factors_dtype,
+                                         int64_t num_tokens, int32_t topk, void* out,
+                                         int32_t out_dtype, void* start_event, void* stop_event,
+                                         void* stream) {
+    return apply_shuffle_mul_sum(y, y_dtype, num_y_rows, hidden, permutation, factors,
+                                 factors_dtype, num_tokens, topk, out, out_dtype, start_event,
+                                 stop_event, stream);
 }
 
 mx_status mx_moe_output_memset(void* out, int64_t num_tokens, int32_t topk, int64_t row_bytes,

@@ -199,46 +199,47 @@ __global__ __launch_bounds__(kCombineThreads) void combine_scalar_kernel(
 template <typename TY, typename TO, int FDT>
 hipError_t launch_typed(const void* y, int64_t num_y_rows, int64_t hidden, const int32_t* perm,
                         const void* factors, int64_t T, int32_t topk, void* out,
-                        hipStream_t stream) {
+                        hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
     using SY = typename TY::storage;
     using SO = typename TO::storage;
     const bool vec = hidden % kGroup == 0 && ((uintptr_t)y % 16) == 0 && ((uintptr_t)out % 16) == 0;
     const RowShape sh = row_shape(vec ? hidden / kGroup : hidden, kCombineThreads);
     const int64_t factor_bytes = FDT == 0 ? 4 : 2;
-    return for_row_batches(T, sh, [&](int64_t t0, int64_t, dim3 grid, dim3 block) {
+    return for_row_batches(T, sh, [&](int64_t t0, int64_t, dim3 grid, dim3 block,
+                                      hipEvent_t e0, hipEvent_t e1) {
         const int32_t* p = perm + t0 * topk;
         const void* f = factors ? static_cast<const char*>(factors) + t0 * topk * factor_bytes
                                 : nullptr;
         SO* o = static_cast<SO*>(out) + t0 * hidden;
         if (vec)
-            combine_vec_kernel<TY, TO, FDT><<<grid, block, 0, stream>>>(
-                static_cast<const SY*>(y), num_y_rows, hidden, p, f, topk, o, sh.chunks);
+            launch_kernel(combine_vec_kernel<TY, TO, FDT>, grid, block, stream, e0, e1,
+                          static_cast<const SY*>(y), num_y_rows, hidden, p, f, topk, o, sh.chunks);
         else
-            combine_scalar_kernel<TY, TO, FDT><<<grid, block, 0, stream>>>(
-                static_cast<const SY*>(y), num_y_rows, hidden, p, f, topk, o, sh.chunks);
-    });
+            launch_kernel(combine_scalar_kernel<TY, TO, FDT>, grid, block, stream, e0, e1,
+                          static_cast<const SY*>(y), num_y_rows, hidden, p, f, topk, o, sh.chunks);
+    }, start, stop);
 }
 
 template <typename TY, typename TO>
 hipError_t launch_factor(int fdt, const void* y, int64_t num_y_rows, int64_t hidden,
                          const int32_t* perm, const void* factors, int64_t T, int32_t topk,
-                         void* out, hipStream_t stream) {
+                         void* out, hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
     switch (fdt) {
-    case -1: return launch_typed<TY, TO, -1>(y, num_y_rows, hidden, perm, factors, T, topk, out, stream);
-    case 0: return launch_typed<TY, TO, 0>(y, num_y_rows, hidden, perm, factors, T, topk, out, stream);
-    case 1: return launch_typed<TY, TO, 1>(y, num_y_rows, hidden, perm, factors, T, topk, out, stream);
-    default: return launch_typed<TY, TO, 2>(y, num_y_rows, hidden, perm, factors, T, topk, out, stream);
+    case -1: return launch_typed<TY, TO, -1>(y, num_y_rows, hidden, perm, factors, T, topk, out, stream, e0, e1);
+    case 0: return launch_typed<TY, TO, 0>(y, num_y_rows, hidden, perm, factors, T, topk, out, stream, e0, e1);
+    case 1: return launch_typed<TY, TO, 1>(y, num_y_rows, hidden, perm, factors, T, topk, out, stream, e0, e1);
+    default: return launch_typed<TY, TO, 2>(y, num_y_rows, hidden, perm, factors, T, topk, out, stream, e0, e1);
     }
 }
 
 template <typename TY>
 hipError_t launch_out(int out_dtype, const void* y, int64_t num_y_rows, int64_t hidden,
                       const int32_t* perm, const void* factors, int fdt, int64_t T,
-                      int32_t topk, void* out, hipStream_t stream) {
+                      int32_t topk, void* out, hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
     switch (out_dtype) {
-    case 0: return launch_factor<TY, F32>(fdt, y, num_y_rows, hidden, perm, factors, T, topk, out, stream);
-    case 1: return launch_factor<TY, F16>(fdt, y, num_y_rows, hidden, perm, factors, T, topk, out, stream);
-    default: return launch_factor<TY, BF16>(fdt, y, num_y_rows, hidden, perm, factors, T, topk, out, stream);
+    case 0: return launch_factor<TY, F32>(fdt, y, num_y_rows, hidden, perm, factors, T, topk, out, stream, e0, e1);
+    case 1: return launch_factor<TY, F16>(fdt, y, num_y_rows, hidden, perm, factors, T, topk, out, stream, e0, e1);
+    default: return launch_factor<TY, BF16>(fdt, y, num_y_rows, hidden, perm, factors, T, topk, out, stream, e0, e1);
     }
 }
 
@@ -247,13 +248,14 @@ hipError_t launch_out(int out_dtype, const void* y, int64_t num_y_rows, int64_t 
 hipError_t launch_combine(const void* y, int y_dtype, int64_t num_y_rows, int64_t hidden,
                           const int32_t* perm, const void* factors, int factors_dtype,
                           int64_t num_tokens, int32_t topk, void* out, int out_dtype,
-                          hipStream_t stream) {
+                          hipStream_t stream, hipEvent_t start_event, hipEvent_t stop_event) {
     if (num_tokens == 0 || hidden == 0) return hipSuccess;
     const int fdt = factors ? factors_dtype : -1;
+    hipEvent_t e0 = start_event, e1 = stop_event;
     switch (y_dtype) {
-    case 0: return launch_out<F32>(out_dtype, y, num_y_rows, hidden, perm, factors, fdt, num_tokens, topk, out, stream);
-    case 1: return launch_out<F16>(out_dtype, y, num_y_rows, hidden, perm, factors, fdt, num_tokens, topk, out, stream);
-    default: return launch_out<BF16>(out_dtype, y, num_y_rows, hidden, perm, factors, fdt, num_tokens, topk, out, stream);
+    case 0: return launch_out<F32>(out_dtype, y, num_y_rows, hidden, perm, factors, fdt, num_tokens, topk, out, stream, e0, e1);
+    case 1: return launch_out<F16>(out_dtype, y, num_y_rows, hidden, perm, factors, fdt, num_tokens, topk, out, stream, e0, e1);
+    default: return launch_out<BF16>(out_dtype, y, num_y_rows, hidden, perm, factors, fdt, num_tokens, topk, out, stream, e0, e1);
     }
 }
 

@@ -1,6 +1,7 @@
 // Device-side helpers shared by the mxmoe HIP kernels (gfx950, wave64).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -34,13 +35,31 @@ inline RowShape row_shape(int64_t items, int64_t max_threads) {
     return s;
 }
 
-// Launches launch(row0, rows, grid, block) for consecutive batches of rows,
-// stopping at the first launch error.
+// Launches kernel<<<grid, block, 0, stream>>>(args...).  With a start or a
+// stop event it goes through hipExtLaunchKernelGGL, which records the events
+// with the kernel dispatch's own begin and end timestamps: the elapsed time
+// between them is the kernel's execution, without the launch gap an event
+// record queued on the stream adds.
+template <typename... KArgs, typename... Args>
+inline void launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t stream,
+                          hipEvent_t start, hipEvent_t stop, Args... args) {
+    if (start != nullptr || stop != nullptr)
+        hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, start, stop, 0u,
+                              static_cast<KArgs>(args)...);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, 0, stream, static_cast<KArgs>(args)...);
+}
+
+// Launches launch(row0, rows, grid, block, ev_start, ev_stop) for consecutive
+// batches of rows, stopping at the first launch error.  `start` goes with the
+// first launch and `stop` with the last (both may be null).
 template <typename F>
-hipError_t for_row_batches(int64_t rows, const RowShape& s, F&& launch) {
+hipError_t for_row_batches(int64_t rows, const RowShape& s, F&& launch,
+                           hipEvent_t start = nullptr, hipEvent_t stop = nullptr) {
     for (int64_t r0 = 0; r0 < rows; r0 += s.rows_per_launch) {
         const int64_t n = rows - r0 < s.rows_per_launch ? rows - r0 : s.rows_per_launch;
-        launch(r0, n, dim3((unsigned)(n * s.chunks), 1, 1), dim3((unsigned)s.threads, 1, 1));
+        launch(r0, n, dim3((unsigned)(n * s.chunks), 1, 1), dim3((unsigned)s.threads, 1, 1),
+               r0 == 0 ? start : nullptr, r0 + n >= rows ? stop : nullptr);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -42,17 +42,20 @@ hipError_t launch_shuffle_rows(const void* src, int64_t num_src_rows, int64_t ro
                                const int32_t* dst2src, int64_t num_dst_rows, void* dst,
                                hipStream_t stream);
 
+// start_event / stop_event (either may be null) are recorded with the begin
+// of the call's first kernel and the end of its last one.
 hipError_t launch_dispatch_rows(const void* src, int64_t num_tokens, int32_t topk,
                                 int64_t row_bytes, const int32_t* output_perm, void* dst,
                                 int64_t num_dst_rows, const void* side_src,
-                                int64_t side_row_bytes, void* side_dst, hipStream_t stream);
+                                int64_t side_row_bytes, void* side_dst, hipStream_t stream,
+                                hipEvent_t start_event, hipEvent_t stop_event);
 
 // dtype codes as in mxmoe.h (MX_F32 = 0, MX_F16 = 1, MX_BF16 = 2); factors_dtype
 // is ignored when factors is null.
 hipError_t launch_combine(const void* y, int y_dtype, int64_t num_y_rows, int64_t hidden,
                           const int32_t* perm, const void* factors, int factors_dtype,
                           int64_t num_tokens, int32_t topk, void* out, int out_dtype,
-                          hipStream_t stream);
+                          hipStream_t stream, hipEvent_t start_event, hipEvent_t stop_event);
 
 hipError_t launch_zero_padding(void* rows, int64_t num_rows, int64_t row_bytes,
                                const int32_t* input_perm, const int32_t* expert_offsets,

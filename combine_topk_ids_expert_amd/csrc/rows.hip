@@ -122,12 +122,12 @@ template <int V, int P>
 void launch_dispatch_v(dim3 grid, dim3 block, int32_t chunks, int side_vec, const uint8_t* s,
                        int64_t row_bytes, int32_t topk, const int32_t* output_perm, uint8_t* d,
                        int64_t num_dst_rows, const uint8_t* ss, int64_t side_row_bytes,
-                       uint8_t* sd, hipStream_t stream) {
+                       uint8_t* sd, hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
     switch (side_vec) {
-    case 0: dispatch_rows_kernel<V, 0, P><<<grid, block, 0, stream>>>(s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd, chunks); break;
-    case 16: dispatch_rows_kernel<V, 16, P><<<grid, block, 0, stream>>>(s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd, chunks); break;
-    case 4: dispatch_rows_kernel<V, 4, P><<<grid, block, 0, stream>>>(s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd, chunks); break;
-    default: dispatch_rows_kernel<V, 1, P><<<grid, block, 0, stream>>>(s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd, chunks); break;
+    case 0: launch_kernel(dispatch_rows_kernel<V, 0, P>, grid, block, stream, e0, e1, s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd, chunks); break;
+    case 16: launch_kernel(dispatch_rows_kernel<V, 16, P>, grid, block, stream, e0, e1, s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd, chunks); break;
+    case 4: launch_kernel(dispatch_rows_kernel<V, 4, P>, grid, block, stream, e0, e1, s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd, chunks); break;
+    default: launch_kernel(dispatch_rows_kernel<V, 1, P>, grid, block, stream, e0, e1, s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd, chunks); break;
     }
 }
 
@@ -141,15 +141,16 @@ hipError_t launch_shuffle_rows(const void* src, int64_t num_src_rows, int64_t ro
     const RowShape sh = row_shape(row_bytes / v, kRowThreads);
     const uint8_t* s = static_cast<const uint8_t*>(src);
     uint8_t* d = static_cast<uint8_t*>(dst);
-    return for_row_batches(num_dst_rows, sh, [&](int64_t r0, int64_t, dim3 grid, dim3 block) {
+    return for_row_batches(num_dst_rows, sh, [&](int64_t r0, int64_t, dim3 grid, dim3 block,
+                                                 hipEvent_t e0, hipEvent_t e1) {
         const int32_t* m = dst2src + r0;
         uint8_t* dr = d + r0 * row_bytes;
         switch (v) {
-        case 16: shuffle_rows_kernel<16><<<grid, block, 0, stream>>>(s, num_src_rows, row_bytes, m, dr, sh.chunks); break;
-        case 8: shuffle_rows_kernel<8><<<grid, block, 0, stream>>>(s, num_src_rows, row_bytes, m, dr, sh.chunks); break;
-        case 4: shuffle_rows_kernel<4><<<grid, block, 0, stream>>>(s, num_src_rows, row_bytes, m, dr, sh.chunks); break;
-        case 2: shuffle_rows_kernel<2><<<grid, block, 0, stream>>>(s, num_src_rows, row_bytes, m, dr, sh.chunks); break;
-        default: shuffle_rows_kernel<1><<<grid, block, 0, stream>>>(s, num_src_rows, row_bytes, m, dr, sh.chunks); break;
+        case 16: launch_kernel(shuffle_rows_kernel<16>, grid, block, stream, e0, e1, s, num_src_rows, row_bytes, m, dr, sh.chunks); break;
+        case 8: launch_kernel(shuffle_rows_kernel<8>, grid, block, stream, e0, e1, s, num_src_rows, row_bytes, m, dr, sh.chunks); break;
+        case 4: launch_kernel(shuffle_rows_kernel<4>, grid, block, stream, e0, e1, s, num_src_rows, row_bytes, m, dr, sh.chunks); break;
+        case 2: launch_kernel(shuffle_rows_kernel<2>, grid, block, stream, e0, e1, s, num_src_rows, row_bytes, m, dr, sh.chunks); break;
+        default: launch_kernel(shuffle_rows_kernel<1>, grid, block, stream, e0, e1, s, num_src_rows, row_bytes, m, dr, sh.chunks); break;
         }
     });
 }
@@ -157,7 +158,8 @@ hipError_t launch_shuffle_rows(const void* src, int64_t num_src_rows, int64_t ro
 hipError_t launch_dispatch_rows(const void* src, int64_t num_tokens, int32_t topk,
                                 int64_t row_bytes, const int32_t* output_perm, void* dst,
                                 int64_t num_dst_rows, const void* side_src,
-                                int64_t side_row_bytes, void* side_dst, hipStream_t stream) {
+                                int64_t side_row_bytes, void* side_dst, hipStream_t stream,
+                                hipEvent_t start_event, hipEvent_t stop_event) {
     if (num_tokens == 0) return hipSuccess;
     const int v = vec_width(row_bytes, src, dst);
     int side_vec = 0;
@@ -171,21 +173,22 @@ hipError_t launch_dispatch_rows(const void* src, int64_t num_tokens, int32_t top
     uint8_t* d = static_cast<uint8_t*>(dst);
     const uint8_t* ss = static_cast<const uint8_t*>(side_src);
     uint8_t* sd = static_cast<uint8_t*>(side_dst);
-    return for_row_batches(num_tokens, sh, [&](int64_t t0, int64_t, dim3 grid, dim3 block) {
+    return for_row_batches(num_tokens, sh, [&](int64_t t0, int64_t, dim3 grid, dim3 block,
+                                               hipEvent_t e0, hipEvent_t e1) {
         const uint8_t* st = s + t0 * row_bytes;
         const int32_t* pt = output_perm + t0 * topk;
         const uint8_t* sst = ss ? ss + t0 * side_row_bytes : nullptr;
         switch (v) {
         case 16:
-            if (keep) launch_dispatch_v<16, kKeep>(grid, block, sh.chunks, side_vec, st, row_bytes, topk, pt, d, num_dst_rows, sst, side_row_bytes, sd, stream);
-            else launch_dispatch_v<16, kStream>(grid, block, sh.chunks, side_vec, st, row_bytes, topk, pt, d, num_dst_rows, sst, side_row_bytes, sd, stream);
+            if (keep) launch_dispatch_v<16, kKeep>(grid, block, sh.chunks, side_vec, st, row_bytes, topk, pt, d, num_dst_rows, sst, side_row_bytes, sd, stream, e0, e1);
+            else launch_dispatch_v<16, kStream>(grid, block, sh.chunks, side_vec, st, row_bytes, topk, pt, d, num_dst_rows, sst, side_row_bytes, sd, stream, e0, e1);
             break;
-        case 8: launch_dispatch_v<8, kStream>(grid, block, sh.chunks, side_vec, st, row_bytes, topk, pt, d, num_dst_rows, sst, side_row_bytes, sd, stream); break;
-        case 4: launch_dispatch_v<4, kStream>(grid, block, sh.chunks, side_vec, st, row_bytes, topk, pt, d, num_dst_rows, sst, side_row_bytes, sd, stream); break;
-        case 2: launch_dispatch_v<2, kStream>(grid, block, sh.chunks, side_vec, st, row_bytes, topk, pt, d, num_dst_rows, sst, side_row_bytes, sd, stream); break;
-        default: launch_dispatch_v<1, kStream>(grid, block, sh.chunks, side_vec, st, row_bytes, topk, pt, d, num_dst_rows, sst, side_row_bytes, sd, stream); break;
+        case 8: launch_dispatch_v<8, kStream>(grid, block, sh.chunks, side_vec, st, row_bytes, topk, pt, d, num_dst_rows, sst, side_row_bytes, sd, stream, e0, e1); break;
+        case 4: launch_dispatch_v<4, kStream>(grid, block, sh.chunks, side_vec, st, row_bytes, topk, pt, d, num_dst_rows, sst, side_row_bytes, sd, stream, e0, e1); break;
+        case 2: launch_dispatch_v<2, kStream>(grid, block, sh.chunks, side_vec, st, row_bytes, topk, pt, d, num_dst_rows, sst, side_row_bytes, sd, stream, e0, e1); break;
+        default: launch_dispatch_v<1, kStream>(grid, block, sh.chunks, side_vec, st, row_bytes, topk, pt, d, num_dst_rows, sst, side_row_bytes, sd, stream, e0, e1); break;
         }
-    });
+    }, start_event, stop_event);
 }
 
 }  // namespace mxmoe

@@ -131,15 +131,16 @@ hipError_t launch_zero_padding(void* rows, int64_t num_rows, int64_t row_bytes,
         return hipGetLastError();
     }
     const RowShape sh = row_shape(row_bytes / v, kZeroThreads);
-    return for_row_batches(num_rows, sh, [&](int64_t r0, int64_t, dim3 grid, dim3 block) {
+    return for_row_batches(num_rows, sh, [&](int64_t r0, int64_t, dim3 grid, dim3 block,
+                                             hipEvent_t e0, hipEvent_t e1) {
         uint8_t* pr = p + r0 * row_bytes;
         const int32_t* m = input_perm + r0;
         switch (v) {
-        case 16: zero_padding_kernel<16><<<grid, block, 0, stream>>>(pr, row_bytes, m, sh.chunks); break;
-        case 8: zero_padding_kernel<8><<<grid, block, 0, stream>>>(pr, row_bytes, m, sh.chunks); break;
-        case 4: zero_padding_kernel<4><<<grid, block, 0, stream>>>(pr, row_bytes, m, sh.chunks); break;
-        case 2: zero_padding_kernel<2><<<grid, block, 0, stream>>>(pr, row_bytes, m, sh.chunks); break;
-        default: zero_padding_kernel<1><<<grid, block, 0, stream>>>(pr, row_bytes, m, sh.chunks); break;
+        case 16: launch_kernel(zero_padding_kernel<16>, grid, block, stream, e0, e1, pr, row_bytes, m, sh.chunks); break;
+        case 8: launch_kernel(zero_padding_kernel<8>, grid, block, stream, e0, e1, pr, row_bytes, m, sh.chunks); break;
+        case 4: launch_kernel(zero_padding_kernel<4>, grid, block, stream, e0, e1, pr, row_bytes, m, sh.chunks); break;
+        case 2: launch_kernel(zero_padding_kernel<2>, grid, block, stream, e0, e1, pr, row_bytes, m, sh.chunks); break;
+        default: launch_kernel(zero_padding_kernel<1>, grid, block, stream, e0, e1, pr, row_bytes, m, sh.chunks); break;
         }
     });
 }
@@ -150,15 +151,16 @@ hipError_t launch_output_memset(void* out, int64_t num_tokens, int32_t topk, int
     const int v = zvec_width(row_bytes, out);
     const RowShape sh = row_shape(row_bytes / v, kZeroThreads);
     uint8_t* p = static_cast<uint8_t*>(out);
-    return for_row_batches(num_tokens, sh, [&](int64_t t0, int64_t, dim3 grid, dim3 block) {
+    return for_row_batches(num_tokens, sh, [&](int64_t t0, int64_t, dim3 grid, dim3 block,
+                                               hipEvent_t e0, hipEvent_t e1) {
         uint8_t* pt = p + t0 * row_bytes;
         const int32_t* e = expanded_to_permuted + t0 * topk;
         switch (v) {
-        case 16: output_memset_kernel<16><<<grid, block, 0, stream>>>(pt, row_bytes, topk, e, sh.chunks); break;
-        case 8: output_memset_kernel<8><<<grid, block, 0, stream>>>(pt, row_bytes, topk, e, sh.chunks); break;
-        case 4: output_memset_kernel<4><<<grid, block, 0, stream>>>(pt, row_bytes, topk, e, sh.chunks); break;
-        case 2: output_memset_kernel<2><<<grid, block, 0, stream>>>(pt, row_bytes, topk, e, sh.chunks); break;
-        default: output_memset_kernel<1><<<grid, block, 0, stream>>>(pt, row_bytes, topk, e, sh.chunks); break;
+        case 16: launch_kernel(output_memset_kernel<16>, grid, block, stream, e0, e1, pt, row_bytes, topk, e, sh.chunks); break;
+        case 8: launch_kernel(output_memset_kernel<8>, grid, block, stream, e0, e1, pt, row_bytes, topk, e, sh.chunks); break;
+        case 4: launch_kernel(output_memset_kernel<4>, grid, block, stream, e0, e1, pt, row_bytes, topk, e, sh.chunks); break;
+        case 2: launch_kernel(output_memset_kernel<2>, grid, block, stream, e0, e1, pt, row_bytes, topk, e, sh.chunks); break;
+        default: launch_kernel(output_memset_kernel<1>, grid, block, stream, e0, e1, pt, row_bytes, topk, e, sh.chunks); break;
         }
     });
 }

@@ -216,6 +216,39 @@ mx_status mx_apply_shuffle_mul_sum(const void* y, int32_t y_dtype, int64_t num_y
                                    void* out, int32_t out_dtype, void* stream);
 
 /*
+ * Timed forms of mx_dispatch_rows and mx_apply_shuffle_mul_sum, for
+ * measuring the two row kernels with the backend's own timing (the benchmark
+ * page "[RFC]: Comprehensive MoE / EP Kernel Benchmark Under Incast
+ * Traffic", section "Timing Method", puts backend-specific timing behind
+ * helpers).  Same arguments, checks, work and results as the plain calls,
+ * plus two events:
+ *
+ * start_event, stop_event   hipEvent_t handles created by the caller (for
+ *                           example with hipEventCreate), or NULL.  The call
+ *                           records start_event with the begin of its first
+ *                           kernel and stop_event with the end of its last,
+ *                           from the kernel dispatch's own timestamps
+ *                           (hipExtLaunchKernel), so hipEventElapsedTime
+ *                           between them is the kernels' execution time
+ *                           without the gap an event record queued on the
+ *                           stream between launches adds.  A call that
+ *                           launches nothing (no tokens, or no rows)
+ *                           records neither event.
+ */
+mx_status mx_dispatch_rows_timed(const void* src, int64_t num_tokens, int32_t topk,
+                                 int64_t row_bytes, const int32_t* output_permutation, void* dst,
+                                 int64_t num_dst_rows, const void* side_src,
+                                 int64_t side_row_bytes, void* side_dst, void* start_event,
+                                 void* stop_event, void* stream);
+
+mx_status mx_apply_shuffle_mul_sum_timed(const void* y, int32_t y_dtype, int64_t num_y_rows,
+                                         int64_t hidden, const int32_t* permutation,
+                                         const void* factors, int32_t factors_dtype,
+                                         int64_t num_tokens, int32_t topk, void* out,
+                                         int32_t out_dtype, void* start_event, void* stop_event,
+                                         void* stream);
+
+/*
  * moe_sort -- tile-padded sort metadata for one rank's window of experts
  * (the TensorRT-LLM page "Enable CuteDSL MoE with Large EP": the sort that
  * returns tile_idx_to_group_idx, tile_idx_to_mn_limit,

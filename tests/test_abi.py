@@ -110,6 +110,19 @@ def test_dispatch_rejects(lib):
     assert f(P, 0, 8, 16, P, P, 80, None, 0, None, S) == OK
 
 
+def test_timed_forms_check_like_the_plain_calls(lib):
+    d = lib.mx_dispatch_rows_timed
+    assert d(P, 10, 0, 16, P, P, 80, None, 0, None, None, None, S) == INVALID
+    assert d(P, 10, 8, 16, P + 1, P, 80, None, 0, None, None, None, S) == MISALIGNED
+    assert d(P, 10, 8, 16, P, P, 80, P, 16, None, None, None, S) == INVALID
+    assert d(P, 0, 8, 16, P, P, 80, None, 0, None, P, P, S) == OK        # nothing launched
+    c = lib.mx_apply_shuffle_mul_sum_timed
+    assert c(P, I32, 10, 8, P, None, 0, 4, 2, P, BF16, None, None, S) == DTYPE
+    assert c(P, BF16, 10, 8, P, None, 0, 4, 0, P, BF16, None, None, S) == INVALID
+    assert c(P + 1, BF16, 10, 8, P, None, 0, 4, 2, P, BF16, None, None, S) == MISALIGNED
+    assert c(P, BF16, 10, 8, P, None, 0, 0, 2, P, BF16, P, P, S) == OK   # nothing launched
+
+
 def test_combine_rejects(lib):
     f = lib.mx_apply_shuffle_mul_sum
     assert f(P, I32, 10, 8, P, None, 0, 4, 2, P, BF16, S) == DTYPE

@@ -68,8 +68,12 @@ def test_dispatch_rows_over_launches():
     x = torch.randint(-2**31, 2**31 - 1, (N, 4), dtype=torch.int32, device=DEV, generator=g)
     perm = torch.randperm(N, device=DEV, generator=g).to(torch.int32)
     xd = torch.zeros((N, 4), dtype=torch.int32, device=DEV)
-    mx.dispatch_rows(x, perm, 1, xd)
+    ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    for e in ev:
+        e.record()
+    mx.dispatch_rows(x, perm, 1, xd, kernel_events=ev)    # start with the first launch, stop with the last
     torch.cuda.synchronize()
+    assert ev[0].elapsed_time(ev[1]) > 0.0
     s = _sample(N, 2)                                  # tokens
     p_s = gu.bits(perm)[s]
     inv = np.argsort(p_s)                              # sampled destination rows, in row order

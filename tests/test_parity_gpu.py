@@ -350,6 +350,47 @@ def test_workload_full_size_sampled(name):
     np.testing.assert_array_equal(got, want)
 
 
+def test_timed_forms_match_and_time_the_kernels():
+    """mx_dispatch_rows_timed / mx_apply_shuffle_mul_sum_timed: the same bytes
+    as the plain calls, and kernel events that lie inside the stage events
+    recorded on the stream around the call."""
+    _print_case("timed forms", 1024, 7168)
+    w = WORKLOADS["uniform_T4096_H7168_E256_k8_pad128"]
+    T, k, E, H = 1024, w.k, w.E, w.H
+    rng = np.random.default_rng(31)
+    ids = routing.uniform_topk(rng, T, E, k)
+    meta = gu.gpu_prepare(ids, E, row_align=128)
+    perm = meta["_t"]["output_permutation"]
+    rows = meta["_t"]["input_permutation"].numel()
+    x = routing.normal_rows(T, H, "bf16", seed=32, device=DEV)
+    y = routing.normal_rows(rows, H, "bf16", seed=33, device=DEV)
+    f = torch.from_numpy(routing.softmax_weights(rng, T, k)).to(DEV)
+    stream = torch.cuda.current_stream()
+    kd = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    kc = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    st = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    for e in (*kd, *kc):
+        e.record(stream)
+    xd1 = torch.full((rows, H), -1, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    xd2 = xd1.clone()
+    o1 = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
+    o2 = torch.empty_like(o1)
+    mx.dispatch_rows(x, perm, k, xd1)
+    mx.apply_shuffle_mul_sum(y, o1, perm, f)
+    st[0].record(stream)
+    mx.dispatch_rows(x, perm, k, xd2, kernel_events=kd)
+    st[1].record(stream)
+    mx.apply_shuffle_mul_sum(y, o2, perm, f, kernel_events=kc)
+    st[2].record(stream)
+    torch.cuda.synchronize()
+    assert torch.equal(xd1.view(torch.int16), xd2.view(torch.int16))
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    for (a, b), (s0, s1) in ((kd, (st[0], st[1])), (kc, (st[1], st[2]))):
+        kernel, stage = a.elapsed_time(b), s0.elapsed_time(s1)
+        assert 0.0 < kernel <= stage
+        assert s0.elapsed_time(a) >= 0.0 and b.elapsed_time(s1) >= 0.0
+
+
 def test_graph_capture_replays_match_eager():
     """The calls enqueue kernels only (no allocation, no memset), so a HIP
     graph can capture prepare, dispatch and combine.  The graph is replayed
