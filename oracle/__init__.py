@@ -27,13 +27,15 @@ DTYPES = {"f32": 0, "f16": 1, "bf16": 2}
 _lib = None
 
 
-def build(out_path: str | None = None, src_path: str | None = None) -> str:
-    """Compile the oracle with gcc; returns the library path."""
+def build(out_path: str | None = None, src_path: str | None = None,
+          extra_flags: list[str] | None = None) -> str:
+    """Compile the oracle with gcc; returns the library path.  ``extra_flags``
+    are appended (the sanitizer test builds an instrumented copy)."""
     out_path = out_path or _LIB_PATH
     src_path = src_path or _SRC
     tmp = f"{out_path}.{os.getpid()}.tmp"
     cmd = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c11", "-Wall",
-           "-Werror", "-fPIC", "-shared", src_path, "-o", tmp, "-lm"]
+           "-Werror", "-fPIC", "-shared", *(extra_flags or []), src_path, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out_path)
     return out_path
