@@ -158,7 +158,7 @@ def copy_probe(nbytes: int, steps: int) -> None:
 def main():
     args = parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+        print(f"bench.py measures one GPU: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus}); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import numpy as np
