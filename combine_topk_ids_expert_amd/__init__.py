@@ -115,11 +115,13 @@ def _ptr(t: torch.Tensor | None):
 
 
 def _check_dev(name: str, t: torch.Tensor, device: torch.device | None = None):
+    # is_cuda / get_device() are the cheap forms of the device checks (a call
+    # is host-bound at small batch sizes).
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.device.type != "cuda":
+    if not t.is_cuda:
         raise ValueError(f"{name} must be on a GPU (got {t.device})")
-    if device is not None and t.device != device:
+    if device is not None and t.get_device() != device.index:
         raise ValueError(f"{name} is on {t.device}, expected {device}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
