@@ -88,7 +88,7 @@ def check_dispatch(x: torch.Tensor, meta: dict, topk: int, scales: torch.Tensor 
         torch.cuda.synchronize()
         got = bits(xd)
         np.testing.assert_array_equal(got[used], want[used], err_msg=mode)
-        raw = xd.view(torch.uint8).cpu().numpy().reshape(rows, -1)
+        raw = xd.view(torch.uint8).cpu().numpy().reshape(rows, int(np.prod(xd.shape[1:])) * xd.element_size())
         assert np.all(raw[~used] == SENTINEL), f"{mode} wrote a padding row"
         if scales is not None:
             sw = oracle.shuffle_rows(bits(scales), inp)
