@@ -10,7 +10,7 @@
 // used, so the result does not depend on launch shapes.
 //
 // One workgroup per token and column chunk of at most 128 threads (the chunks
-// of a token are neighbours in the grid).  A thread owns 8 columns and
+// of a token are neighbours in the grid), at most 7 per CU.  A thread owns 8 columns and
 // issues the loads of up to 8 picks before the first multiply-add, so each
 // wave keeps 8 KiB (16-bit y) of reads in flight; the row indices and weights
 // are loaded one per lane and broadcast with readlane.
@@ -23,6 +23,15 @@ namespace {
 constexpr int kGroup = 8;      // columns per thread in the vector path
 constexpr int kPickBatch = 8;  // picks whose loads are issued together
 constexpr int kCombineThreads = 128;  // workgroup width; longer rows are cut into chunks
+
+// LDS reserved per workgroup of the vector path: at most 7 of its workgroups
+// per CU instead of 16.  Fewer gathers in flight per CU ran faster on MI355X:
+// 90 -> 88.6 us at T = 4096, 175.6 -> 167.2 us at K-hot T = 8192, 200.4 ->
+// 193.5 us for the Zipf workload and 1608 -> 1572 us at T = 65536 with fp32
+// output.  21-22.5 KiB measured alike; 23-26 KiB (6 per CU) gained another
+// 1.5% at T = 65536 but lost about 1% on the others, and 26.5 KiB lost the
+// gain altogether.
+constexpr size_t kCombineLds = 22 * 1024;
 
 
 // N consecutive elements of a row, moved with one 8- or 16-byte access.
@@ -212,10 +221,10 @@ hipError_t launch_typed(const void* y, int64_t num_y_rows, int64_t hidden, const
                                 : nullptr;
         SO* o = static_cast<SO*>(out) + t0 * hidden;
         if (vec)
-            launch_kernel(combine_vec_kernel<TY, TO, FDT>, grid, block, stream, e0, e1,
+            launch_kernel(combine_vec_kernel<TY, TO, FDT>, grid, block, kCombineLds, stream, e0, e1,
                           static_cast<const SY*>(y), num_y_rows, hidden, p, f, topk, o, sh.chunks);
         else
-            launch_kernel(combine_scalar_kernel<TY, TO, FDT>, grid, block, stream, e0, e1,
+            launch_kernel(combine_scalar_kernel<TY, TO, FDT>, grid, block, 0, stream, e0, e1,
                           static_cast<const SY*>(y), num_y_rows, hidden, p, f, topk, o, sh.chunks);
     }, start, stop);
 }

@@ -35,19 +35,29 @@ inline RowShape row_shape(int64_t items, int64_t max_threads) {
     return s;
 }
 
-// Launches kernel<<<grid, block, 0, stream>>>(args...).  With a start or a
-// stop event it goes through hipExtLaunchKernelGGL, which records the events
-// with the kernel dispatch's own begin and end timestamps: the elapsed time
-// between them is the kernel's execution, without the launch gap an event
-// record queued on the stream adds.
+// Occupancy cap through LDS.  A CU of gfx950 has 160 KiB of LDS, so a launch
+// that reserves b bytes of dynamic LDS per workgroup, which the kernel never
+// touches, places at most 160 KiB / b of its workgroups on one CU.  The row
+// kernels hold no LDS of their own and their registers allow 16 two-wave
+// workgroups per CU; the scattered writes of the row dispatch, the gathers of
+// the combine and the padding fill each ran faster on MI355X with fewer of
+// them in flight per CU (the reservations are chosen by measurement, at each
+// kernel's constant).  Kernels without a cap pass 0.
+constexpr size_t kLdsBytesPerCu = 160 * 1024;
+
+// Launches kernel<<<grid, block, lds_bytes, stream>>>(args...).  With a start
+// or a stop event it goes through hipExtLaunchKernelGGL, which records the
+// events with the kernel dispatch's own begin and end timestamps: the elapsed
+// time between them is the kernel's execution, without the launch gap an
+// event record queued on the stream adds.
 template <typename... KArgs, typename... Args>
-inline void launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t stream,
-                          hipEvent_t start, hipEvent_t stop, Args... args) {
+inline void launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t lds_bytes,
+                          hipStream_t stream, hipEvent_t start, hipEvent_t stop, Args... args) {
     if (start != nullptr || stop != nullptr)
-        hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, start, stop, 0u,
+        hipExtLaunchKernelGGL(kernel, grid, block, lds_bytes, stream, start, stop, 0u,
                               static_cast<KArgs>(args)...);
     else
-        hipLaunchKernelGGL(kernel, grid, block, 0, stream, static_cast<KArgs>(args)...);
+        hipLaunchKernelGGL(kernel, grid, block, lds_bytes, stream, static_cast<KArgs>(args)...);
 }
 
 // Launches launch(row0, rows, grid, block, ev_start, ev_stop) for consecutive

@@ -121,7 +121,7 @@ hipError_t launch_dispatch_quant_fp8(const void* src, int64_t num_tokens, int32_
     const uint16_t* s = static_cast<const uint16_t*>(src);
     return for_row_batches(num_tokens, sh, [&](int64_t t0, int64_t, dim3 grid, dim3 block,
                                                hipEvent_t e0, hipEvent_t e1) {
-        launch_kernel(dispatch_quant_fp8_kernel, grid, block, stream, e0, e1, s + t0 * hidden,
+        launch_kernel(dispatch_quant_fp8_kernel, grid, block, 0, stream, e0, e1, s + t0 * hidden,
                       hidden, topk, output_perm + t0 * topk, static_cast<uint8_t*>(dst_q),
                       dst_scales, num_dst_rows, sh.chunks);
     });

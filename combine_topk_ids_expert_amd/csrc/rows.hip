@@ -7,7 +7,7 @@
 // Both are HBM-bound byte copies.  A workgroup owns a column chunk of at most
 // 128 vectors of one row (the chunks of a row are neighbours in the grid) and
 // each thread moves exactly one 16-byte vector: one load, then one store per
-// destination.  Short-lived workgroups with one access per thread sustained
+// destination; the scatter form runs at most 8 workgroups per CU.  Short-lived workgroups with one access per thread sustained
 // the highest write rate on MI355X (several accesses per thread, or looping
 // workgroups, wrote slower).  The write-once destination rows are stored
 // system-coherent: non-temporal while the source rows fit in the Infinity
@@ -25,6 +25,14 @@ namespace {
 // into column chunks.  Two-wave workgroups copied 1-2% faster than one
 // workgroup per 14 KiB row (896 threads).
 constexpr int kRowThreads = 128;
+
+// LDS reserved per workgroup of the row dispatch: at most 8 of its
+// workgroups per CU (16 waves) instead of 16.  Fewer scattered destination
+// streams per CU wrote faster on MI355X: 1632 -> 1502 us at T = 65536 over
+// 288 slots, 105.3 -> 98.7 us for the FP8 rows of the Zipf workload, 170 ->
+// 167 us at K-hot T = 8192 and 94 -> 92.7 us at T = 4096.  18-20 KiB
+// measured alike; from 16 KiB down, or 21 KiB up, some workload lost.
+constexpr size_t kDispatchLds = 19 * 1024;
 
 
 template <int V> struct Vec;
@@ -124,10 +132,10 @@ void launch_dispatch_v(dim3 grid, dim3 block, int32_t chunks, int side_vec, cons
                        int64_t num_dst_rows, const uint8_t* ss, int64_t side_row_bytes,
                        uint8_t* sd, hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
     switch (side_vec) {
-    case 0: launch_kernel(dispatch_rows_kernel<V, 0, P>, grid, block, stream, e0, e1, s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd, chunks); break;
-    case 16: launch_kernel(dispatch_rows_kernel<V, 16, P>, grid, block, stream, e0, e1, s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd, chunks); break;
-    case 4: launch_kernel(dispatch_rows_kernel<V, 4, P>, grid, block, stream, e0, e1, s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd, chunks); break;
-    default: launch_kernel(dispatch_rows_kernel<V, 1, P>, grid, block, stream, e0, e1, s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd, chunks); break;
+    case 0: launch_kernel(dispatch_rows_kernel<V, 0, P>, grid, block, kDispatchLds, stream, e0, e1, s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd, chunks); break;
+    case 16: launch_kernel(dispatch_rows_kernel<V, 16, P>, grid, block, kDispatchLds, stream, e0, e1, s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd, chunks); break;
+    case 4: launch_kernel(dispatch_rows_kernel<V, 4, P>, grid, block, kDispatchLds, stream, e0, e1, s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd, chunks); break;
+    default: launch_kernel(dispatch_rows_kernel<V, 1, P>, grid, block, kDispatchLds, stream, e0, e1, s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd, chunks); break;
     }
 }
 
@@ -146,11 +154,11 @@ hipError_t launch_shuffle_rows(const void* src, int64_t num_src_rows, int64_t ro
         const int32_t* m = dst2src + r0;
         uint8_t* dr = d + r0 * row_bytes;
         switch (v) {
-        case 16: launch_kernel(shuffle_rows_kernel<16>, grid, block, stream, e0, e1, s, num_src_rows, row_bytes, m, dr, sh.chunks); break;
-        case 8: launch_kernel(shuffle_rows_kernel<8>, grid, block, stream, e0, e1, s, num_src_rows, row_bytes, m, dr, sh.chunks); break;
-        case 4: launch_kernel(shuffle_rows_kernel<4>, grid, block, stream, e0, e1, s, num_src_rows, row_bytes, m, dr, sh.chunks); break;
-        case 2: launch_kernel(shuffle_rows_kernel<2>, grid, block, stream, e0, e1, s, num_src_rows, row_bytes, m, dr, sh.chunks); break;
-        default: launch_kernel(shuffle_rows_kernel<1>, grid, block, stream, e0, e1, s, num_src_rows, row_bytes, m, dr, sh.chunks); break;
+        case 16: launch_kernel(shuffle_rows_kernel<16>, grid, block, 0, stream, e0, e1, s, num_src_rows, row_bytes, m, dr, sh.chunks); break;
+        case 8: launch_kernel(shuffle_rows_kernel<8>, grid, block, 0, stream, e0, e1, s, num_src_rows, row_bytes, m, dr, sh.chunks); break;
+        case 4: launch_kernel(shuffle_rows_kernel<4>, grid, block, 0, stream, e0, e1, s, num_src_rows, row_bytes, m, dr, sh.chunks); break;
+        case 2: launch_kernel(shuffle_rows_kernel<2>, grid, block, 0, stream, e0, e1, s, num_src_rows, row_bytes, m, dr, sh.chunks); break;
+        default: launch_kernel(shuffle_rows_kernel<1>, grid, block, 0, stream, e0, e1, s, num_src_rows, row_bytes, m, dr, sh.chunks); break;
         }
     });
 }

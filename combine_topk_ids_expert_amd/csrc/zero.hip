@@ -16,6 +16,12 @@ namespace {
 
 constexpr int kZeroThreads = 128;       // workgroup width (longer rows are cut into column chunks)
 
+// LDS reserved per workgroup of the per-segment padding fill: at most 8 of
+// its workgroups per CU instead of 16, which filled the padding of the T =
+// 4096 workload in 36.7 us instead of 40.6 us.  The output memset keeps no
+// cap: capped at 8 or 6 per CU it was slower (15.1 and 20.1 us against 12.4).
+constexpr size_t kZeroPaddingLds = 19 * 1024;
+
 
 template <int V> struct ZVec;
 template <> struct ZVec<16> { using T = u32x4; };
@@ -131,11 +137,11 @@ hipError_t launch_zero_padding(void* rows, int64_t num_rows, int64_t row_bytes,
         return for_row_batches(pairs, sh, [&](int64_t es0, int64_t, dim3 grid, dim3 block,
                                               hipEvent_t e0, hipEvent_t e1) {
             switch (v) {
-            case 16: launch_kernel(zero_padding_expert_kernel<16>, grid, block, stream, e0, e1, p, num_rows, row_bytes, input_perm, eo, es0, sh.chunks); break;
-            case 8: launch_kernel(zero_padding_expert_kernel<8>, grid, block, stream, e0, e1, p, num_rows, row_bytes, input_perm, eo, es0, sh.chunks); break;
-            case 4: launch_kernel(zero_padding_expert_kernel<4>, grid, block, stream, e0, e1, p, num_rows, row_bytes, input_perm, eo, es0, sh.chunks); break;
-            case 2: launch_kernel(zero_padding_expert_kernel<2>, grid, block, stream, e0, e1, p, num_rows, row_bytes, input_perm, eo, es0, sh.chunks); break;
-            default: launch_kernel(zero_padding_expert_kernel<1>, grid, block, stream, e0, e1, p, num_rows, row_bytes, input_perm, eo, es0, sh.chunks); break;
+            case 16: launch_kernel(zero_padding_expert_kernel<16>, grid, block, kZeroPaddingLds, stream, e0, e1, p, num_rows, row_bytes, input_perm, eo, es0, sh.chunks); break;
+            case 8: launch_kernel(zero_padding_expert_kernel<8>, grid, block, kZeroPaddingLds, stream, e0, e1, p, num_rows, row_bytes, input_perm, eo, es0, sh.chunks); break;
+            case 4: launch_kernel(zero_padding_expert_kernel<4>, grid, block, kZeroPaddingLds, stream, e0, e1, p, num_rows, row_bytes, input_perm, eo, es0, sh.chunks); break;
+            case 2: launch_kernel(zero_padding_expert_kernel<2>, grid, block, kZeroPaddingLds, stream, e0, e1, p, num_rows, row_bytes, input_perm, eo, es0, sh.chunks); break;
+            default: launch_kernel(zero_padding_expert_kernel<1>, grid, block, kZeroPaddingLds, stream, e0, e1, p, num_rows, row_bytes, input_perm, eo, es0, sh.chunks); break;
             }
         });
     }
@@ -144,11 +150,11 @@ hipError_t launch_zero_padding(void* rows, int64_t num_rows, int64_t row_bytes,
         uint8_t* pr = p + r0 * row_bytes;
         const int32_t* m = input_perm + r0;
         switch (v) {
-        case 16: launch_kernel(zero_padding_kernel<16>, grid, block, stream, e0, e1, pr, row_bytes, m, sh.chunks); break;
-        case 8: launch_kernel(zero_padding_kernel<8>, grid, block, stream, e0, e1, pr, row_bytes, m, sh.chunks); break;
-        case 4: launch_kernel(zero_padding_kernel<4>, grid, block, stream, e0, e1, pr, row_bytes, m, sh.chunks); break;
-        case 2: launch_kernel(zero_padding_kernel<2>, grid, block, stream, e0, e1, pr, row_bytes, m, sh.chunks); break;
-        default: launch_kernel(zero_padding_kernel<1>, grid, block, stream, e0, e1, pr, row_bytes, m, sh.chunks); break;
+        case 16: launch_kernel(zero_padding_kernel<16>, grid, block, 0, stream, e0, e1, pr, row_bytes, m, sh.chunks); break;
+        case 8: launch_kernel(zero_padding_kernel<8>, grid, block, 0, stream, e0, e1, pr, row_bytes, m, sh.chunks); break;
+        case 4: launch_kernel(zero_padding_kernel<4>, grid, block, 0, stream, e0, e1, pr, row_bytes, m, sh.chunks); break;
+        case 2: launch_kernel(zero_padding_kernel<2>, grid, block, 0, stream, e0, e1, pr, row_bytes, m, sh.chunks); break;
+        default: launch_kernel(zero_padding_kernel<1>, grid, block, 0, stream, e0, e1, pr, row_bytes, m, sh.chunks); break;
         }
     });
 }
@@ -164,11 +170,11 @@ hipError_t launch_output_memset(void* out, int64_t num_tokens, int32_t topk, int
         uint8_t* pt = p + t0 * row_bytes;
         const int32_t* e = expanded_to_permuted + t0 * topk;
         switch (v) {
-        case 16: launch_kernel(output_memset_kernel<16>, grid, block, stream, e0, e1, pt, row_bytes, topk, e, sh.chunks); break;
-        case 8: launch_kernel(output_memset_kernel<8>, grid, block, stream, e0, e1, pt, row_bytes, topk, e, sh.chunks); break;
-        case 4: launch_kernel(output_memset_kernel<4>, grid, block, stream, e0, e1, pt, row_bytes, topk, e, sh.chunks); break;
-        case 2: launch_kernel(output_memset_kernel<2>, grid, block, stream, e0, e1, pt, row_bytes, topk, e, sh.chunks); break;
-        default: launch_kernel(output_memset_kernel<1>, grid, block, stream, e0, e1, pt, row_bytes, topk, e, sh.chunks); break;
+        case 16: launch_kernel(output_memset_kernel<16>, grid, block, 0, stream, e0, e1, pt, row_bytes, topk, e, sh.chunks); break;
+        case 8: launch_kernel(output_memset_kernel<8>, grid, block, 0, stream, e0, e1, pt, row_bytes, topk, e, sh.chunks); break;
+        case 4: launch_kernel(output_memset_kernel<4>, grid, block, 0, stream, e0, e1, pt, row_bytes, topk, e, sh.chunks); break;
+        case 2: launch_kernel(output_memset_kernel<2>, grid, block, 0, stream, e0, e1, pt, row_bytes, topk, e, sh.chunks); break;
+        default: launch_kernel(output_memset_kernel<1>, grid, block, 0, stream, e0, e1, pt, row_bytes, topk, e, sh.chunks); break;
         }
     });
 }
