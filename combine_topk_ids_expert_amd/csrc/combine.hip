@@ -9,8 +9,8 @@
 // skipped.  The ascending-j chain of fused multiply-adds is the only order
 // used, so the result does not depend on launch shapes.
 //
-// One workgroup per token and column chunk of at most 128 threads (the chunks
-// of a token are neighbours in the grid), at most 7 per CU.  A thread owns 8 columns and
+// One workgroup per token and column chunk of one wave (the chunks of a token
+// are neighbours in the grid), at most 12 per CU.  A thread owns 8 columns and
 // issues the loads of up to 8 picks before the first multiply-add, so each
 // wave keeps 8 KiB (16-bit y) of reads in flight; the row indices and weights
 // are loaded one per lane and broadcast with readlane.
@@ -22,16 +22,17 @@ namespace {
 
 constexpr int kGroup = 8;      // columns per thread in the vector path
 constexpr int kPickBatch = 8;  // picks whose loads are issued together
-constexpr int kCombineThreads = 128;  // workgroup width; longer rows are cut into chunks
+constexpr int kCombineThreads = 64;   // workgroup width; longer rows are cut into chunks
 
-// LDS reserved per workgroup of the vector path: at most 7 of its workgroups
-// per CU instead of 16.  Fewer gathers in flight per CU ran faster on MI355X:
-// 90 -> 88.6 us at T = 4096, 175.6 -> 167.2 us at K-hot T = 8192, 200.4 ->
-// 193.5 us for the Zipf workload and 1608 -> 1572 us at T = 65536 with fp32
-// output.  21-22.5 KiB measured alike; 23-26 KiB (6 per CU) gained another
-// 1.5% at T = 65536 but lost about 1% on the others, and 26.5 KiB lost the
-// gain altogether.
-constexpr size_t kCombineLds = 22 * 1024;
+// LDS reserved per workgroup of the vector path: at most 12 one-wave
+// workgroups per CU instead of 32.  Fewer gathers in flight per CU ran faster
+// on MI355X.  Against two-wave chunks capped at 7 per CU, one-wave chunks at
+// 12 per CU took 1580 -> 1535 us at T = 65536 with fp32 output, 194 -> 190.5
+// us for the Zipf workload, 165.8 -> 164.3 us at K-hot T = 8192 and 88.7-90.4
+// -> 87.9 us at T = 4096; uncapped, the one-wave chunks had been slower than
+// the two-wave ones.  12 and 13 per CU measured alike, 11 or fewer and 14 or
+// more were slower.
+constexpr size_t kCombineLds = 13 * 1024;
 
 
 // N consecutive elements of a row, moved with one 8- or 16-byte access.

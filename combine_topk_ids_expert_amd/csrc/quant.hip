@@ -11,7 +11,8 @@
 // division), so the codes do not depend on launch shapes.
 //
 // A workgroup holds one token row, or a chunk of at most 1024 threads of a
-// longer one (the chunks of a row are neighbours in the grid).  Each thread
+// longer one (the chunks of a row are neighbours in the grid), with about 21
+// waves per CU.  Each thread
 // owns 16 consecutive elements: two 16-byte loads, and one 16-byte store of
 // codes per destination through store16 with the non-temporal,
 // system-coherent policy at every size: 11% faster than a plain
@@ -35,6 +36,19 @@ constexpr int kGroupsPerWave = kWave / kThreadsPerGroup;          // 8
 // threads at 7168).  Chunks of 64 to 256 threads, which suit the plain row
 // copies, made this kernel 1-10% slower on MI355X.
 constexpr int kQuantThreads = 1024;
+
+// LDS reserved per workgroup so that about 21 waves share a CU (3 workgroups
+// of the 7-wave rows of H = 7168, where the registers allow 4): 56.6 -> 55.6
+// us at T = 4096, 104 -> 100.9 us at K-hot T = 8192 and 975 -> 954 us at T =
+// 65536 on MI355X.  Chunks of 64 to 256 threads were slower at every cap
+// tried.  The reservation stays within the 64 KiB a launch may ask for.
+constexpr int kQuantWavesPerCu = 21;
+
+size_t quant_lds(int threads) {
+    const size_t waves = (size_t)(threads / kWave);
+    const size_t b = kLdsBytesPerCu * waves / kQuantWavesPerCu / 512 * 512;
+    return b < 64 * 1024 ? b : 64 * 1024;
+}
 
 
 // Four binary32 values -> four OCP e4m3fn codes (byte i = value i): round to
@@ -121,7 +135,7 @@ hipError_t launch_dispatch_quant_fp8(const void* src, int64_t num_tokens, int32_
     const uint16_t* s = static_cast<const uint16_t*>(src);
     return for_row_batches(num_tokens, sh, [&](int64_t t0, int64_t, dim3 grid, dim3 block,
                                                hipEvent_t e0, hipEvent_t e1) {
-        launch_kernel(dispatch_quant_fp8_kernel, grid, block, 0, stream, e0, e1, s + t0 * hidden,
+        launch_kernel(dispatch_quant_fp8_kernel, grid, block, quant_lds(sh.threads), stream, e0, e1, s + t0 * hidden,
                       hidden, topk, output_perm + t0 * topk, static_cast<uint8_t*>(dst_q),
                       dst_scales, num_dst_rows, sh.chunks);
     });
