@@ -37,12 +37,13 @@ inline RowShape row_shape(int64_t items, int64_t max_threads) {
 
 // Occupancy cap through LDS.  A CU of gfx950 has 160 KiB of LDS, so a launch
 // that reserves b bytes of dynamic LDS per workgroup, which the kernel never
-// touches, places at most 160 KiB / b of its workgroups on one CU.  The row
-// kernels hold no LDS of their own and their registers allow 16 two-wave
-// workgroups per CU; the scattered writes of the row dispatch, the gathers of
-// the combine and the padding fill each ran faster on MI355X with fewer of
-// them in flight per CU (the reservations are chosen by measurement, at each
-// kernel's constant).  Kernels without a cap pass 0.
+// touches, places at most about 160 KiB / b of its workgroups on one CU (the
+// exact count also depends on allocation granularity, so the reservations
+// were chosen by measurement, at each kernel's constant).  The row kernels
+// hold no LDS of their own and their registers allow 32 waves per CU; the
+// scattered writes of the row dispatch, the gathers of the combine, the
+// padding fill and the FP8 dispatch each ran faster on MI355X with fewer
+// waves in flight per CU.  Kernels without a cap pass 0.
 constexpr size_t kLdsBytesPerCu = 160 * 1024;
 
 // Launches kernel<<<grid, block, lds_bytes, stream>>>(args...).  With a start
