@@ -37,7 +37,9 @@ constexpr size_t kCombineLds = 13 * 1024;
 
 // N consecutive elements of a row, moved with one 8- or 16-byte access.
 // Expert output rows are read exactly once, so the loads carry the
-// non-temporal hint; so do the stores of the write-once output rows.
+// non-temporal hint.  The 16-byte stores of the output rows go through
+// store16 with the policy combine_store_policy picks, the 8-byte ones are
+// non-temporal.
 template <typename TY, int N>
 struct Cols {
     static constexpr int kBytes = N * (int)sizeof(typename TY::storage);
@@ -68,12 +70,16 @@ __device__ __forceinline__ Cols<TY, N> load_cols(const typename TY::storage* p) 
     return v;
 }
 
-template <typename TO, int N>
-__device__ __forceinline__ void store_cols(typename TO::storage* p, const float* acc) {
-    constexpr int kBytes = N * (int)sizeof(typename TO::storage);
+// Stores columns [col, col + N) of the output row that starts at `row`
+// (wave-uniform) and holds `hidden` elements.
+template <typename TO, int N, int P>
+__device__ __forceinline__ void store_cols(typename TO::storage* row, int64_t hidden, int64_t col,
+                                           const float* acc) {
+    using SO = typename TO::storage;
+    constexpr int kBytes = N * (int)sizeof(SO);
     static_assert(kBytes == 8 || kBytes == 16, "one 8- or 16-byte access per set");
     uint32_t w[kBytes / 4];
-    if constexpr (sizeof(typename TO::storage) == 2) {
+    if constexpr (sizeof(SO) == 2) {
 #pragma unroll
         for (int i = 0; i < kBytes / 4; ++i)
             w[i] = (uint32_t)from_f32(TO{}, acc[2 * i]) |
@@ -84,11 +90,25 @@ __device__ __forceinline__ void store_cols(typename TO::storage* p, const float*
     }
     if constexpr (kBytes == 16) {
         const u32x4 q = {w[0], w[1], w[2], w[3]};
-        __builtin_nontemporal_store(q, reinterpret_cast<u32x4*>(p));
+        store16<P>(q, reinterpret_cast<uint8_t*>(row), hidden * (int64_t)sizeof(SO),
+                   col * (int64_t)sizeof(SO));
     } else {
         const u32x2 q = {w[0], w[1]};
-        __builtin_nontemporal_store(q, reinterpret_cast<u32x2*>(p));
+        __builtin_nontemporal_store(q, reinterpret_cast<u32x2*>(row + col));
     }
+}
+
+// Cache policy of the output stores.  While the whole output fits in the 256
+// MB Infinity Cache the stores allocate (kKeep) and the lines are written
+// back after the kernel, during whatever runs next; a larger output streams
+// (kStream).  On MI355X, under the occupancy cap, allocating stores took
+// combine from 90.2 to 88.3 us at T = 4096 (58.7 MB of output), 165.1 ->
+// 161.0 us at K-hot T = 8192 and 189.7 -> 185.5 us for the Zipf workload,
+// with the whole step shorter by as much; the 1.88 GB fp32 output at T =
+// 65536 ran 1572 us allocating against 1522 us streaming and 1528 us with
+// plain non-temporal stores.
+inline StorePolicy combine_store_policy(int64_t out_bytes) {
+    return out_bytes > kCacheResidentBytes ? kStream : kKeep;
 }
 
 // Weight of pick (t, j) in fp32.  FDT: -1 unit weights, else the dtype code
@@ -120,7 +140,7 @@ __device__ __forceinline__ float readlane_f(float v, int lane) {
 // weights one per lane (one vector load each) and broadcasts them with
 // readlane; every loop around a readlane is uniform, so threads past the row
 // end stay in the loops and only skip their memory accesses.
-template <typename TY, typename TO, int FDT>
+template <typename TY, typename TO, int FDT, int P>
 __global__ __launch_bounds__(kCombineThreads) void combine_vec_kernel(
     const typename TY::storage* __restrict__ y, int64_t num_y_rows, int64_t hidden,
     const int32_t* __restrict__ perm, const void* __restrict__ factors, int32_t topk,
@@ -182,7 +202,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_vec_kernel(
     }
 #pragma unroll
     for (int s = 0; s < kSets; ++s)
-        if (active[s]) store_cols<TO, kCols>(out + t * hidden + col[s], acc[s]);
+        if (active[s]) store_cols<TO, kCols, P>(out + t * hidden, hidden, col[s], acc[s]);
 }
 
 // Scalar path for any hidden size and element-aligned pointers.
@@ -215,15 +235,21 @@ hipError_t launch_typed(const void* y, int64_t num_y_rows, int64_t hidden, const
     const bool vec = hidden % kGroup == 0 && ((uintptr_t)y % 16) == 0 && ((uintptr_t)out % 16) == 0;
     const RowShape sh = row_shape(vec ? hidden / kGroup : hidden, kCombineThreads);
     const int64_t factor_bytes = FDT == 0 ? 4 : 2;
+    const bool keep = combine_store_policy(T * hidden * (int64_t)sizeof(SO)) == kKeep;
     return for_row_batches(T, sh, [&](int64_t t0, int64_t, dim3 grid, dim3 block,
                                       hipEvent_t e0, hipEvent_t e1) {
         const int32_t* p = perm + t0 * topk;
         const void* f = factors ? static_cast<const char*>(factors) + t0 * topk * factor_bytes
                                 : nullptr;
         SO* o = static_cast<SO*>(out) + t0 * hidden;
-        if (vec)
-            launch_kernel(combine_vec_kernel<TY, TO, FDT>, grid, block, kCombineLds, stream, e0, e1,
-                          static_cast<const SY*>(y), num_y_rows, hidden, p, f, topk, o, sh.chunks);
+        if (vec && keep)
+            launch_kernel(combine_vec_kernel<TY, TO, FDT, kKeep>, grid, block, kCombineLds, stream,
+                          e0, e1, static_cast<const SY*>(y), num_y_rows, hidden, p, f, topk, o,
+                          sh.chunks);
+        else if (vec)
+            launch_kernel(combine_vec_kernel<TY, TO, FDT, kStream>, grid, block, kCombineLds, stream,
+                          e0, e1, static_cast<const SY*>(y), num_y_rows, hidden, p, f, topk, o,
+                          sh.chunks);
         else
             launch_kernel(combine_scalar_kernel<TY, TO, FDT>, grid, block, 0, stream, e0, e1,
                           static_cast<const SY*>(y), num_y_rows, hidden, p, f, topk, o, sh.chunks);

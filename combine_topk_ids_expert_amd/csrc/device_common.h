@@ -94,7 +94,7 @@ __device__ __forceinline__ int64_t chunk_row(int32_t chunks, int64_t& chunk) {
 // kKeep was 1.6-2.6% faster (T = 24576 to 65536 rows of 14 KiB), and below
 // it 12-14% slower, since the allocated destination lines evict the source
 // rows.  kCacheResidentBytes is the source size up to which the row dispatch
-// uses kStream.
+// uses kStream, and the output size up to which the combine uses kKeep.
 enum StorePolicy : int { kStream = 1 | 2 | 16, kKeep = 16 };
 constexpr int64_t kCacheResidentBytes = (int64_t)256 << 20;
 
