@@ -10,7 +10,7 @@
 // used, so the result does not depend on launch shapes.
 //
 // One workgroup per token and column chunk of one wave (the chunks of a token
-// are neighbours in the grid), at most 12 per CU.  A thread owns 8 columns and
+// are neighbours in the grid), at most 12 or 13 per CU.  A thread owns 8 columns and
 // issues the loads of up to 8 picks before the first multiply-add, so each
 // wave keeps 8 KiB (16-bit y) of reads in flight; the row indices and weights
 // are loaded one per lane and broadcast with readlane.
@@ -24,15 +24,20 @@ constexpr int kGroup = 8;      // columns per thread in the vector path
 constexpr int kPickBatch = 8;  // picks whose loads are issued together
 constexpr int kCombineThreads = 64;   // workgroup width; longer rows are cut into chunks
 
-// LDS reserved per workgroup of the vector path: at most 12 one-wave
-// workgroups per CU instead of 32.  Fewer gathers in flight per CU ran faster
-// on MI355X.  Against two-wave chunks capped at 7 per CU, one-wave chunks at
-// 12 per CU took 1580 -> 1535 us at T = 65536 with fp32 output, 194 -> 190.5
-// us for the Zipf workload, 165.8 -> 164.3 us at K-hot T = 8192 and 88.7-90.4
-// -> 87.9 us at T = 4096; uncapped, the one-wave chunks had been slower than
-// the two-wave ones.  12 and 13 per CU measured alike, 11 or fewer and 14 or
-// more were slower.
-constexpr size_t kCombineLds = 13 * 1024;
+// LDS reserved per workgroup of the vector path, which caps the one-wave
+// workgroups per CU (32 without a cap): fewer gathers in flight per CU ran
+// faster on MI355X.  The best cap depends on the output store policy
+// (combine_store_policy below).
+//   Streaming stores: 12 per CU.  Against two-wave chunks capped at 7 per CU
+//     it took 1580 -> 1535 us at T = 65536 with fp32 output; 13 per CU ran
+//     1522 against 1515 us, 14 and more or 11 and fewer were slower still.
+//     (Uncapped, one-wave chunks had been slower than two-wave ones.)
+//   Allocating stores: 13 per CU.  Against 12: 85.4 -> 84.1 us at T = 4096,
+//     159.9 -> 157.3 us at K-hot T = 8192, 185.3 -> 184.3 us on the Zipf
+//     workload; 14 per CU was faster at T = 4096 only, 11 and fewer slower
+//     everywhere.
+constexpr size_t kCombineLdsStream = 13 * 1024;  // 12 per CU
+constexpr size_t kCombineLdsKeep = 12 * 1024;    // 13 per CU
 
 
 // N consecutive elements of a row, moved with one 8- or 16-byte access.
@@ -243,11 +248,11 @@ hipError_t launch_typed(const void* y, int64_t num_y_rows, int64_t hidden, const
                                 : nullptr;
         SO* o = static_cast<SO*>(out) + t0 * hidden;
         if (vec && keep)
-            launch_kernel(combine_vec_kernel<TY, TO, FDT, kKeep>, grid, block, kCombineLds, stream,
+            launch_kernel(combine_vec_kernel<TY, TO, FDT, kKeep>, grid, block, kCombineLdsKeep, stream,
                           e0, e1, static_cast<const SY*>(y), num_y_rows, hidden, p, f, topk, o,
                           sh.chunks);
         else if (vec)
-            launch_kernel(combine_vec_kernel<TY, TO, FDT, kStream>, grid, block, kCombineLds, stream,
+            launch_kernel(combine_vec_kernel<TY, TO, FDT, kStream>, grid, block, kCombineLdsStream, stream,
                           e0, e1, static_cast<const SY*>(y), num_y_rows, hidden, p, f, topk, o,
                           sh.chunks);
         else
