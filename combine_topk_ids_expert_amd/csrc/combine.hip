@@ -10,10 +10,11 @@
 // used, so the result does not depend on launch shapes.
 //
 // One workgroup per token and column chunk of one wave (the chunks of a token
-// are neighbours in the grid), at most 12 or 13 per CU.  A thread owns 8 columns and
-// issues the loads of up to 8 picks before the first multiply-add, so each
-// wave keeps 8 KiB (16-bit y) of reads in flight; the row indices and weights
-// are loaded one per lane and broadcast with readlane.
+// are neighbours in the grid), at most 12 or 13 per CU.  A thread owns 8
+// columns and issues the loads of up to 8 picks before the first
+// multiply-add, so each wave keeps 8 KiB (16-bit y) of reads in flight; the
+// row indices and weights are loaded one per lane and broadcast with
+// readlane.
 #include "device_common.h"
 #include "launch.h"
 
