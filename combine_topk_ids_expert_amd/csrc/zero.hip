@@ -16,11 +16,12 @@ namespace {
 
 constexpr int kZeroThreads = 128;       // workgroup width (longer rows are cut into column chunks)
 
-// LDS reserved per workgroup of the per-segment padding fill: at most 8 of
-// its workgroups per CU instead of 16, which filled the padding of the T =
-// 4096 workload in 36.7 us instead of 40.6 us.  The output memset keeps no
-// cap: capped at 8 or 6 per CU it was slower (15.1 and 20.1 us against 12.4).
-constexpr size_t kZeroPaddingLds = 19 * 1024;
+// LDS reserved per workgroup of the per-segment padding fill: at most 10 of
+// its two-wave workgroups per CU instead of 16.  At T = 4096 (event times on
+// MI355X) it filled the padding in 35.5 us, against 37.9 us uncapped, 36.0 us
+// at 8 per CU, 35.8 at 12 and 37.8 at 16.  The output memset keeps no cap:
+// capped at 8 or 6 per CU it was slower (15.1 and 20.1 us against 12.4).
+constexpr size_t kZeroPaddingLds = 16 * 1024;
 
 
 template <int V> struct ZVec;
