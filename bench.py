@@ -6,20 +6,40 @@ metadata) -> dispatch_rows (token rows into expert-contiguous rows) ->
 apply_shuffle_mul_sum (gather, weight, fp32 sum back to tokens).  Inputs are
 seeded synthetic routing and activations, resident in HBM before timing.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME|all]
 
-Prints one JSON line: tokens/s over the K timed steps (wall clock between
-two device synchronisations); from a second pass of K steps, per-stage times
-from HIP events recorded on the launch stream around each stage, and the
-dispatch and combine kernels' own durations from HIP events recorded with
-the kernels' begin and end timestamps; the dominant kernel's achieved
-algorithmic HBM bandwidth against MI355X's 8 TB/s; and the CPU oracle timed
-on a bounded sample of the same workload on the host.
+Prints one JSON line.  The headline workload is the largest one that fits one
+GPU (T = 65536 tokens, hidden 7168, 288 expert slots, fp32 output); with the
+default ``--workload all`` the other four workloads ride along in the same
+line under ``workloads``.  Each workload is timed three ways, each over 5
+repetitions of exactly K steps between two device synchronisations:
 
---graph captures one step's launches in a HIP graph and times K replays of
-it, so the headline holds no host launch cost (the per-stage event pass stays
-eager).  --copy-probe BYTES times a plain device copy of BYTES bytes instead
-(the reference kernel whose HBM counters calibrate the traffic figures).
+  cold  -- before every step, outside the timed interval, 512 MiB are written
+           and then 1 GiB is read, which evicts the 256 MB Infinity Cache and
+           the L2s and leaves only clean lines behind; the step is timed from
+           the begin of its first kernel to the end of its last, by events
+           the timed entry points record with the kernel dispatches' own
+           timestamps.  ``value`` and ``ms_per_step`` are the cold figures.
+  warm  -- K steps back to back with the plain entry points, one event pair
+           around the K steps (the figure a pipeline that keeps the data
+           resident would see; a step's deferred write-backs land in the next
+           step, so they are counted).
+  warm_timed -- the same steps back to back through the timed entry points,
+           for per-step percentiles and the split into stages.
+
+Stages follow the benchmark RFC page's split: dispatch = prepare_moe_input +
+dispatch_rows (from the begin of the routing kernels to the end of the
+dispatch kernel), combine = apply_shuffle_mul_sum.  Mean over repetitions,
+the spread of the repetition means, and p50 / p90 / p99 / p999 over all steps.
+
+The roofline is the dominant row kernel's algorithmic bytes per launch over
+its mean cold kernel time, against 8 TB/s.  ``cpu_baseline`` times the CPU
+oracle on a bounded token sample of the headline workload, on one thread and
+on the host's cores (the row loops split over threads; routing stays one
+thread, as it is defined).
+
+--graph captures one step in a HIP graph and adds a warm figure of K graph
+replays.  --copy-probe BYTES times a plain device copy instead.
 """
 
 from __future__ import annotations
@@ -28,8 +48,10 @@ import argparse
 import hashlib
 import json
 import os
+import platform
 import re
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -37,9 +59,16 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
-DEFAULT_WORKLOAD = "uniform_T4096_H7168_E256_k8_pad128"
 METRIC = "dispatch+combine tokens/s; achieved HBM GB/s vs MI355X peak"
+HEADLINE = "replica288_T65536_H7168_k8_f32out"
+# headline first, then the other workloads carried in the same line
+ORDER = (HEADLINE, "uniform_T4096_H7168_E256_k8_pad128", "khot8_T8192_H7168_E256_k8",
+         "zipf1.2_T16384_H4096fp8_E128_k8", "uniform_T32_H4096_E256_k8")
+REPS = 5
+FLUSH_WRITE_BYTES = 512 << 20
+FLUSH_READ_BYTES = 1 << 30
 KERNEL_SOURCES = ("route.hip", "rows.hip", "combine.hip", "device_common.h")
+KERNEL_NAMES = {"dispatch": "dispatch_rows_kernel", "combine": "combine_vec_kernel"}
 
 
 def _code_only(text: str) -> str:
@@ -58,27 +87,28 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def parse_args():
+def parse_args(argv=None):
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    p.add_argument("--cpu-seconds", type=float, default=12.0,
-                   help="wall-clock budget of the CPU-oracle sample")
+    p.add_argument("--steps", type=int, default=50, help="steps per repetition")
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="all",
+                   help="'all' (headline plus the other workloads) or one workload name")
+    p.add_argument("--cpu-seconds", type=float, default=8.0,
+                   help="wall-clock budget of each leg of the CPU-oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-probe", type=int, default=0, metavar="BYTES")
     p.add_argument("--graph", action="store_true",
-                   help="time replays of a HIP graph of one step instead of eager launches")
+                   help="also time K replays of a HIP graph of one step (warm)")
     p.add_argument("--with", dest="extras", default="",
-                   help="comma-separated extra stages added to each step and reported "
-                        "separately: zero_padding (zero-fill the padding rows after "
-                        "dispatch), output_memset (zero the output rows before combine), "
-                        "moe_sort (tile-padded sort metadata over all experts, tiles of "
-                        "row_align rows, after prepare), quantize_dispatch (bf16 rows "
-                        "quantized to fp8 e4m3 with 1x128 scales and dispatched, after "
-                        "dispatch)")
-    return p.parse_args()
+                   help="comma-separated extra stages added to each step of the first "
+                        "workload and reported separately: zero_padding (zero-fill the "
+                        "padding rows after dispatch), output_memset (zero the output rows "
+                        "before combine), moe_sort (tile-padded sort metadata over all "
+                        "experts, tiles of row_align rows, after prepare), quantize_dispatch "
+                        "(bf16 rows quantized to fp8 e4m3 with 1x128 scales and dispatched, "
+                        "after dispatch)")
+    return p.parse_args(argv)
 
 
 def algorithmic_bytes(w, n_valid: int, cap: int, id_bytes: int) -> dict:
@@ -96,11 +126,19 @@ def algorithmic_bytes(w, n_valid: int, cap: int, id_bytes: int) -> dict:
     return {"prepare": prep, "dispatch": disp, "combine": comb}
 
 
+def gate_ms(w, step_bytes: int):
+    """Step time at 70% of 8 TB/s for the gated workloads (T >= 4096 and
+    hidden 7168), else None."""
+    if w.T >= 4096 and w.H == 7168:
+        return step_bytes / (0.7 * HBM_PEAK_GBPS * 1e9) * 1e3
+    return None
+
+
 def load_traffic(workload: str, kernel: str) -> dict | None:
-    """HBM bytes per launch of ``kernel`` from the committed rocprofv3
-    counter summary (FETCH_SIZE and WRITE_SIZE, each scaled by what the same
-    counter reads for a plain copy of known size), if it was taken on the
-    current kernel sources; None otherwise."""
+    """L2-to-fabric bytes per launch of ``kernel`` from the committed
+    rocprofv3 counter summary (FETCH_SIZE and WRITE_SIZE, scaled by the
+    factors of a calibration kernel), if it was taken on the current kernel
+    sources; None otherwise."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     try:
         with open(path) as f:
@@ -112,31 +150,400 @@ def load_traffic(workload: str, kernel: str) -> dict | None:
     return rec.get("kernels", {}).get(kernel)
 
 
-def cpu_baseline(w, inp, x, y, budget_s: float) -> dict:
-    """The oracle, as it stands, on the same workload: whole steps (prepare,
-    row gather, combine) repeated until the time budget is spent."""
+def stats(values) -> dict:
+    """mean, p50 / p90 / p99 / p999 and min over all samples (ms)."""
+    import numpy as np
+    a = np.asarray(values, dtype=np.float64)
+    return {"mean": float(a.mean()), "p50": float(np.percentile(a, 50)),
+            "p90": float(np.percentile(a, 90)), "p99": float(np.percentile(a, 99)),
+            "p999": float(np.percentile(a, 99.9)), "min": float(a.min()),
+            "samples": int(a.size)}
+
+
+def rep_stats(per_rep) -> dict:
+    """Mean over repetitions of the repetition means, and their spread."""
+    import numpy as np
+    m = np.array([float(np.mean(r)) for r in per_rep])
+    return {"mean": float(m.mean()), "rep_means": [float(x) for x in m],
+            "rep_spread": float(m.max() - m.min()), "reps": int(m.size)}
+
+
+# ---- CPU baseline -----------------------------------------------------------
+
+def host_description() -> dict:
+    model = platform.processor() or ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    return {"cpu_model": model, "nproc": avail, "os_cpu_count": os.cpu_count()}
+
+
+def cpu_baseline(w, budget_s: float, dev) -> dict:
+    """The oracle, as it stands, on a bounded sample of the workload: the
+    same routing, hidden size and dtypes with fewer tokens.  One step of the
+    sample = prepare_moe_input over its picks (one thread, as defined), the
+    row gather into expert-contiguous rows, and the combine.  Timed on one
+    thread and with the row loops split over the host's cores (threads call
+    the C oracle, which releases the GIL), each leg repeated until its budget
+    is spent."""
     import numpy as np
     import torch
     import oracle
+    from workloads import build_inputs
+    from workloads.configs import expert_output
 
-    ids = inp["ids"]
-    x_bits = x.cpu().contiguous()
-    x_bits = x_bits.view(torch.uint8).numpy()
-    y_bits = y.cpu().view(torch.int16).numpy().view(np.uint16) if y.dtype != torch.float32 \
-        else y.cpu().numpy()
-    y_code = {"bf16": "bf16", "f16": "f16", "f32": "f32"}[w.y_dtype]
-    steps, t_total = 0, 0.0
-    while steps == 0 or (t_total < budget_s and steps < 50):
-        t0 = time.perf_counter()
+    host = host_description()
+    threads = max(1, min(host["nproc"], 16))
+    legs = {}
+    for name, n_threads, t_sample in (("single_thread", 1, min(w.T, 2048)),
+                                      ("all_cores", threads, min(w.T, 8192))):
+        inp = build_inputs(w, dev, T=t_sample)
+        ids = inp["ids"]
         m = oracle.prepare_moe_input(ids, w.E, row_align=w.row_align)
-        oracle.shuffle_rows(x_bits, m["input_permutation"])
-        oracle.apply_shuffle_mul_sum(y_bits, y_code, m["output_permutation"], inp["weights"],
-                                     "f32", w.T, w.k, w.out_dtype)
-        t_total += time.perf_counter() - t0
-        steps += 1
-    return {"value": w.T * steps / t_total, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{steps} whole step(s) of {w.name} (T={w.T}), single-threaded C oracle, "
-                      f"{t_total:.1f} s"}
+        rows = len(m["input_permutation"])
+        x = inp["x"]
+        x_host = x.cpu().contiguous().view(torch.uint8).numpy().reshape(t_sample, -1)
+        y = expert_output(w, rows, dev)
+        y_host = (y.cpu().view(torch.int16).numpy().view(np.uint16) if y.dtype != torch.float32
+                  else y.cpu().numpy())
+        del x, y
+        torch.cuda.empty_cache()
+        xd = np.zeros((rows, x_host.shape[1]), np.uint8)
+        out = {}
+
+        def rows_part(r0, r1, perm):
+            oracle.shuffle_rows(x_host, perm[r0:r1], dst=xd[r0:r1])
+
+        def comb_part(t0, t1, perm):
+            out[t0] = oracle.apply_shuffle_mul_sum(
+                y_host, w.y_dtype, perm[t0 * w.k:t1 * w.k], inp["weights"][t0:t1], "f32",
+                t1 - t0, w.k, w.out_dtype)
+
+        def run_split(fn, n, perm):
+            if n_threads == 1:
+                fn(0, n, perm)
+                return
+            bounds = [n * i // n_threads for i in range(n_threads + 1)]
+            ts = [threading.Thread(target=fn, args=(bounds[i], bounds[i + 1], perm))
+                  for i in range(n_threads) if bounds[i + 1] > bounds[i]]
+            for t in ts:
+                t.start()
+            for t in ts:
+                t.join()
+
+        steps, t_total = 0, 0.0
+        while steps == 0 or (t_total < budget_s and steps < 20):
+            t0 = time.perf_counter()
+            m = oracle.prepare_moe_input(ids, w.E, row_align=w.row_align)
+            run_split(rows_part, rows, m["input_permutation"])
+            run_split(comb_part, t_sample, m["output_permutation"])
+            t_total += time.perf_counter() - t0
+            steps += 1
+        legs[name] = {"value": t_sample * steps / t_total, "threads": n_threads,
+                      "sample_tokens": t_sample, "steps": steps, "seconds": t_total}
+    allc = legs["all_cores"]
+    return {"value": allc["value"], "unit": "tokens/s", "cores": allc["threads"],
+            "kind": "oracle",
+            "sample": (f"{w.name} routing, hidden and dtypes with T = {allc['sample_tokens']} "
+                       f"tokens ({legs['single_thread']['sample_tokens']} on one thread); whole "
+                       f"steps: prepare (one thread), row gather and combine split over "
+                       f"threads; {allc['steps']} steps on {allc['threads']} threads, "
+                       f"{legs['single_thread']['steps']} on one"),
+            "single_thread_value": legs["single_thread"]["value"], "legs": legs, **host}
+
+
+# ---- GPU measurement ----------------------------------------------------------
+
+class Flusher:
+    """Evicts the Infinity Cache and the L2s: writes 512 MiB, then reads
+    1 GiB of other memory, so the written lines are written back during the
+    flush and only clean lines stay cached."""
+
+    def __init__(self, dev):
+        import torch
+        self.w = torch.empty(FLUSH_WRITE_BYTES, dtype=torch.uint8, device=dev)
+        self.r = torch.ones(FLUSH_READ_BYTES // 4, dtype=torch.int32, device=dev)
+        self.n = 0
+
+    def __call__(self):
+        self.n += 1
+        self.w.fill_(self.n & 0xff)
+        self.r.max()
+
+
+class Step:
+    """Buffers and bound calls of one step of workload ``w``."""
+
+    def __init__(self, w, dev, extras=()):
+        import torch
+        import combine_topk_ids_expert_amd as mx
+        from workloads import build_inputs
+        from workloads.configs import expert_output
+
+        self.w = w
+        inp = build_inputs(w, dev)
+        T, k, E, H = w.T, w.k, w.E, w.H
+        self.ids = torch.from_numpy(inp["ids"]).to(dev)
+        self.weights = torch.from_numpy(inp["weights"]).to(dev)
+        x, scales = inp["x"], inp["scales"]
+        r = mx.empty_routing(T, k, E, dev, row_align=w.row_align, blockscale=w.blockscale)
+        self.r = r
+        self.cap = r["input_permutation"].numel()
+        xd = torch.empty((self.cap, H), dtype=x.dtype, device=dev)
+        sd = (torch.empty((self.cap, scales.shape[1]), dtype=torch.float32, device=dev)
+              if scales is not None else None)
+        y = expert_output(w, self.cap, dev)
+        odt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[w.out_dtype]
+        out = torch.empty((T, H), dtype=odt, device=dev)
+        self.x, self.xd, self.y, self.out = x, xd, y, out
+        self.prepare = mx.bind(mx.prepare_moe_input, self.ids, r["expert_offsets"],
+                               r["problem_sizes1"], r["problem_sizes2"], r["input_permutation"],
+                               r["output_permutation"], E, 2048, H, r["blockscale_offsets"],
+                               row_align=w.row_align, workspace=r["workspace"])
+        self.dispatch = mx.bind(mx.dispatch_rows, x, r["output_permutation"], k, xd, scales, sd)
+        self.combine = mx.bind(mx.apply_shuffle_mul_sum, y, out, r["output_permutation"],
+                               self.weights)
+        self.extras = []
+        self.extra_bytes = {}
+        row_b = H * x.element_size()
+        for e in extras:
+            if e == "zero_padding":
+                fn = mx.bind(mx.zero_padding_rows, xd, r["input_permutation"],
+                             r["expert_offsets"])
+            elif e == "output_memset":
+                fn = mx.bind(mx.moe_output_memset, out, r["output_permutation"], k)
+            elif e == "moe_sort":
+                sort_ws = torch.empty(max(mx.prepare_workspace_size(T, k, E), 16),
+                                      dtype=torch.uint8, device=dev)
+                sort_out = mx.moe_sort(self.ids, E, 0, E, max(w.row_align, 1), workspace=sort_ws)
+                self._sort = (sort_out, sort_ws)
+
+                def fn(so=sort_out, ws=sort_ws):
+                    mx.moe_sort(self.ids, E, 0, E, max(w.row_align, 1), out=so, workspace=ws)
+            elif e == "quantize_dispatch":
+                if x.dtype != torch.bfloat16 or H % 128:
+                    raise SystemExit("quantize_dispatch needs a bf16 workload with hidden % 128 == 0")
+                xq = torch.empty((self.cap, H), dtype=torch.float8_e4m3fn, device=dev)
+                sq = torch.empty((self.cap, H // 128), dtype=torch.float32, device=dev)
+                fn = mx.bind(mx.dispatch_rows_fp8, x, r["output_permutation"], k, xq, sq)
+            else:
+                raise SystemExit(f"unknown --with stage {e!r}; known: zero_padding, "
+                                 "output_memset, moe_sort, quantize_dispatch")
+            self.extras.append((e, fn))
+        self.row_b = row_b
+
+    def run(self):
+        self.prepare()
+        for name, fn in self.extras:
+            if name == "moe_sort":
+                fn()
+        self.dispatch()
+        for name, fn in self.extras:
+            if name in ("quantize_dispatch", "zero_padding", "output_memset"):
+                fn()
+        self.combine()
+
+    def run_timed(self, ev):
+        """The step through the timed entry points; ev = six events (prepare,
+        dispatch and combine kernel begin / end).  Extra stages run plain."""
+        self.prepare(kernel_events=(ev[0], ev[1]))
+        for name, fn in self.extras:
+            if name == "moe_sort":
+                fn()
+        self.dispatch(kernel_events=(ev[2], ev[3]))
+        for name, fn in self.extras:
+            if name in ("quantize_dispatch", "zero_padding", "output_memset"):
+                fn()
+        self.combine(kernel_events=(ev[4], ev[5]))
+
+
+def _events(n):
+    import torch
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for e in evs:              # torch creates an event's HIP handle at its first record
+        e.record()
+    return evs
+
+
+def timed_pass(step: Step, K: int, flush) -> dict:
+    """REPS repetitions of K steps through the timed entry points; with
+    ``flush`` the caches are evicted before every step, outside the timed
+    interval.  Returns per-rep lists of per-step times (ms)."""
+    import torch
+    evs = [_events(6) for _ in range(K)]
+    out = {"e2e": [], "dispatch": [], "combine": [], "prepare_kernel": [],
+           "dispatch_kernel": [], "wall_per_step": []}
+    for _ in range(REPS):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(K):
+            if flush is not None:
+                flush()
+            step.run_timed(evs[s])
+        torch.cuda.synchronize()
+        out["wall_per_step"].append([(time.perf_counter() - t0) / K * 1e3])
+        out["e2e"].append([e[0].elapsed_time(e[5]) for e in evs])
+        out["dispatch"].append([e[0].elapsed_time(e[3]) for e in evs])
+        out["combine"].append([e[4].elapsed_time(e[5]) for e in evs])
+        out["prepare_kernel"].append([e[0].elapsed_time(e[1]) for e in evs])
+        out["dispatch_kernel"].append([e[2].elapsed_time(e[3]) for e in evs])
+    return out
+
+
+def warm_pass(run, K: int) -> dict:
+    """REPS repetitions of K back-to-back steps, one event pair around each
+    repetition, and the host's clock between the two synchronisations."""
+    import torch
+    a, b = _events(2)
+    per_rep, wall = [], []
+    for _ in range(REPS):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        a.record()
+        for _ in range(K):
+            run()
+        b.record()
+        torch.cuda.synchronize()
+        wall.append((time.perf_counter() - t0) / K * 1e3)
+        per_rep.append([a.elapsed_time(b) / K])
+    return {"per_rep": per_rep, "wall": wall}
+
+
+def extras_pass(step: Step, K: int) -> dict:
+    """Stage events around every stage of the step (extra stages included),
+    warm, for the extra stages' times."""
+    import torch
+    names = ["prepare"] + [n for n, _ in step.extras if n == "moe_sort"] + ["dispatch"] + \
+        [n for n, _ in step.extras if n != "moe_sort"] + ["combine"]
+    fns = dict(step.extras)
+    fns.update(prepare=step.prepare, dispatch=step.dispatch, combine=step.combine)
+    ev = [_events(len(names) + 1) for _ in range(K)]
+    torch.cuda.synchronize()
+    for s in range(K):
+        ev[s][0].record()
+        for i, n in enumerate(names):
+            fns[n]()
+            ev[s][i + 1].record()
+    torch.cuda.synchronize()
+    return {n: [ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(K)]
+            for i, n in enumerate(names)}
+
+
+def measure(w, args, dev, flush, extras=(), with_cpu=False) -> dict:
+    import numpy as np
+    import torch
+
+    step = Step(w, dev, extras)
+    K = args.steps
+    for _ in range(args.warmup):
+        step.run()
+    torch.cuda.synchronize()
+    cold = timed_pass(step, K, flush)
+    warm = warm_pass(step.run, K)
+    warm_t = timed_pass(step, K, None)
+    graph = None
+    if args.graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step.run()
+        for _ in range(args.warmup):
+            g.replay()
+        graph = warm_pass(g.replay, K)
+
+    counts = step.r["problem_sizes1"][:, 0].cpu().numpy()
+    n_valid = int(counts.sum())
+    nbytes = algorithmic_bytes(w, n_valid, step.cap, step.ids.element_size())
+    step_bytes = sum(nbytes.values())
+    T = w.T
+
+    def flat(per_rep):
+        return [v for r in per_rep for v in r]
+
+    def summary(passes: dict, label: str) -> dict:
+        e2e = stats(flat(passes["e2e"]))
+        ms = e2e["mean"]
+        kd = stats(flat(passes["dispatch_kernel"]))
+        kc = stats(flat(passes["combine"]))
+        dom = "dispatch" if kd["mean"] >= kc["mean"] else "combine"
+        kdom = kd if dom == "dispatch" else kc
+        gbps = nbytes[dom] / (kdom["mean"] * 1e-3) / 1e9
+        return {
+            "cache": label,
+            "step_ms": ms, "tokens_per_s": T / (ms * 1e-3),
+            "step_gbps": step_bytes / (ms * 1e-3) / 1e9,
+            "step_frac": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+            "reps": rep_stats(passes["e2e"]),
+            "e2e_ms": e2e, "dispatch_ms": stats(flat(passes["dispatch"])),
+            "combine_ms": kc,
+            "prepare_kernel_ms": stats(flat(passes["prepare_kernel"])),
+            "dispatch_kernel_ms": kd,
+            "host_wall_ms_per_step": float(np.mean(flat(passes["wall_per_step"]))),
+            "dominant_kernel": KERNEL_NAMES[dom], "dominant_stage": dom,
+            "dominant_kernel_gbps": gbps, "dominant_kernel_frac": gbps / HBM_PEAK_GBPS,
+            "row_kernels_frac": (nbytes["dispatch"] + nbytes["combine"])
+                                 / ((kd["mean"] + kc["mean"]) * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        }
+
+    res = {
+        "workload": w.name, "T": T, "H": w.H, "E": w.E, "topk": w.k, "routing": w.mode,
+        "row_align": w.row_align, "x_dtype": w.x_dtype, "out_dtype": w.out_dtype,
+        "algorithmic_bytes": nbytes, "step_bytes": step_bytes,
+        "cold": summary(cold, "cold: 512 MiB written and 1 GiB read before each step, "
+                              "outside the timed interval"),
+        "warm_timed": summary(warm_t, "warm: back to back, timed entry points"),
+        "expert_load": {"max": int(counts.max()), "min": int(counts.min()),
+                        "mean": float(counts.mean()),
+                        "imbalance_ratio": float(counts.max() / max(counts.mean(), 1e-9))},
+    }
+    wm = rep_stats(warm["per_rep"])["mean"]
+    res["warm"] = {"cache": "warm: K steps back to back, plain entry points, one event pair "
+                            "around each repetition",
+                   "step_ms": wm, "tokens_per_s": T / (wm * 1e-3),
+                   "step_frac": step_bytes / (wm * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                   "reps": rep_stats(warm["per_rep"]),
+                   "host_wall_ms_per_step": float(np.mean(warm["wall"]))}
+    if graph is not None:
+        gm = rep_stats(graph["per_rep"])["mean"]
+        res["warm_graph"] = {"step_ms": gm, "tokens_per_s": T / (gm * 1e-3),
+                             "reps": rep_stats(graph["per_rep"])}
+    g = gate_ms(w, step_bytes)
+    if g is not None:
+        res["gate_70pct"] = {"step_ms_max": g, "met_cold": res["cold"]["step_ms"] <= g,
+                             "met_warm": wm <= g}
+    if step.extras:
+        ex = extras_pass(step, K)
+        row_b = step.row_b
+        extra_b = {}
+        for e, _ in step.extras:
+            if e == "zero_padding":
+                padded = int(step.r["expert_offsets"][-1].item())
+                extra_b[e] = (padded - n_valid) * row_b + step.cap * 4
+            elif e == "output_memset":
+                has_pick = (step.r["output_permutation"].view(T, w.k) >= 0).any(dim=1).sum().item()
+                extra_b[e] = int(has_pick) * w.H * step.out.element_size() + T * w.k * 4
+            elif e == "quantize_dispatch":
+                extra_b[e] = T * w.H * 2 + n_valid * (w.H + w.H // 128 * 4) + T * w.k * 4
+            elif e == "moe_sort":
+                so = step._sort[0]
+                scap = so["permuted_idx_to_expanded_idx"].numel()
+                extra_b[e] = (T * w.k * step.ids.element_size() + T * w.k * 4 + scap * 4
+                              + 2 * 4 * so["tile_idx_to_group_idx"].numel() + 4 * (w.E + 3))
+        res["extras"] = {e: {"ms": float(np.mean(ex[e])), "algorithmic_bytes": extra_b[e],
+                             "frac": extra_b[e] / (float(np.mean(ex[e])) * 1e-3) / 1e9
+                             / HBM_PEAK_GBPS} for e, _ in step.extras}
+    res["_cap"] = step.cap
+    del step
+    torch.cuda.empty_cache()
+    return res
 
 
 def copy_probe(nbytes: int, steps: int) -> None:
@@ -155,228 +562,101 @@ def copy_probe(nbytes: int, steps: int) -> None:
                       "gbps_read_plus_write": 2 * nbytes / dt / 1e9}), flush=True)
 
 
-def main():
-    args = parse_args()
+def main(argv=None):
+    args = parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus}); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
-    import numpy as np
     import torch
 
     if args.copy_probe:
         copy_probe(args.copy_probe, max(args.steps, 1))
         return
 
-    import combine_topk_ids_expert_amd as mx
-    from workloads import get_workload, build_inputs
-    from workloads.configs import expert_output
+    from workloads import get_workload
 
-    w = get_workload(args.workload)
+    names = ORDER if args.workload == "all" else (args.workload,)
+    ws = [get_workload(n) for n in names]
+    extras = [e for e in args.extras.split(",") if e]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    inp = build_inputs(w, dev)
-    T, k, E, H = w.T, w.k, w.E, w.H
-    ids = torch.from_numpy(inp["ids"]).to(dev)
-    weights = torch.from_numpy(inp["weights"]).to(dev)
-    x, scales = inp["x"], inp["scales"]
-    r = mx.empty_routing(T, k, E, dev, row_align=w.row_align, blockscale=w.blockscale)
-    cap = r["input_permutation"].numel()
-    xd = torch.empty((cap, H), dtype=x.dtype, device=dev)
-    sd = torch.empty((cap, scales.shape[1]), dtype=torch.float32, device=dev) \
-        if scales is not None else None
-    y = expert_output(w, cap, dev)
-    odt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[w.out_dtype]
-    out = torch.empty((T, H), dtype=odt, device=dev)
-    stream = torch.cuda.current_stream(dev)
+    flush = Flusher(dev)
+    results = []
+    for i, w in enumerate(ws):
+        print(f"bench: {w.name} ...", file=sys.stderr, flush=True)
+        results.append(measure(w, args, dev, flush, extras if i == 0 else ()))
+    head, w = results[0], ws[0]
+    del flush
+    torch.cuda.empty_cache()
 
-    def prepare():
-        mx.prepare_moe_input(ids, r["expert_offsets"], r["problem_sizes1"], r["problem_sizes2"],
-                             r["input_permutation"], r["output_permutation"], E, 2048, H,
-                             r["blockscale_offsets"], row_align=w.row_align,
-                             workspace=r["workspace"])
-
-    def dispatch(kernel_events=None):
-        mx.dispatch_rows(x, r["output_permutation"], k, xd, scales, sd,
-                         kernel_events=kernel_events)
-
-    def combine(kernel_events=None):
-        mx.apply_shuffle_mul_sum(y, out, r["output_permutation"], weights,
-                                 kernel_events=kernel_events)
-
-    def zero_padding():
-        mx.zero_padding_rows(xd, r["input_permutation"], r["expert_offsets"])
-
-    def output_memset():
-        mx.moe_output_memset(out, r["output_permutation"], k)
-
-    sort_tile = max(w.row_align, 1)
-    sort_out = {}
-    sort_ws = torch.empty(max(mx.prepare_workspace_size(T, k, E), 4), dtype=torch.uint8,
-                          device=dev)
-
-    def moe_sort():
-        sort_out.update(mx.moe_sort(ids, E, 0, E, sort_tile, out=sort_out or None,
-                                    workspace=sort_ws))
-
-    extras = [e for e in args.extras.split(",") if e]
-    xq = sq = None
-    if "quantize_dispatch" in extras:
-        if x.dtype != torch.bfloat16 or H % 128:
-            raise SystemExit("quantize_dispatch needs a bf16 workload with hidden % 128 == 0")
-        xq = torch.empty((cap, H), dtype=torch.float8_e4m3fn, device=dev)
-        sq = torch.empty((cap, H // 128), dtype=torch.float32, device=dev)
-
-    def quantize_dispatch():
-        mx.dispatch_rows_fp8(x, r["output_permutation"], k, xq, sq)
-
-    known = {"zero_padding": zero_padding, "output_memset": output_memset, "moe_sort": moe_sort,
-             "quantize_dispatch": quantize_dispatch}
-    for e in extras:
-        if e not in known:
-            raise SystemExit(f"unknown --with stage {e!r}; known: {sorted(known)}")
-    stages = [("prepare", prepare)]
-    if "moe_sort" in extras:
-        stages.append(("moe_sort", moe_sort))
-    stages.append(("dispatch", dispatch))
-    if "quantize_dispatch" in extras:
-        stages.append(("quantize_dispatch", quantize_dispatch))
-    if "zero_padding" in extras:
-        stages.append(("zero_padding", zero_padding))
-    if "output_memset" in extras:
-        stages.append(("output_memset", output_memset))
-    stages.append(("combine", combine))
-    stages = tuple(stages)
-    for _ in range(args.warmup):
-        for _, fn in stages:
-            fn()
-    torch.cuda.synchronize()
-
-    K = args.steps
-    graph = None
-    if args.graph:
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for _, fn in stages:
-                fn()
-        for _ in range(args.warmup):
-            graph.replay()
-        torch.cuda.synchronize()
-    # Headline: exactly K steps between two device synchronisations.
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    if graph is not None:
-        for _ in range(K):
-            graph.replay()
-    else:
-        for _ in range(K):
-            for _, fn in stages:
-                fn()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-
-    # Per-stage and per-kernel durations: a second pass of K steps (kept out of
-    # the headline pass, since each event record adds a few microseconds
-    # between kernels).  HIP events are recorded on the launch stream around
-    # every stage; dispatch and combine also record a pair of events with
-    # their kernels' own begin and end timestamps (the timed entry points).
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
-          for _ in range(K)]
-    kev = {name: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                  for _ in range(K)] for name in ("dispatch", "combine")}
-    for pairs in kev.values():
-        for a, b in pairs:                  # torch creates an event's HIP handle at its first record
-            a.record(stream)
-            b.record(stream)
-    torch.cuda.synchronize()
-    for s in range(K):
-        ev[s][0].record(stream)
-        for i, (name, fn) in enumerate(stages):
-            if name in kev:
-                fn(kernel_events=kev[name][s])
-            else:
-                fn()
-            ev[s][i + 1].record(stream)
-    torch.cuda.synchronize()
-    kernel_ms = {}
-    for name, pairs in kev.items():
-        ts = np.array([a.elapsed_time(b) for a, b in pairs])
-        kernel_ms[name] = {"mean": float(ts.mean()), "p50": float(np.percentile(ts, 50)),
-                           "p90": float(np.percentile(ts, 90)), "min": float(ts.min())}
-
-    stage_ms = {}
-    for i, (name, _) in enumerate(stages):
-        ts = np.array([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(K)])
-        stage_ms[name] = {"mean": float(ts.mean()), "p50": float(np.percentile(ts, 50)),
-                          "p90": float(np.percentile(ts, 90)), "p99": float(np.percentile(ts, 99)),
-                          "min": float(ts.min())}
-    counts = r["problem_sizes1"][:, 0].cpu().numpy()
-    n_valid = int(counts.sum())
-    nbytes = algorithmic_bytes(w, n_valid, cap, ids.element_size())
-    row_b = H * x.element_size()
-    extra_report = {}
-    if "zero_padding" in extras:
-        padded = int(r["expert_offsets"][-1].item())
-        nbytes["zero_padding"] = (padded - n_valid) * row_b + cap * 4
-    if "output_memset" in extras:
-        has_pick = (r["output_permutation"].view(T, k) >= 0).any(dim=1).sum().item()
-        nbytes["output_memset"] = int(has_pick) * H * out.element_size() + T * k * 4
-    if "quantize_dispatch" in extras:
-        nbytes["quantize_dispatch"] = T * H * 2 + n_valid * (H + H // 128 * 4) + T * k * 4
-    if "moe_sort" in extras:
-        scap = sort_out["permuted_idx_to_expanded_idx"].numel()
-        nbytes["moe_sort"] = (T * k * ids.element_size() + T * k * 4 + scap * 4
-                              + 2 * 4 * sort_out["tile_idx_to_group_idx"].numel() + 4 * (E + 3))
-    for e in extras:
-        gbps = nbytes[e] / (stage_ms[e]["mean"] * 1e-3) / 1e9
-        extra_report[e] = {"ms": stage_ms[e]["mean"], "algorithmic_bytes": nbytes[e],
-                           "achieved_gbps": gbps, "frac": gbps / HBM_PEAK_GBPS}
-    dom = max(("dispatch", "combine"), key=lambda n: kernel_ms[n]["mean"])
-    kernel_name = {"dispatch": "dispatch_rows_kernel", "combine": "combine_vec_kernel"}[dom]
-    achieved = nbytes[dom] / (kernel_ms[dom]["mean"] * 1e-3) / 1e9
+    cold = head["cold"]
+    dom = cold["dominant_stage"]
+    kernel_name = KERNEL_NAMES[dom]
+    kms = cold["dispatch_kernel_ms" if dom == "dispatch" else "combine_ms"]["mean"]
+    achieved = head["algorithmic_bytes"][dom] / (kms * 1e-3) / 1e9
     traffic = load_traffic(w.name, kernel_name)
-    step_bytes = sum(nbytes.values())
-    ms_per_step = elapsed / K * 1e3
-    value = T * K / elapsed
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, inp, x, y, args.cpu_seconds)
+        print("bench: cpu baseline ...", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w, args.cpu_seconds, dev)
 
+    def brief(r):
+        c, wm = r["cold"], r["warm"]
+        b = {"step_ms_cold": c["step_ms"], "tokens_per_s_cold": c["tokens_per_s"],
+             "step_frac_cold": c["step_frac"], "step_ms_warm": wm["step_ms"],
+             "tokens_per_s_warm": wm["tokens_per_s"], "step_frac_warm": wm["step_frac"],
+             "dominant_kernel": c["dominant_kernel"],
+             "dominant_kernel_frac_cold": c["dominant_kernel_frac"],
+             "dominant_kernel_frac_warm": r["warm_timed"]["dominant_kernel_frac"],
+             "row_kernels_frac_cold": c["row_kernels_frac"],
+             "row_kernels_frac_warm": r["warm_timed"]["row_kernels_frac"]}
+        if "gate_70pct" in r:
+            b["gate_70pct"] = r["gate_70pct"]
+        if "warm_graph" in r:
+            b["step_ms_warm_graph"] = r["warm_graph"]["step_ms"]
+        return b
+
+    for r in results:
+        r.pop("_cap", None)
     line = {
         "metric": METRIC,
-        "value": value,
+        "value": cold["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": K,
+        "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": cold["step_ms"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": {"fp8": "fp8-e4m3 rows, bf16 combine"}.get(w.x_dtype, w.x_dtype),
         "data": "synthetic",
-        "config": {"workload": w.name, "T": T, "H": H, "E": E, "topk": k, "routing": w.mode,
-                   "row_align": w.row_align, "x_dtype": w.x_dtype, "out_dtype": w.out_dtype,
-                   "launch": "hip_graph" if graph is not None else "eager"},
+        "config": {"workload": w.name, "T": w.T, "H": w.H, "E": w.E, "topk": w.k,
+                   "routing": w.mode, "row_align": w.row_align, "x_dtype": w.x_dtype,
+                   "out_dtype": w.out_dtype, "launch": "eager",
+                   "cache": "cold (value, ms_per_step); warm beside it",
+                   "repetitions": REPS},
         "roofline": {"bound": "hbm", "kernel": kernel_name, "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic["traffic_bytes"] if traffic else None,
-                     "traffic_detail": traffic, "bytes_per_launch": nbytes[dom],
-                     "avg_launch_ms": kernel_ms[dom]["mean"],
+                     "traffic_meaning": "bytes between the L2s and the fabric (FETCH_SIZE + "
+                                        "WRITE_SIZE, calibrated); Infinity Cache hits count "
+                                        "too, so these are not HBM bytes",
+                     "traffic_detail": traffic,
+                     "bytes_per_launch": head["algorithmic_bytes"][dom],
+                     "avg_launch_ms": kms,
                      "avg_launch_ms_source": "HIP events recorded with the kernel's own begin "
-                                             "and end timestamps (hipExtLaunchKernel)",
-                     "avg_stage_ms_events_between_launches": stage_ms[dom]["mean"]},
+                                             "and end timestamps (hipExtLaunchKernel), cold steps"},
         "cpu_baseline": cpu,
-        "stages_ms": stage_ms,
-        "kernels_ms": kernel_ms,
-        "extras": extra_report or None,
-        "algorithmic_bytes": nbytes,
-        "step_hbm_gbps": step_bytes / (ms_per_step * 1e-3) / 1e9,
-        "step_frac_of_peak": step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-        "expert_load": {"max": int(counts.max()), "min": int(counts.min()),
-                        "mean": float(counts.mean()),
-                        "imbalance_ratio": float(counts.max() / max(counts.mean(), 1e-9))},
+        "warm": {"ms_per_step": head["warm"]["step_ms"],
+                 "tokens_per_s": head["warm"]["tokens_per_s"],
+                 "step_frac_of_peak": head["warm"]["step_frac"]},
+        "step_frac_of_peak": cold["step_frac"],
+        "headline": head,
+        "workloads": {r["workload"]: brief(r) for r in results},
+        "workload_detail": {r["workload"]: r for r in results[1:]},
         "kernel_source_hash": kernel_source_hash(),
     }
     print(json.dumps(line), flush=True)

@@ -11,6 +11,11 @@ kernels" (section "Changes"): ``prepare_moe_input`` (routing metadata),
 ``shuffle_rows`` (row gather), ``apply_shuffle_mul_sum`` (gather, scale,
 fp32 sum); ``dispatch_rows`` is the token-major form of the row gather.
 Outputs are written in place, as the page's custom-op registration marks.
+
+``bind(fn, *args, **kwargs)`` runs the checks and the marshalling of one call
+once and returns a ``BoundCall``; calling that enqueues the same work again
+with no Python-side checks, for small batches where a call is bound by host
+time.
 """
 
 from __future__ import annotations
@@ -25,7 +30,7 @@ __all__ = [
     "prepare_moe_input", "shuffle_rows", "dispatch_rows", "apply_shuffle_mul_sum",
     "moe_output_memset", "zero_padding_rows", "moe_sort", "dispatch_rows_fp8",
     "dispatch_capacity", "prepare_workspace_size", "empty_routing", "MxError",
-    "library_path", "load_library", "EXPORTED_SYMBOLS",
+    "library_path", "load_library", "EXPORTED_SYMBOLS", "bind", "BoundCall",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -41,7 +46,7 @@ EXPORTED_SYMBOLS = (
     "mx_prepare_workspace_size", "mx_prepare_moe_input", "mx_shuffle_rows",
     "mx_dispatch_rows", "mx_apply_shuffle_mul_sum", "mx_moe_output_memset",
     "mx_zero_padding_rows", "mx_moe_sort", "mx_dispatch_rows_fp8",
-    "mx_dispatch_rows_timed", "mx_apply_shuffle_mul_sum_timed",
+    "mx_dispatch_rows_timed", "mx_apply_shuffle_mul_sum_timed", "mx_prepare_moe_input_timed",
 )
 
 
@@ -84,6 +89,10 @@ def load_library():
     lib.mx_prepare_moe_input.argtypes = [
         vp, i32, i64, i32, i32, i32, i32, i32, i32, i32,
         vp, vp, vp, vp, i64, vp, vp, i32, vp, sz, vp]
+    lib.mx_prepare_moe_input_timed.restype = ctypes.c_int
+    lib.mx_prepare_moe_input_timed.argtypes = [
+        vp, i32, i64, i32, i32, i32, i32, i32, i32, i32,
+        vp, vp, vp, vp, i64, vp, vp, i32, vp, sz, vp, vp, vp]
     lib.mx_shuffle_rows.restype = ctypes.c_int
     lib.mx_shuffle_rows.argtypes = [vp, i64, i64, vp, i64, vp, vp]
     lib.mx_dispatch_rows.restype = ctypes.c_int
@@ -166,6 +175,69 @@ def _call(status: int, what: str):
         raise MxError(status, what)
 
 
+class BoundCall:
+    """One call of a C entry point whose arguments were checked and marshalled
+    once (see ``bind``).  Calling it enqueues the same work on the tensors'
+    device's current stream.  It holds the tensors it points to, so they stay
+    allocated while it lives; it does not see later changes to them (resizing
+    or replacing a tensor needs a new bind).
+
+    ``result`` is what the plain call returns (e.g. the output tensor).
+    ``bound(kernel_events=(start, stop))`` uses the timed entry point, where
+    the call has one."""
+
+    __slots__ = ("_fn", "_timed", "_args", "_dev", "_what", "result", "_keep")
+
+    def __init__(self, name: str, timed: str | None, args: tuple, dev: torch.device, what: str,
+                 result, keep: tuple):
+        lib = load_library()
+        fn = getattr(lib, name)
+        # pre-built ctypes objects pass through the argument conversion as they are
+        self._args = tuple(t(a) if not isinstance(a, t) else a
+                           for t, a in zip(fn.argtypes, args))
+        self._fn = fn
+        self._timed = getattr(lib, timed) if timed else None
+        self._dev = dev
+        self._what = what
+        self.result = result
+        self._keep = keep
+
+    def __call__(self, kernel_events=None):
+        dev = self._dev
+        if kernel_events is None:
+            st = _on(dev, self._fn, *self._args)
+        else:
+            if self._timed is None:
+                raise ValueError(f"{self._what} has no timed form")
+            st = _on(dev, self._timed, *self._args, *_event_handles(kernel_events))
+        if st != 0:
+            raise MxError(st, self._what)
+        return self.result
+
+
+def bind(fn, *args, **kwargs) -> BoundCall:
+    """Check and marshal ``fn(*args, **kwargs)`` (one of this module's calls)
+    once and return a ``BoundCall`` that repeats it without the checks."""
+    bindable = (prepare_moe_input, shuffle_rows, dispatch_rows, apply_shuffle_mul_sum,
+                moe_output_memset, zero_padding_rows, dispatch_rows_fp8)
+    if fn not in bindable:
+        raise TypeError(f"cannot bind {getattr(fn, '__name__', fn)!r}")
+    return fn(*args, _bind=True, **kwargs)
+
+
+def _finish(dev: torch.device, name: str, args: tuple, what: str, bind_: bool, result=None,
+            keep: tuple = (), timed: str | None = None, kernel_events=None):
+    """Run (or, with bind_, bind) the entry point ``name`` on checked args."""
+    if bind_:
+        return BoundCall(name, timed, args, dev, what, result, keep)
+    lib = load_library()
+    if kernel_events is None:
+        _call(_on(dev, getattr(lib, name), *args), what)
+    else:
+        _call(_on(dev, getattr(lib, timed), *args, *_event_handles(kernel_events)), what)
+    return result
+
+
 def _event_handles(kernel_events):
     """Raw hipEvent_t handles of a (start, stop) pair of torch.cuda.Event
     (created with enable_timing=True), for the timed entry points.  torch
@@ -220,13 +292,18 @@ def prepare_moe_input(topk_ids: torch.Tensor, expert_offsets: torch.Tensor,
                       num_experts: int, n: int, k: int,
                       blockscale_offsets: torch.Tensor | None = None, *,
                       row_align: int = 1, blockscale_align: int = 128,
-                      workspace: torch.Tensor | None = None) -> None:
+                      workspace: torch.Tensor | None = None, kernel_events=None,
+                      _bind: bool = False):
     """Routing metadata for ``topk_ids`` [T, topk] (int32 or int64), in place.
 
     ``n`` and ``k`` are the expert MLP's intermediate and hidden sizes; the
     problem sizes are (count, 2n, k) for the gate+up GEMM and (count, k, n)
     for the down GEMM.  ``input_permutation`` must hold at least
     ``dispatch_capacity(T, topk, num_experts, row_align)`` entries.
+
+    kernel_events: optional (start, stop) torch.cuda.Event pair, recorded with
+    the begin and end of the routing kernels themselves
+    (mx_prepare_moe_input_timed).
     """
     lib = load_library()
     _check_dev("topk_ids", topk_ids)
@@ -251,18 +328,20 @@ def prepare_moe_input(topk_ids: torch.Tensor, expert_offsets: torch.Tensor,
         workspace = torch.empty(max(lib.mx_prepare_workspace_size(T, topk, E), 4),
                                 dtype=torch.uint8, device=dev)
     _check_dev("workspace", workspace, dev)
-    _call(_on(
-        dev, lib.mx_prepare_moe_input,
-        _ptr(topk_ids), MX_I64 if topk_ids.dtype == torch.int64 else MX_I32, T, topk, E,
-        2 * n, k, k, n, row_align,
-        _ptr(expert_offsets), _ptr(problem_sizes1), _ptr(problem_sizes2),
-        _ptr(input_permutation), input_permutation.numel(), _ptr(output_permutation),
-        _ptr(blockscale_offsets), blockscale_align,
-        _ptr(workspace), workspace.numel()), "prepare_moe_input")
+    args = (_ptr(topk_ids), MX_I64 if topk_ids.dtype == torch.int64 else MX_I32, T, topk, E,
+            2 * n, k, k, n, row_align,
+            _ptr(expert_offsets), _ptr(problem_sizes1), _ptr(problem_sizes2),
+            _ptr(input_permutation), input_permutation.numel(), _ptr(output_permutation),
+            _ptr(blockscale_offsets), blockscale_align,
+            _ptr(workspace), workspace.numel())
+    return _finish(dev, "mx_prepare_moe_input", args, "prepare_moe_input", _bind, None,
+                   (topk_ids, expert_offsets, problem_sizes1, problem_sizes2, input_permutation,
+                    output_permutation, blockscale_offsets, workspace),
+                   "mx_prepare_moe_input_timed", kernel_events)
 
 
 def shuffle_rows(input: torch.Tensor, dst2src_map: torch.Tensor,
-                 output: torch.Tensor | None = None) -> torch.Tensor:
+                 output: torch.Tensor | None = None, _bind: bool = False) -> torch.Tensor:
     """output[r] = input[dst2src_map[r]] byte for byte (rows with an index out
     of range keep their contents).  Any dtype; row = everything past dim 0."""
     lib = load_library()
@@ -277,16 +356,17 @@ def shuffle_rows(input: torch.Tensor, dst2src_map: torch.Tensor,
     if output.dtype != input.dtype or output.shape[1:] != input.shape[1:] or len(output) != n_dst:
         raise ValueError("output must be [len(dst2src_map), *input.shape[1:]] of input's dtype")
     row_bytes = _row_bytes(input)
-    if n_dst:
-        _call(_on(dev, lib.mx_shuffle_rows, _ptr(input), input.shape[0], row_bytes,
-                  _ptr(dst2src_map), n_dst, _ptr(output)), "shuffle_rows")
-    return output
+    if not n_dst and not _bind:
+        return output
+    args = (_ptr(input), input.shape[0], row_bytes, _ptr(dst2src_map), n_dst, _ptr(output))
+    return _finish(dev, "mx_shuffle_rows", args, "shuffle_rows", _bind, output,
+                   (input, dst2src_map, output))
 
 
 def dispatch_rows(input: torch.Tensor, output_permutation: torch.Tensor, topk: int,
                   output: torch.Tensor, side_input: torch.Tensor | None = None,
                   side_output: torch.Tensor | None = None,
-                  kernel_events=None) -> torch.Tensor:
+                  kernel_events=None, _bind: bool = False) -> torch.Tensor:
     """output[output_permutation[t*topk + j]] = input[t] for every token t and
     pick j (destinations out of range are skipped); optionally the same for
     a side row per token (e.g. FP8 block scales).
@@ -312,20 +392,18 @@ def dispatch_rows(input: torch.Tensor, output_permutation: torch.Tensor, topk: i
             raise ValueError("side rows must match the main rows' counts and each other's shape")
         side_rb = _row_bytes(side_input)
     T = input.shape[0]
-    if T and output.shape[0]:
-        args = (_ptr(input), T, topk, _row_bytes(input), _ptr(output_permutation), _ptr(output),
-                output.shape[0], _ptr(side_input), side_rb, _ptr(side_output))
-        if kernel_events is None:
-            _call(_on(dev, lib.mx_dispatch_rows, *args), "dispatch_rows")
-        else:
-            _call(_on(dev, lib.mx_dispatch_rows_timed, *args, *_event_handles(kernel_events)),
-                  "dispatch_rows")
-    return output
+    if not (T and output.shape[0]) and not _bind:
+        return output
+    args = (_ptr(input), T, topk, _row_bytes(input), _ptr(output_permutation), _ptr(output),
+            output.shape[0], _ptr(side_input), side_rb, _ptr(side_output))
+    return _finish(dev, "mx_dispatch_rows", args, "dispatch_rows", _bind, output,
+                   (input, output_permutation, output, side_input, side_output),
+                   "mx_dispatch_rows_timed", kernel_events)
 
 
 def apply_shuffle_mul_sum(input: torch.Tensor, output: torch.Tensor,
                           permutation: torch.Tensor, factors: torch.Tensor | None = None,
-                          kernel_events=None) -> None:
+                          kernel_events=None, _bind: bool = False):
     """output[t] = round(sum_j factors[t, j] * input[permutation[t*k + j]]) with
     fp32 accumulation (k = permutation.numel() // output.shape[0]); in place.
 
@@ -343,11 +421,11 @@ def apply_shuffle_mul_sum(input: torch.Tensor, output: torch.Tensor,
     if input.dim() != 2 or output.dim() != 2 or input.shape[1] != output.shape[1]:
         raise ValueError("input [rows, hidden] and output [tokens, hidden] must share hidden")
     T, H = output.shape
-    if T == 0:
-        return
-    if permutation.numel() % T:
+    if T == 0 and not _bind:
+        return None
+    if T and permutation.numel() % T:
         raise ValueError("permutation length must be a multiple of the token count")
-    topk = permutation.numel() // T
+    topk = permutation.numel() // T if T else 1
     fcode = 0
     if factors is not None:
         _check_dev("factors", factors, dev)
@@ -356,14 +434,13 @@ def apply_shuffle_mul_sum(input: torch.Tensor, output: torch.Tensor,
         fcode = _FLOAT_CODES[factors.dtype]
     args = (_ptr(input), _FLOAT_CODES[input.dtype], input.shape[0], H, _ptr(permutation),
             _ptr(factors), fcode, T, topk, _ptr(output), _FLOAT_CODES[output.dtype])
-    if kernel_events is None:
-        _call(_on(dev, lib.mx_apply_shuffle_mul_sum, *args), "apply_shuffle_mul_sum")
-    else:
-        _call(_on(dev, lib.mx_apply_shuffle_mul_sum_timed, *args,
-                  *_event_handles(kernel_events)), "apply_shuffle_mul_sum")
+    return _finish(dev, "mx_apply_shuffle_mul_sum", args, "apply_shuffle_mul_sum", _bind, None,
+                   (input, output, permutation, factors), "mx_apply_shuffle_mul_sum_timed",
+                   kernel_events)
 
 
-def moe_output_memset(output: torch.Tensor, output_permutation: torch.Tensor, topk: int) -> None:
+def moe_output_memset(output: torch.Tensor, output_permutation: torch.Tensor, topk: int,
+                      _bind: bool = False):
     """In place: output row t becomes zeros iff one of its picks has a
     permuted index >= 0; the other rows are left untouched."""
     lib = load_library()
@@ -372,13 +449,15 @@ def moe_output_memset(output: torch.Tensor, output_permutation: torch.Tensor, to
     T = output.shape[0]
     _check_dev("output_permutation", output_permutation, dev)
     _check_i32("output_permutation", output_permutation, T * topk)
-    if T:
-        _call(_on(dev, lib.mx_moe_output_memset, _ptr(output), T, topk, _row_bytes(output),
-                  _ptr(output_permutation)), "moe_output_memset")
+    if not T and not _bind:
+        return None
+    args = (_ptr(output), T, topk, _row_bytes(output), _ptr(output_permutation))
+    return _finish(dev, "mx_moe_output_memset", args, "moe_output_memset", _bind, None,
+                   (output, output_permutation))
 
 
 def zero_padding_rows(rows: torch.Tensor, input_permutation: torch.Tensor,
-                      expert_offsets: torch.Tensor | None = None) -> None:
+                      expert_offsets: torch.Tensor | None = None, _bind: bool = False):
     """In place: dispatched rows below the padded total (expert_offsets[-1],
     read on the device) whose source index is negative become zeros."""
     lib = load_library()
@@ -394,9 +473,11 @@ def zero_padding_rows(rows: torch.Tensor, input_permutation: torch.Tensor,
         _check_dev("expert_offsets", expert_offsets, dev)
         _check_i32("expert_offsets", expert_offsets)
         E = expert_offsets.numel() - 1
-    if n:
-        _call(_on(dev, lib.mx_zero_padding_rows, _ptr(rows), n, _row_bytes(rows),
-                  _ptr(input_permutation), _ptr(expert_offsets), E), "zero_padding_rows")
+    if not n and not _bind:
+        return None
+    args = (_ptr(rows), n, _row_bytes(rows), _ptr(input_permutation), _ptr(expert_offsets), E)
+    return _finish(dev, "mx_zero_padding_rows", args, "zero_padding_rows", _bind, None,
+                   (rows, input_permutation, expert_offsets))
 
 
 def moe_sort(topk_ids: torch.Tensor, num_experts: int, local_expert_offset: int,
@@ -448,7 +529,7 @@ def moe_sort(topk_ids: torch.Tensor, num_experts: int, local_expert_offset: int,
 
 
 def dispatch_rows_fp8(input: torch.Tensor, output_permutation: torch.Tensor, topk: int,
-                      output: torch.Tensor, output_scales: torch.Tensor) -> None:
+                      output: torch.Tensor, output_scales: torch.Tensor, _bind: bool = False):
     """Quantize bf16 token rows to e4m3fn in 1x128 groups (scale = amax / 448)
     and write codes and scales to each token's k dispatched rows, in place.
     output: [rows, hidden] torch.float8_e4m3fn (or uint8); output_scales:
@@ -467,7 +548,8 @@ def dispatch_rows_fp8(input: torch.Tensor, output_permutation: torch.Tensor, top
         raise ValueError("output must be [rows, hidden] of a 1-byte dtype")
     if output_scales.dtype != torch.float32 or tuple(output_scales.shape) != (output.shape[0], H // 128):
         raise ValueError("output_scales must be float32 [rows, hidden / 128]")
-    _call(_on(dev, lib.mx_dispatch_rows_fp8, _ptr(input), MX_BF16, T, topk, H,
-              _ptr(output_permutation), _ptr(output), _ptr(output_scales), output.shape[0]),
-          "dispatch_rows_fp8")
+    args = (_ptr(input), MX_BF16, T, topk, H, _ptr(output_permutation), _ptr(output),
+            _ptr(output_scales), output.shape[0])
+    return _finish(dev, "mx_dispatch_rows_fp8", args, "dispatch_rows_fp8", _bind, None,
+                   (input, output_permutation, output, output_scales))
 

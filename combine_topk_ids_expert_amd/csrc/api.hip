@@ -85,6 +85,68 @@ mx_status apply_shuffle_mul_sum(const void* y, int32_t y_dtype, int64_t num_y_ro
                                             static_cast<hipEvent_t>(stop_event)));
 }
 
+// The routing metadata call with optional start / stop events (null for the
+// plain entry point).
+mx_status prepare_moe_input(const void* topk_ids, int32_t ids_dtype, int64_t num_tokens,
+                            int32_t topk, int32_t num_experts, int32_t gemm1_n, int32_t gemm1_k,
+                            int32_t gemm2_n, int32_t gemm2_k, int32_t row_align,
+                            int32_t* expert_offsets, int32_t* problem_sizes1,
+                            int32_t* problem_sizes2, int32_t* input_permutation,
+                            int64_t input_permutation_len, int32_t* output_permutation,
+                            int32_t* blockscale_offsets, int32_t blockscale_align,
+                            void* workspace, size_t workspace_bytes, void* start_event,
+                            void* stop_event, void* stream) {
+    if (ids_dtype != MX_I32 && ids_dtype != MX_I64) return MX_ERR_UNSUPPORTED_DTYPE;
+    if (num_tokens < 0 || topk < 1 || num_experts < 1 || num_experts > MX_MAX_EXPERTS ||
+        row_align < 1)
+        return MX_ERR_INVALID_ARGUMENT;
+    const int64_t cap = mx_dispatch_capacity(num_tokens, topk, num_experts, row_align);
+    if (cap < 0) return MX_ERR_INVALID_ARGUMENT;
+    if (blockscale_offsets != nullptr) {
+        if (blockscale_align < 1) return MX_ERR_INVALID_ARGUMENT;
+        if (num_tokens * topk + (int64_t)num_experts * (blockscale_align - 1) > kMax31)
+            return MX_ERR_INVALID_ARGUMENT;
+    }
+    const int64_t n = num_tokens * topk;
+    if ((n > 0 && (topk_ids == nullptr || output_permutation == nullptr)) ||
+        expert_offsets == nullptr || (input_permutation_len > 0 && input_permutation == nullptr))
+        return MX_ERR_INVALID_ARGUMENT;
+    if (input_permutation_len < cap) return MX_ERR_CAPACITY;
+    if (input_permutation_len > kMax31) return MX_ERR_INVALID_ARGUMENT;
+    if (!aligned(topk_ids, ids_dtype == MX_I64 ? 8 : 4) || !aligned(expert_offsets, 4) ||
+        !aligned(problem_sizes1, 4) || !aligned(problem_sizes2, 4) ||
+        !aligned(input_permutation, 4) || !aligned(output_permutation, 4) ||
+        !aligned(blockscale_offsets, 4) || !aligned(workspace, 16))
+        return MX_ERR_MISALIGNED;
+    const size_t need = mxmoe::route_workspace_bytes(n, num_experts);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+        return MX_ERR_WORKSPACE_TOO_SMALL;
+
+    mxmoe::RouteArgs a{};
+    a.ids = topk_ids;
+    a.ids64 = ids_dtype == MX_I64;
+    a.num_picks = n;
+    a.topk = topk;
+    a.num_experts = num_experts;
+    a.row_align = row_align;
+    a.bs_align = blockscale_offsets ? blockscale_align : 1;
+    a.gemm[0] = gemm1_n;
+    a.gemm[1] = gemm1_k;
+    a.gemm[2] = gemm2_n;
+    a.gemm[3] = gemm2_k;
+    a.expert_offsets = expert_offsets;
+    a.problem_sizes1 = problem_sizes1;
+    a.problem_sizes2 = problem_sizes2;
+    a.blockscale_offsets = blockscale_offsets;
+    a.input_perm = input_permutation;
+    a.input_perm_len = input_permutation_len;
+    a.output_perm = output_permutation;
+    a.workspace = static_cast<int32_t*>(workspace);
+    return hip_status(mxmoe::launch_route(a, static_cast<hipStream_t>(stream),
+                                          static_cast<hipEvent_t>(start_event),
+                                          static_cast<hipEvent_t>(stop_event)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -129,53 +191,28 @@ mx_status mx_prepare_moe_input(const void* topk_ids, int32_t ids_dtype, int64_t 
                                int32_t* output_permutation,
                                int32_t* blockscale_offsets, int32_t blockscale_align,
                                void* workspace, size_t workspace_bytes, void* stream) {
-    if (ids_dtype != MX_I32 && ids_dtype != MX_I64) return MX_ERR_UNSUPPORTED_DTYPE;
-    if (num_tokens < 0 || topk < 1 || num_experts < 1 || num_experts > MX_MAX_EXPERTS ||
-        row_align < 1)
-        return MX_ERR_INVALID_ARGUMENT;
-    const int64_t cap = mx_dispatch_capacity(num_tokens, topk, num_experts, row_align);
-    if (cap < 0) return MX_ERR_INVALID_ARGUMENT;
-    if (blockscale_offsets != nullptr) {
-        if (blockscale_align < 1) return MX_ERR_INVALID_ARGUMENT;
-        if (num_tokens * topk + (int64_t)num_experts * (blockscale_align - 1) > kMax31)
-            return MX_ERR_INVALID_ARGUMENT;
-    }
-    const int64_t n = num_tokens * topk;
-    if ((n > 0 && (topk_ids == nullptr || output_permutation == nullptr)) ||
-        expert_offsets == nullptr || (input_permutation_len > 0 && input_permutation == nullptr))
-        return MX_ERR_INVALID_ARGUMENT;
-    if (input_permutation_len < cap) return MX_ERR_CAPACITY;
-    if (input_permutation_len > kMax31) return MX_ERR_INVALID_ARGUMENT;
-    if (!aligned(topk_ids, ids_dtype == MX_I64 ? 8 : 4) || !aligned(expert_offsets, 4) ||
-        !aligned(problem_sizes1, 4) || !aligned(problem_sizes2, 4) ||
-        !aligned(input_permutation, 4) || !aligned(output_permutation, 4) ||
-        !aligned(blockscale_offsets, 4) || !aligned(workspace, 4))
-        return MX_ERR_MISALIGNED;
-    const size_t need = mxmoe::route_workspace_bytes(n, num_experts);
-    if (need > 0 && (workspace == nullptr || workspace_bytes < need))
-        return MX_ERR_WORKSPACE_TOO_SMALL;
+    return prepare_moe_input(topk_ids, ids_dtype, num_tokens, topk, num_experts, gemm1_n, gemm1_k,
+                             gemm2_n, gemm2_k, row_align, expert_offsets, problem_sizes1,
+                             problem_sizes2, input_permutation, input_permutation_len,
+                             output_permutation, blockscale_offsets, blockscale_align, workspace,
+                             workspace_bytes, nullptr, nullptr, stream);
+}
 
-    mxmoe::RouteArgs a{};
-    a.ids = topk_ids;
-    a.ids64 = ids_dtype == MX_I64;
-    a.num_picks = n;
-    a.topk = topk;
-    a.num_experts = num_experts;
-    a.row_align = row_align;
-    a.bs_align = blockscale_offsets ? blockscale_align : 1;
-    a.gemm[0] = gemm1_n;
-    a.gemm[1] = gemm1_k;
-    a.gemm[2] = gemm2_n;
-    a.gemm[3] = gemm2_k;
-    a.expert_offsets = expert_offsets;
-    a.problem_sizes1 = problem_sizes1;
-    a.problem_sizes2 = problem_sizes2;
-    a.blockscale_offsets = blockscale_offsets;
-    a.input_perm = input_permutation;
-    a.input_perm_len = input_permutation_len;
-    a.output_perm = output_permutation;
-    a.workspace = static_cast<int32_t*>(workspace);
-    return hip_status(mxmoe::launch_route(a, static_cast<hipStream_t>(stream)));
+mx_status mx_prepare_moe_input_timed(const void* topk_ids, int32_t ids_dtype, int64_t num_tokens,
+                                     int32_t topk, int32_t num_experts, int32_t gemm1_n,
+                                     int32_t gemm1_k, int32_t gemm2_n, int32_t gemm2_k,
+                                     int32_t row_align, int32_t* expert_offsets,
+                                     int32_t* problem_sizes1, int32_t* problem_sizes2,
+                                     int32_t* input_permutation, int64_t input_permutation_len,
+                                     int32_t* output_permutation, int32_t* blockscale_offsets,
+                                     int32_t blockscale_align, void* workspace,
+                                     size_t workspace_bytes, void* start_event, void* stop_event,
+                                     void* stream) {
+    return prepare_moe_input(topk_ids, ids_dtype, num_tokens, topk, num_experts, gemm1_n, gemm1_k,
+                             gemm2_n, gemm2_k, row_align, expert_offsets, problem_sizes1,
+                             problem_sizes2, input_permutation, input_permutation_len,
+                             output_permutation, blockscale_offsets, blockscale_align, workspace,
+                             workspace_bytes, start_event, stop_event, stream);
 }
 
 mx_status mx_shuffle_rows(const void* src, int64_t num_src_rows, int64_t row_bytes,
@@ -292,7 +329,7 @@ mx_status mx_moe_sort(const void* topk_ids, int32_t ids_dtype, int64_t num_token
         !aligned(expanded_idx_to_permuted_idx, 4) || !aligned(permuted_idx_to_expanded_idx, 4) ||
         !aligned(tile_idx_to_group_idx, 4) || !aligned(tile_idx_to_mn_limit, 4) ||
         !aligned(total_num_padded_tokens, 4) || !aligned(num_non_exiting_tiles, 4) ||
-        !aligned(expert_offsets, 4) || !aligned(workspace, 4))
+        !aligned(expert_offsets, 4) || !aligned(workspace, 16))
         return MX_ERR_MISALIGNED;
     const size_t need = mxmoe::route_workspace_bytes(n, num_local_experts);
     if (need > 0 && (workspace == nullptr || workspace_bytes < need))

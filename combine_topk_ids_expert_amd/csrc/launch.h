@@ -36,7 +36,10 @@ struct RouteArgs {
 
 // Device workspace the routing kernels need for `num_picks` picks.
 size_t route_workspace_bytes(int64_t num_picks, int32_t num_experts);
-hipError_t launch_route(const RouteArgs& a, hipStream_t stream);
+// start_event / stop_event (either may be null) are recorded with the begin
+// of the first routing kernel and the end of the last one.
+hipError_t launch_route(const RouteArgs& a, hipStream_t stream, hipEvent_t start_event = nullptr,
+                        hipEvent_t stop_event = nullptr);
 
 hipError_t launch_shuffle_rows(const void* src, int64_t num_src_rows, int64_t row_bytes,
                                const int32_t* dst2src, int64_t num_dst_rows, void* dst,

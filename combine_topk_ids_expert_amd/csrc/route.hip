@@ -64,7 +64,10 @@ constexpr int64_t kTileQuantum = kRouteThreads; // tile sizes are multiples of t
 // the tile count is capped near kTableBudget / E, but never so low that a
 // tile passes kOneRoundTile picks (E = 1000, 32768 picks: 16 tiles, 13.7 us
 // where 64 took 19.0 us).
-constexpr int64_t kTableBudget = 16384;
+#ifndef MXMOE_TABLE_BUDGET
+#define MXMOE_TABLE_BUDGET 16384
+#endif
+constexpr int64_t kTableBudget = MXMOE_TABLE_BUDGET;
 constexpr int64_t kOneRoundTile = (int64_t)kBatch * kWave * kRouteWaves;  // 4096
 
 // Tile size of the two-launch path: the smallest multiple of kTileQuantum
@@ -531,20 +534,24 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(RouteArgs 
 int id_bits(int E) { return E <= 1 ? 0 : 32 - __builtin_clz((unsigned)(E - 1)); }
 
 template <typename IdT>
-hipError_t launch_typed(const RouteArgs& a, hipStream_t stream) {
+hipError_t launch_typed(const RouteArgs& a, hipStream_t stream, hipEvent_t start,
+                        hipEvent_t stop) {
     Shape s{a.num_picks, a.num_experts, id_bits(a.num_experts), a.topk, a.id_offset,
             a.inp_expanded};
     if (a.num_picks <= kFusedAlways ||
         (a.num_picks <= kFusedMax && a.input_perm_len <= 2 * a.num_picks)) {
-        route_fused_kernel<IdT><<<1, kRouteThreads, 0, stream>>>(a, s);
+        launch_kernel(route_fused_kernel<IdT>, dim3(1), dim3(kRouteThreads), 0, stream, start,
+                      stop, a, s);
         return hipGetLastError();
     }
     const int64_t tile = tile_picks(a.num_picks, a.num_experts);
     const int tiles = (int)((a.num_picks + tile - 1) / tile);
-    route_count_kernel<IdT><<<tiles, kRouteThreads, 0, stream>>>(a, s, tile, tiles);
+    launch_kernel(route_count_kernel<IdT>, dim3(tiles), dim3(kRouteThreads), 0, stream, start,
+                  nullptr, a, s, tile, tiles);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    route_scatter_kernel<IdT><<<tiles, kRouteThreads, 0, stream>>>(a, s, tile, tiles);
+    launch_kernel(route_scatter_kernel<IdT>, dim3(tiles), dim3(kRouteThreads), 0, stream,
+                  nullptr, stop, a, s, tile, tiles);
     return hipGetLastError();
 }
 
@@ -557,8 +564,10 @@ size_t route_workspace_bytes(int64_t num_picks, int32_t num_experts) {
     return (size_t)((tiles + 3) / 4 * 4 * (int64_t)num_experts * (int64_t)sizeof(int32_t));
 }
 
-hipError_t launch_route(const RouteArgs& a, hipStream_t stream) {
-    return a.ids64 ? launch_typed<int64_t>(a, stream) : launch_typed<int32_t>(a, stream);
+hipError_t launch_route(const RouteArgs& a, hipStream_t stream, hipEvent_t start_event,
+                        hipEvent_t stop_event) {
+    return a.ids64 ? launch_typed<int64_t>(a, stream, start_event, stop_event)
+                   : launch_typed<int32_t>(a, stream, start_event, stop_event);
 }
 
 }  // namespace mxmoe

@@ -116,8 +116,9 @@ size_t mx_prepare_workspace_size(int64_t num_tokens, int32_t topk, int32_t num_e
  * blockscale_offsets  out [E+1] int32, or NULL to skip; blockscale_align >= 1
  *                     (128 for 1x128 FP8 block scales) when given
  * workspace           device scratch of at least
- *                     mx_prepare_workspace_size(T, k, E) bytes, 4-byte
- *                     aligned; contents on entry do not matter
+ *                     mx_prepare_workspace_size(T, k, E) bytes, 16-byte
+ *                     aligned (else MX_ERR_MISALIGNED: the kernels read it
+ *                     with 16-byte loads); contents on entry do not matter
  */
 mx_status mx_prepare_moe_input(const void* topk_ids, int32_t ids_dtype, int64_t num_tokens,
                                int32_t topk, int32_t num_experts,
@@ -129,6 +130,24 @@ mx_status mx_prepare_moe_input(const void* topk_ids, int32_t ids_dtype, int64_t 
                                int32_t* output_permutation,
                                int32_t* blockscale_offsets, int32_t blockscale_align,
                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Timed form of mx_prepare_moe_input: the same arguments, checks, work and
+ * results, plus start_event / stop_event (hipEvent_t created by the caller,
+ * or NULL), recorded with the begin of the first routing kernel and the end
+ * of the last one from the kernel dispatches' own timestamps (see the timed
+ * forms of dispatch and combine below).
+ */
+mx_status mx_prepare_moe_input_timed(const void* topk_ids, int32_t ids_dtype, int64_t num_tokens,
+                                     int32_t topk, int32_t num_experts, int32_t gemm1_n,
+                                     int32_t gemm1_k, int32_t gemm2_n, int32_t gemm2_k,
+                                     int32_t row_align, int32_t* expert_offsets,
+                                     int32_t* problem_sizes1, int32_t* problem_sizes2,
+                                     int32_t* input_permutation, int64_t input_permutation_len,
+                                     int32_t* output_permutation, int32_t* blockscale_offsets,
+                                     int32_t blockscale_align, void* workspace,
+                                     size_t workspace_bytes, void* start_event, void* stop_event,
+                                     void* stream);
 
 /*
  * shuffle_rows -- dtype-agnostic row gather (sglang page, "Changes" item 2):
@@ -278,7 +297,8 @@ mx_status mx_apply_shuffle_mul_sum_timed(const void* y, int32_t y_dtype, int64_t
  * MX_ERR_CAPACITY; every entry of both arrays is written.  0 <=
  * local_expert_offset, local_expert_offset + num_local_experts <=
  * num_experts, num_local_experts <= MX_MAX_EXPERTS, tile_size >= 1.
- * workspace: mx_prepare_workspace_size(T, k, num_local_experts) bytes.
+ * workspace: mx_prepare_workspace_size(T, k, num_local_experts) bytes,
+ * 16-byte aligned.
  */
 mx_status mx_moe_sort(const void* topk_ids, int32_t ids_dtype, int64_t num_tokens, int32_t topk,
                       int32_t num_experts, int32_t local_expert_offset,

@@ -84,6 +84,23 @@ def test_prepare_rejects(lib):
     assert _prep(lib, outp=P + 1) == MISALIGNED
     assert _prep(lib, T=65536, inp_len=65536 * 8, ws=None) == WORKSPACE
     assert _prep(lib, T=65536, inp_len=65536 * 8, wsb=16) == WORKSPACE
+    # the count table is read with 16-byte loads: a 4-aligned workspace is refused
+    assert _prep(lib, T=65536, inp_len=65536 * 8, ws=P + 4) == MISALIGNED
+    assert _prep(lib, T=65536, inp_len=65536 * 8, ws=P + 8) == MISALIGNED
+
+
+def test_timed_prepare_checks_like_the_plain_call(lib):
+    def prep_timed(**kw):
+        a = dict(ids=P, dt=I32, T=64, k=8, E=256, A=1, inp_len=64 * 8, ws=P)
+        a.update(kw)
+        return lib.mx_prepare_moe_input_timed(a["ids"], a["dt"], a["T"], a["k"], a["E"],
+                                              1, 2, 3, 4, a["A"], P, P, P, P, a["inp_len"], P,
+                                              None, 128, a["ws"], 1 << 20, None, None, S)
+    assert prep_timed(dt=F32) == DTYPE
+    assert prep_timed(E=0) == INVALID
+    assert prep_timed(inp_len=64 * 8 - 1) == CAPACITY
+    assert prep_timed(ids=P + 2) == MISALIGNED
+    assert prep_timed(T=65536, inp_len=65536 * 8, ws=P + 4) == MISALIGNED
 
 
 def test_shuffle_rejects(lib):
@@ -197,6 +214,8 @@ def test_moe_sort_rejects(lib):
     assert _sort(lib, tl=P + 2) == MISALIGNED
     assert _sort(lib, T=65536, cap=65536 * 8 + 32 * 127, mt=(65536 * 8 + 32 * 127) // 128 + 1,
                  ws=None) == WORKSPACE
+    assert _sort(lib, T=65536, cap=65536 * 8 + 32 * 127, mt=(65536 * 8 + 32 * 127) // 128 + 1,
+                 ws=P + 4) == MISALIGNED
 
 
 def test_dispatch_fp8_rejects(lib):

@@ -48,3 +48,29 @@ def test_source_hash_ignores_comments_and_whitespace():
     b = "int f(int x)\n{\n\treturn x + 1;\n}"
     assert bench._code_only(a) == bench._code_only(b)
     assert bench._code_only(a) != bench._code_only(b.replace("1", "2"))
+
+
+def test_stats_and_gate():
+    s = bench.stats([1.0, 2.0, 3.0, 4.0])
+    assert s["mean"] == 2.5 and s["min"] == 1.0 and s["samples"] == 4
+    assert s["p50"] == 2.5 and s["p999"] <= 4.0
+    r = bench.rep_stats([[1.0, 3.0], [2.0, 2.0], [4.0, 4.0]])
+    assert r["rep_means"] == [2.0, 2.0, 4.0] and r["rep_spread"] == 2.0
+    assert r["mean"] == pytest.approx(8.0 / 3.0)
+    # 70% of 8 TB/s: the T = 4096 workload's 1.058 GB give about 189 us
+    w = WORKLOADS["uniform_T4096_H7168_E256_k8_pad128"]
+    assert bench.gate_ms(w, 1_057_971_200) == pytest.approx(0.18892, abs=1e-4)
+    assert bench.gate_ms(WORKLOADS["uniform_T32_H4096_E256_k8"], 10**6) is None
+    assert bench.gate_ms(WORKLOADS["zipf1.2_T16384_H4096fp8_E128_k8"], 10**9) is None
+
+
+def test_cpu_baseline_legs_on_the_host():
+    """The oracle timed on one thread and on the host's cores, on a bounded
+    sample; routing stays single-threaded, the row loops split."""
+    w = WORKLOADS["uniform_T32_H4096_E256_k8"]
+    r = bench.cpu_baseline(w, 0.2, "cpu")
+    assert r["kind"] == "oracle" and r["unit"] == "tokens/s"
+    assert r["legs"]["single_thread"]["threads"] == 1
+    assert r["cores"] == r["legs"]["all_cores"]["threads"] >= 1
+    assert r["value"] > 0 and r["single_thread_value"] > 0
+    assert r["nproc"] >= 1 and isinstance(r["cpu_model"], str)

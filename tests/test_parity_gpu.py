@@ -5,8 +5,8 @@ combine must be within rtol 1.6e-2 / atol 1e-2 (16-bit output) or rtol 1e-5
 (fp32 output), and is also expected to match bit for bit because both sides
 take the same fused multiply-add order.  Sizes span several routing tiles
 (512 to 4096 picks each) with ragged tails, rows wider than one workgroup chunk,
-and every workload's real shape at a reduced token count; the full-size
-workloads are checked on sampled outputs and whole-array properties.
+and every workload's real shape at a reduced token count; at full size every
+metadata entry, every dispatched row and every combined token is compared.
 """
 
 import numpy as np
@@ -290,11 +290,48 @@ def test_workload_end_to_end_reduced(name):
 
 
 # --------------------------------------------------------------------------
-# full sizes, launched as the benchmark launches them; sampled outputs
+# full sizes, launched as the benchmark launches them: every metadata entry,
+# every dispatched row and every combined token against the oracle
 # --------------------------------------------------------------------------
 
+def _oracle_combine_all(y, perm_all, weights, T, k, out_dtype, chunk=2048):
+    """The oracle's combine over all T tokens, in token chunks: each chunk
+    reads only the y rows its picks name (gathered on the device and copied
+    to the host, then renumbered), so the host never holds all of y.  The
+    chunks run on threads (the C oracle releases the GIL)."""
+    from concurrent.futures import ThreadPoolExecutor
+    rows = y.shape[0]
+    perm_all = perm_all.reshape(T, k)
+    outs = {}
+
+    def host_chunk(t0):
+        t1 = min(T, t0 + chunk)
+        perm = perm_all[t0:t1]
+        need = np.unique(perm[perm >= 0])
+        remap = np.full(rows, -1, np.int64)
+        remap[need] = np.arange(need.size)
+        sub_perm = np.where(perm >= 0, remap[np.maximum(perm, 0)], -1).astype(np.int32).ravel()
+        sub_y = gu.bits(y[torch.from_numpy(need).to(DEV)])
+        return t0, t1, sub_y, sub_perm
+
+    def run(args):
+        t0, t1, sub_y, sub_perm = args
+        outs[t0] = oracle.apply_shuffle_mul_sum(sub_y, gu.code(y.dtype), sub_perm,
+                                                weights[t0:t1], "f32", t1 - t0, k, out_dtype)
+
+    with ThreadPoolExecutor(max_workers=8) as pool:
+        futs = []
+        for t0 in range(0, T, chunk):
+            futs.append(pool.submit(run, host_chunk(t0)))   # device gathers stay on this thread
+            if len(futs) >= 16:
+                futs.pop(0).result()
+        for f in futs:
+            f.result()
+    return np.concatenate([outs[t0] for t0 in sorted(outs)])
+
+
 @pytest.mark.parametrize("name", sorted(WORKLOADS))
-def test_workload_full_size_sampled(name):
+def test_workload_full_size(name):
     w = WORKLOADS[name]
     _print_case("workload full", name, w.T)
     inp = build_inputs(w, DEV)
@@ -328,26 +365,84 @@ def test_workload_full_size_sampled(name):
         np.testing.assert_array_equal(gu.bits(sd[torch.from_numpy(sample).to(DEV)]),
                                       oracle.shuffle_rows(gu.bits(inp["scales"]),
                                                           inp_perm[sample]))
-    # every used row holds its source token's bytes (exact, in chunks)
+    # every used row holds its source token's bytes (exact, in chunks): with
+    # the metadata equal to the oracle's, this is the oracle's gather
     for c0 in range(0, used.size, 16384):
         idx = torch.from_numpy(used[c0:c0 + 16384]).to(DEV)
         src = torch.from_numpy(inp_perm[used[c0:c0 + 16384]].astype(np.int64)).to(DEV)
         assert torch.equal(xd[idx].view(torch.uint8), x[src].view(torch.uint8))
         if sd is not None:
             assert torch.equal(sd[idx], inp["scales"][src])
-    # combine: 64 sampled tokens through the oracle, reading only their rows
-    toks = rng.choice(T, size=min(64, T), replace=False)
-    perm = meta["output_permutation"].reshape(T, k)[toks]
-    need = np.unique(perm[perm >= 0])
-    remap = np.full(rows, -1, np.int64)
-    remap[need] = np.arange(need.size)
-    sub_perm = np.where(perm >= 0, remap[np.maximum(perm, 0)], -1).astype(np.int32).ravel()
-    sub_y = gu.bits(y[torch.from_numpy(need).to(DEV)])
-    want = oracle.apply_shuffle_mul_sum(sub_y, gu.code(y.dtype), sub_perm,
-                                        inp["weights"][toks], "f32", toks.size, k,
-                                        w.out_dtype)
-    got = gu.bits(out[torch.from_numpy(toks).to(DEV)])
+    del xd, sd
+    # combine: every token through the oracle
+    _print_case("workload full combine", name, T)
+    want = _oracle_combine_all(y, meta["output_permutation"], inp["weights"], T, k,
+                               w.out_dtype)
+    got = gu.bits(out)
+    if w.out_dtype == "f32":
+        np.testing.assert_allclose(got, want, rtol=1e-5, atol=0)
+    else:
+        wt = torch.from_numpy(want.view(np.int16)).view(odt).float().numpy()
+        np.testing.assert_allclose(out.float().cpu().numpy(), wt, rtol=1.6e-2, atol=1e-2)
     np.testing.assert_array_equal(got, want)
+
+
+def test_bound_calls_match_plain_calls():
+    """bind(): checked and marshalled once, each call of the BoundCall gives
+    the plain call's bytes (and the timed form's), on the stream current at
+    the time of the call."""
+    _print_case("bound calls", 512, 4096)
+    T, k, E, H = 512, 8, 64, 4096
+    rng = np.random.default_rng(41)
+    ids = torch.from_numpy(routing.uniform_topk(rng, T, E, k)).to(DEV)
+    x = routing.normal_rows(T, H, "bf16", seed=42, device=DEV)
+    f = torch.from_numpy(routing.softmax_weights(rng, T, k)).to(DEV)
+    outs = []
+    for use_bind in (False, True):
+        r = mx.empty_routing(T, k, E, DEV, row_align=16, blockscale=True)
+        rows = r["input_permutation"].numel()
+        xd = torch.zeros((rows, H), dtype=torch.bfloat16, device=DEV)
+        xg = torch.zeros_like(xd)
+        y = routing.normal_rows(rows, H, "bf16", seed=43, device=DEV)
+        out = torch.empty((T, H), dtype=torch.float32, device=DEV)
+        args_p = (ids, r["expert_offsets"], r["problem_sizes1"], r["problem_sizes2"],
+                  r["input_permutation"], r["output_permutation"], E, 256, H,
+                  r["blockscale_offsets"])
+        kw_p = dict(row_align=16, workspace=r["workspace"])
+        if use_bind:
+            calls = [mx.bind(mx.prepare_moe_input, *args_p, **kw_p),
+                     mx.bind(mx.dispatch_rows, x, r["output_permutation"], k, xd),
+                     mx.bind(mx.shuffle_rows, x, r["input_permutation"], xg),
+                     mx.bind(mx.apply_shuffle_mul_sum, y, out, r["output_permutation"], f)]
+            assert calls[1].result is xd and calls[2].result is xg
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):                  # the stream current at call time
+                for c in calls:
+                    c()
+            torch.cuda.current_stream().wait_stream(side)
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+            for e in evs:
+                e.record()
+            out.fill_(float("nan"))
+            calls[0](kernel_events=(evs[0], evs[1]))        # timed forms, same bytes again
+            calls[1](kernel_events=(evs[2], evs[3]))
+            calls[3](kernel_events=(evs[4], evs[5]))
+            with pytest.raises(ValueError):
+                calls[2](kernel_events=(evs[0], evs[1]))    # shuffle_rows has no timed form
+        else:
+            mx.prepare_moe_input(*args_p, **kw_p)
+            mx.dispatch_rows(x, r["output_permutation"], k, xd)
+            mx.shuffle_rows(x, r["input_permutation"], xg)
+            mx.apply_shuffle_mul_sum(y, out, r["output_permutation"], f)
+        torch.cuda.synchronize()
+        outs.append([r[key].clone() for key in ("expert_offsets", "input_permutation",
+                                                "output_permutation", "blockscale_offsets",
+                                                "problem_sizes1")] + [xd, xg, out])
+    for a, b in zip(*outs):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+    with pytest.raises(TypeError):
+        mx.bind(mx.moe_sort, ids, E, 0, E, 16)
 
 
 def test_timed_forms_match_and_time_the_kernels():
