@@ -16,21 +16,23 @@ repetitions of exactly K steps between two device synchronisations:
 
   cold  -- before every step, outside the timed interval, 512 MiB are written
            and then 1 GiB is read, which evicts the 256 MB Infinity Cache and
-           the L2s and leaves only clean lines behind; the step is timed from
-           the begin of its first kernel to the end of its last, by events
-           the timed entry points record with the kernel dispatches' own
-           timestamps.  ``value`` and ``ms_per_step`` are the cold figures.
-  warm  -- K steps back to back with the plain entry points, one event pair
-           around the K steps (the figure a pipeline that keeps the data
-           resident would see; a step's deferred write-backs land in the next
-           step, so they are counted).
-  warm_timed -- the same steps back to back through the timed entry points,
-           for per-step percentiles and the split into stages.
+           the L2s and leaves only clean lines behind; each step is timed by an
+           event pair recorded on the stream around its three calls.
+           ``value`` and ``ms_per_step`` are the cold figures.
+  warm  -- K steps back to back with one event pair around the K steps (the
+           figure a pipeline that keeps its data resident would see; a step's
+           deferred write-backs land in the next step, so they are counted);
+           per-step percentiles from a second pass with an event pair around
+           each step.
 
-Stages follow the benchmark RFC page's split: dispatch = prepare_moe_input +
-dispatch_rows (from the begin of the routing kernels to the end of the
-dispatch kernel), combine = apply_shuffle_mul_sum.  Mean over repetitions,
-the spread of the repetition means, and p50 / p90 / p99 / p999 over all steps.
+Event pairs around every step add about 3 us per step to what back-to-back
+steps take (T = 4096 on MI355X); the timed entry points, whose events carry
+the kernels' own begin and end timestamps, add more gaps between kernels, so
+they run in passes of their own and give only the kernel times: the stages
+of the benchmark RFC page, dispatch = prepare_moe_input + dispatch_rows
+kernels and combine = apply_shuffle_mul_sum's kernel.  Every pass runs 5
+repetitions; reported are the mean over repetitions, the spread of the
+repetition means, and p50 / p90 / p99 / p999 over all steps.
 
 The roofline is the dominant row kernel's algorithmic bytes per launch over
 its mean cold kernel time, against 8 TB/s.  ``cpu_baseline`` times the CPU
@@ -39,7 +41,10 @@ on the host's cores (the row loops split over threads; routing stays one
 thread, as it is defined).
 
 --graph captures one step in a HIP graph and adds a warm figure of K graph
-replays.  --copy-probe BYTES times a plain device copy instead.
+replays.  --copy-probe BYTES times a plain device copy instead.  --calibrate
+runs the two row kernels on identity maps (T = 16384 rows of 14 KiB, k = 8:
+every row read once and written once, in order), the known byte counts that
+scale the L2-to-fabric counters of the traffic figures.
 """
 
 from __future__ import annotations
@@ -98,6 +103,9 @@ def parse_args(argv=None):
                    help="wall-clock budget of each leg of the CPU-oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-probe", type=int, default=0, metavar="BYTES")
+    p.add_argument("--calibrate", action="store_true",
+                   help="run dispatch_rows and apply_shuffle_mul_sum on identity maps "
+                        "(known bytes, for counter calibration) and print them")
     p.add_argument("--graph", action="store_true",
                    help="also time K replays of a HIP graph of one step (warm)")
     p.add_argument("--with", dest="extras", default="",
@@ -374,28 +382,44 @@ def _events(n):
     return evs
 
 
-def timed_pass(step: Step, K: int, flush) -> dict:
-    """REPS repetitions of K steps through the timed entry points; with
-    ``flush`` the caches are evicted before every step, outside the timed
-    interval.  Returns per-rep lists of per-step times (ms)."""
+def steps_pass(run, K: int, flush) -> dict:
+    """REPS repetitions of K steps with an event pair around each step; with
+    ``flush`` the caches are evicted before every step, outside the pair.
+    Per-rep lists of step times (ms) and the host's clock per step."""
     import torch
-    evs = [_events(6) for _ in range(K)]
-    out = {"e2e": [], "dispatch": [], "combine": [], "prepare_kernel": [],
-           "dispatch_kernel": [], "wall_per_step": []}
+    evs = [_events(2) for _ in range(K)]
+    out = {"e2e": [], "wall_per_step": []}
     for _ in range(REPS):
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for s in range(K):
             if flush is not None:
                 flush()
+            evs[s][0].record()
+            run()
+            evs[s][1].record()
+        torch.cuda.synchronize()
+        out["wall_per_step"].append((time.perf_counter() - t0) / K * 1e3)
+        out["e2e"].append([a.elapsed_time(b) for a, b in evs])
+    return out
+
+
+def kernels_pass(step: Step, K: int, flush) -> dict:
+    """REPS repetitions of K steps through the timed entry points (caches
+    evicted before every step with ``flush``): each kernel's own duration."""
+    import torch
+    evs = [_events(6) for _ in range(K)]
+    out = {"prepare_kernel": [], "dispatch_kernel": [], "combine_kernel": []}
+    for _ in range(REPS):
+        torch.cuda.synchronize()
+        for s in range(K):
+            if flush is not None:
+                flush()
             step.run_timed(evs[s])
         torch.cuda.synchronize()
-        out["wall_per_step"].append([(time.perf_counter() - t0) / K * 1e3])
-        out["e2e"].append([e[0].elapsed_time(e[5]) for e in evs])
-        out["dispatch"].append([e[0].elapsed_time(e[3]) for e in evs])
-        out["combine"].append([e[4].elapsed_time(e[5]) for e in evs])
         out["prepare_kernel"].append([e[0].elapsed_time(e[1]) for e in evs])
         out["dispatch_kernel"].append([e[2].elapsed_time(e[3]) for e in evs])
+        out["combine_kernel"].append([e[4].elapsed_time(e[5]) for e in evs])
     return out
 
 
@@ -438,7 +462,7 @@ def extras_pass(step: Step, K: int) -> dict:
             for i, n in enumerate(names)}
 
 
-def measure(w, args, dev, flush, extras=(), with_cpu=False) -> dict:
+def measure(w, args, dev, flush, extras=()) -> dict:
     import numpy as np
     import torch
 
@@ -447,9 +471,11 @@ def measure(w, args, dev, flush, extras=(), with_cpu=False) -> dict:
     for _ in range(args.warmup):
         step.run()
     torch.cuda.synchronize()
-    cold = timed_pass(step, K, flush)
+    cold = steps_pass(step.run, K, flush)
+    cold_k = kernels_pass(step, K, flush)
     warm = warm_pass(step.run, K)
-    warm_t = timed_pass(step, K, None)
+    warm_s = steps_pass(step.run, K, None)
+    warm_k = kernels_pass(step, K, None)
     graph = None
     if args.graph:
         g = torch.cuda.CUDAGraph()
@@ -468,49 +494,56 @@ def measure(w, args, dev, flush, extras=(), with_cpu=False) -> dict:
     def flat(per_rep):
         return [v for r in per_rep for v in r]
 
-    def summary(passes: dict, label: str) -> dict:
-        e2e = stats(flat(passes["e2e"]))
-        ms = e2e["mean"]
-        kd = stats(flat(passes["dispatch_kernel"]))
-        kc = stats(flat(passes["combine"]))
+    def kernels(kp: dict) -> dict:
+        kp_ = {k: flat(v) for k, v in kp.items()}
+        kd, kc = stats(kp_["dispatch_kernel"]), stats(kp_["combine_kernel"])
         dom = "dispatch" if kd["mean"] >= kc["mean"] else "combine"
         kdom = kd if dom == "dispatch" else kc
         gbps = nbytes[dom] / (kdom["mean"] * 1e-3) / 1e9
+        return {
+            "prepare_kernel_ms": stats(kp_["prepare_kernel"]), "dispatch_kernel_ms": kd,
+            "combine_kernel_ms": kc,
+            # the RFC page's stages: dispatch = routing + row dispatch, combine
+            "dispatch_ms": stats([p + d for p, d in zip(kp_["prepare_kernel"],
+                                                        kp_["dispatch_kernel"])]),
+            "combine_ms": kc,
+            "dominant_kernel": KERNEL_NAMES[dom], "dominant_stage": dom,
+            "dominant_kernel_gbps": gbps, "dominant_kernel_frac": gbps / HBM_PEAK_GBPS,
+            "row_kernels_frac": (nbytes["dispatch"] + nbytes["combine"])
+                                / ((kd["mean"] + kc["mean"]) * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        }
+
+    def summary(steps: dict, kp: dict, label: str, mean_ms=None) -> dict:
+        e2e = stats(flat(steps["e2e"]))
+        ms = e2e["mean"] if mean_ms is None else mean_ms
         return {
             "cache": label,
             "step_ms": ms, "tokens_per_s": T / (ms * 1e-3),
             "step_gbps": step_bytes / (ms * 1e-3) / 1e9,
             "step_frac": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-            "reps": rep_stats(passes["e2e"]),
-            "e2e_ms": e2e, "dispatch_ms": stats(flat(passes["dispatch"])),
-            "combine_ms": kc,
-            "prepare_kernel_ms": stats(flat(passes["prepare_kernel"])),
-            "dispatch_kernel_ms": kd,
-            "host_wall_ms_per_step": float(np.mean(flat(passes["wall_per_step"]))),
-            "dominant_kernel": KERNEL_NAMES[dom], "dominant_stage": dom,
-            "dominant_kernel_gbps": gbps, "dominant_kernel_frac": gbps / HBM_PEAK_GBPS,
-            "row_kernels_frac": (nbytes["dispatch"] + nbytes["combine"])
-                                 / ((kd["mean"] + kc["mean"]) * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+            "e2e_ms": e2e, "e2e_reps": rep_stats(steps["e2e"]),
+            "host_wall_ms_per_step": float(np.mean(steps["wall_per_step"])),
+            **kernels(kp),
         }
 
     res = {
         "workload": w.name, "T": T, "H": w.H, "E": w.E, "topk": w.k, "routing": w.mode,
         "row_align": w.row_align, "x_dtype": w.x_dtype, "out_dtype": w.out_dtype,
         "algorithmic_bytes": nbytes, "step_bytes": step_bytes,
-        "cold": summary(cold, "cold: 512 MiB written and 1 GiB read before each step, "
-                              "outside the timed interval"),
-        "warm_timed": summary(warm_t, "warm: back to back, timed entry points"),
+        "cold": summary(cold, cold_k, "cold: 512 MiB written and 1 GiB read before each "
+                                      "step, outside the event pair around the step"),
         "expert_load": {"max": int(counts.max()), "min": int(counts.min()),
                         "mean": float(counts.mean()),
                         "imbalance_ratio": float(counts.max() / max(counts.mean(), 1e-9))},
     }
-    wm = rep_stats(warm["per_rep"])["mean"]
-    res["warm"] = {"cache": "warm: K steps back to back, plain entry points, one event pair "
-                            "around each repetition",
-                   "step_ms": wm, "tokens_per_s": T / (wm * 1e-3),
-                   "step_frac": step_bytes / (wm * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-                   "reps": rep_stats(warm["per_rep"]),
-                   "host_wall_ms_per_step": float(np.mean(warm["wall"]))}
+    wm = rep_stats(warm["per_rep"])
+    res["warm"] = summary(warm_s, warm_k, "warm: K steps back to back; step_ms from one event "
+                                          "pair around each repetition, e2e percentiles from "
+                                          "a pass with a pair around each step",
+                          mean_ms=wm["mean"])
+    res["warm"]["reps"] = wm
+    res["warm"]["host_wall_ms_per_step_back_to_back"] = float(np.mean(warm["wall"]))
+    wm = wm["mean"]
     if graph is not None:
         gm = rep_stats(graph["per_rep"])["mean"]
         res["warm_graph"] = {"step_ms": gm, "tokens_per_s": T / (gm * 1e-3),
@@ -562,6 +595,37 @@ def copy_probe(nbytes: int, steps: int) -> None:
                       "gbps_read_plus_write": 2 * nbytes / dt / 1e9}), flush=True)
 
 
+CALIBRATE_T, CALIBRATE_K, CALIBRATE_H = 16384, 8, 7168
+
+
+def calibrate(steps: int) -> None:
+    """The row kernels on identity maps: dispatch reads T rows and writes
+    token t to rows t*k .. t*k+k-1; combine reads those T*k rows once each
+    (unit weights) and writes T rows.  Prints the algorithmic bytes of each
+    launch, which the FETCH_SIZE / WRITE_SIZE counters of the same launches
+    are divided by."""
+    import torch
+    import combine_topk_ids_expert_amd as mx
+    from workloads import routing
+    T, k, H = CALIBRATE_T, CALIBRATE_K, CALIBRATE_H
+    dev = torch.device("cuda:0")
+    x = routing.normal_rows(T, H, "bf16", 7, device=dev)
+    perm = torch.arange(T * k, dtype=torch.int32, device=dev)
+    xd = torch.empty((T * k, H), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    disp = mx.bind(mx.dispatch_rows, x, perm, k, xd)
+    comb = mx.bind(mx.apply_shuffle_mul_sum, xd, out, perm)
+    for _ in range(steps):
+        disp()
+        comb()
+    torch.cuda.synchronize()
+    row = H * 2
+    print(json.dumps({"calibrate": {
+        "dispatch_rows_kernel": {"read_bytes": T * row + T * k * 4, "write_bytes": T * k * row},
+        "combine_vec_kernel": {"read_bytes": T * k * row + T * k * 4, "write_bytes": T * row},
+        "launches": steps}}), flush=True)
+
+
 def main(argv=None):
     args = parse_args(argv)
     if args.gpus != 1:
@@ -572,6 +636,9 @@ def main(argv=None):
 
     if args.copy_probe:
         copy_probe(args.copy_probe, max(args.steps, 1))
+        return
+    if args.calibrate:
+        calibrate(max(args.steps, 1))
         return
 
     from workloads import get_workload
@@ -593,7 +660,7 @@ def main(argv=None):
     cold = head["cold"]
     dom = cold["dominant_stage"]
     kernel_name = KERNEL_NAMES[dom]
-    kms = cold["dispatch_kernel_ms" if dom == "dispatch" else "combine_ms"]["mean"]
+    kms = cold["dispatch_kernel_ms" if dom == "dispatch" else "combine_kernel_ms"]["mean"]
     achieved = head["algorithmic_bytes"][dom] / (kms * 1e-3) / 1e9
     traffic = load_traffic(w.name, kernel_name)
 
@@ -609,9 +676,9 @@ def main(argv=None):
              "tokens_per_s_warm": wm["tokens_per_s"], "step_frac_warm": wm["step_frac"],
              "dominant_kernel": c["dominant_kernel"],
              "dominant_kernel_frac_cold": c["dominant_kernel_frac"],
-             "dominant_kernel_frac_warm": r["warm_timed"]["dominant_kernel_frac"],
+             "dominant_kernel_frac_warm": wm["dominant_kernel_frac"],
              "row_kernels_frac_cold": c["row_kernels_frac"],
-             "row_kernels_frac_warm": r["warm_timed"]["row_kernels_frac"]}
+             "row_kernels_frac_warm": wm["row_kernels_frac"]}
         if "gate_70pct" in r:
             b["gate_70pct"] = r["gate_70pct"]
         if "warm_graph" in r:
@@ -649,6 +716,10 @@ def main(argv=None):
                      "avg_launch_ms": kms,
                      "avg_launch_ms_source": "HIP events recorded with the kernel's own begin "
                                              "and end timestamps (hipExtLaunchKernel), cold steps"},
+        "timing_note": "value / ms_per_step: mean over 5 repetitions of K cold steps, each "
+                       "timed by an event pair around its three calls (adds about 3 us per "
+                       "step); kernel times from separate passes through the timed entry "
+                       "points",
         "cpu_baseline": cpu,
         "warm": {"ms_per_step": head["warm"]["step_ms"],
                  "tokens_per_s": head["warm"]["tokens_per_s"],
