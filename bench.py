@@ -42,9 +42,10 @@ thread, as it is defined).
 
 --graph captures one step in a HIP graph and adds a warm figure of K graph
 replays.  --copy-probe BYTES times a plain device copy instead.  --calibrate
-runs the two row kernels on identity maps (T = 16384 rows of 14 KiB, k = 8:
-every row read once and written once, in order), the known byte counts that
-scale the L2-to-fabric counters of the traffic figures.
+runs the two row kernels on identity maps (T tokens of 14 KiB rows, k = 8,
+T = 16384 unless --calibrate-tokens: every row read once and written once, in
+order), the known byte counts that scale the L2-to-fabric counters of the
+traffic figures, and a sequential-write reference for the kernel times.
 """
 
 from __future__ import annotations
@@ -106,6 +107,10 @@ def parse_args(argv=None):
     p.add_argument("--calibrate", action="store_true",
                    help="run dispatch_rows and apply_shuffle_mul_sum on identity maps "
                         "(known bytes, for counter calibration) and print them")
+    p.add_argument("--calibrate-tokens", type=int, default=16384,
+                   help="tokens of the --calibrate run (rows of 14 KiB, k = 8)")
+    p.add_argument("--calibrate-out", choices=("bf16", "f32"), default="bf16",
+                   help="combine output dtype of the --calibrate run")
     p.add_argument("--graph", action="store_true",
                    help="also time K replays of a HIP graph of one step (warm)")
     p.add_argument("--with", dest="extras", default="",
@@ -595,10 +600,10 @@ def copy_probe(nbytes: int, steps: int) -> None:
                       "gbps_read_plus_write": 2 * nbytes / dt / 1e9}), flush=True)
 
 
-CALIBRATE_T, CALIBRATE_K, CALIBRATE_H = 16384, 8, 7168
+CALIBRATE_K, CALIBRATE_H = 8, 7168
 
 
-def calibrate(steps: int) -> None:
+def calibrate(steps: int, T: int, out_dtype: str = "bf16") -> None:
     """The row kernels on identity maps: dispatch reads T rows and writes
     token t to rows t*k .. t*k+k-1; combine reads those T*k rows once each
     (unit weights) and writes T rows.  Prints the algorithmic bytes of each
@@ -607,23 +612,32 @@ def calibrate(steps: int) -> None:
     import torch
     import combine_topk_ids_expert_amd as mx
     from workloads import routing
-    T, k, H = CALIBRATE_T, CALIBRATE_K, CALIBRATE_H
+    k, H = CALIBRATE_K, CALIBRATE_H
     dev = torch.device("cuda:0")
     x = routing.normal_rows(T, H, "bf16", 7, device=dev)
     perm = torch.arange(T * k, dtype=torch.int32, device=dev)
     xd = torch.empty((T * k, H), dtype=torch.bfloat16, device=dev)
-    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    ob = 4 if out_dtype == "f32" else 2
+    out = torch.empty((T, H), dtype=torch.float32 if ob == 4 else torch.bfloat16, device=dev)
     disp = mx.bind(mx.dispatch_rows, x, perm, k, xd)
     comb = mx.bind(mx.apply_shuffle_mul_sum, xd, out, perm)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for e in evs:
+        e.record()
+    td, tc = [], []
     for _ in range(steps):
-        disp()
-        comb()
-    torch.cuda.synchronize()
+        disp(kernel_events=(evs[0], evs[1]))
+        comb(kernel_events=(evs[2], evs[3]))
+        torch.cuda.synchronize()
+        td.append(evs[0].elapsed_time(evs[1]))
+        tc.append(evs[2].elapsed_time(evs[3]))
     row = H * 2
     print(json.dumps({"calibrate": {
         "dispatch_rows_kernel": {"read_bytes": T * row + T * k * 4, "write_bytes": T * k * row},
-        "combine_vec_kernel": {"read_bytes": T * k * row + T * k * 4, "write_bytes": T * row},
-        "launches": steps}}), flush=True)
+        "combine_vec_kernel": {"read_bytes": T * k * row + T * k * 4, "write_bytes": T * H * ob},
+        "launches": steps, "tokens": T,
+        "kernel_ms": {"dispatch_rows_kernel": sorted(td)[len(td) // 2],
+                      "combine_vec_kernel": sorted(tc)[len(tc) // 2]}}}), flush=True)
 
 
 def main(argv=None):
@@ -638,7 +652,7 @@ def main(argv=None):
         copy_probe(args.copy_probe, max(args.steps, 1))
         return
     if args.calibrate:
-        calibrate(max(args.steps, 1))
+        calibrate(max(args.steps, 1), args.calibrate_tokens, args.calibrate_out)
         return
 
     from workloads import get_workload
