@@ -29,7 +29,8 @@ import torch  # loads the HIP runtime this library must share; keep before CDLL
 __all__ = [
     "prepare_moe_input", "shuffle_rows", "dispatch_rows", "apply_shuffle_mul_sum",
     "moe_output_memset", "zero_padding_rows", "moe_sort", "dispatch_rows_fp8",
-    "dispatch_capacity", "prepare_workspace_size", "empty_routing", "MxError",
+    "prepare_moe_input_noalloc", "dispatch_capacity", "prepare_workspace_size",
+    "empty_routing", "MxError",
     "library_path", "load_library", "EXPORTED_SYMBOLS", "bind", "BoundCall",
 ]
 
@@ -47,6 +48,7 @@ EXPORTED_SYMBOLS = (
     "mx_dispatch_rows", "mx_apply_shuffle_mul_sum", "mx_moe_output_memset",
     "mx_zero_padding_rows", "mx_moe_sort", "mx_dispatch_rows_fp8",
     "mx_dispatch_rows_timed", "mx_apply_shuffle_mul_sum_timed", "mx_prepare_moe_input_timed",
+    "mx_prepare_moe_input_noalloc",
 )
 
 
@@ -93,6 +95,10 @@ def load_library():
     lib.mx_prepare_moe_input_timed.argtypes = [
         vp, i32, i64, i32, i32, i32, i32, i32, i32, i32,
         vp, vp, vp, vp, i64, vp, vp, i32, vp, sz, vp, vp, vp]
+    lib.mx_prepare_moe_input_noalloc.restype = ctypes.c_int
+    lib.mx_prepare_moe_input_noalloc.argtypes = [
+        vp, i32, i64, i32, i32, i32, i32, i32, i32, i32,
+        vp, vp, vp, vp, i64, vp, vp, i32, vp]
     lib.mx_shuffle_rows.restype = ctypes.c_int
     lib.mx_shuffle_rows.argtypes = [vp, i64, i64, vp, i64, vp, vp]
     lib.mx_dispatch_rows.restype = ctypes.c_int
@@ -338,6 +344,44 @@ def prepare_moe_input(topk_ids: torch.Tensor, expert_offsets: torch.Tensor,
                    (topk_ids, expert_offsets, problem_sizes1, problem_sizes2, input_permutation,
                     output_permutation, blockscale_offsets, workspace),
                    "mx_prepare_moe_input_timed", kernel_events)
+
+
+def prepare_moe_input_noalloc(topk_ids: torch.Tensor, expert_offsets: torch.Tensor,
+                              problem_sizes1: torch.Tensor | None,
+                              problem_sizes2: torch.Tensor | None,
+                              input_permutation: torch.Tensor, output_permutation: torch.Tensor,
+                              num_experts: int, n: int, k: int,
+                              blockscale_offsets: torch.Tensor | None = None, *,
+                              row_align: int = 1, blockscale_align: int = 128) -> None:
+    """prepare_moe_input without a workspace (mx_prepare_moe_input_noalloc):
+    the routing scratch is the library's own per-GPU array, so the call
+    allocates nothing.  Calls that overlap on one GPU share that array and
+    race; calls ordered on one stream are safe."""
+    lib = load_library()
+    _check_dev("topk_ids", topk_ids)
+    dev = topk_ids.device
+    if topk_ids.dim() != 2 or topk_ids.dtype not in (torch.int32, torch.int64):
+        raise TypeError("topk_ids must be a 2-D int32 or int64 tensor")
+    T, topk = topk_ids.shape
+    E = int(num_experts)
+    for name, t, numel in [("expert_offsets", expert_offsets, E + 1),
+                           ("output_permutation", output_permutation, T * topk),
+                           ("input_permutation", input_permutation, None),
+                           ("problem_sizes1", problem_sizes1, 3 * E),
+                           ("problem_sizes2", problem_sizes2, 3 * E),
+                           ("blockscale_offsets", blockscale_offsets, E + 1)]:
+        if t is None:
+            if name in ("expert_offsets", "output_permutation", "input_permutation"):
+                raise ValueError(f"{name} is required")
+            continue
+        _check_dev(name, t, dev)
+        _check_i32(name, t, numel)
+    _call(_on(dev, lib.mx_prepare_moe_input_noalloc,
+              _ptr(topk_ids), MX_I64 if topk_ids.dtype == torch.int64 else MX_I32, T, topk, E,
+              2 * n, k, k, n, row_align,
+              _ptr(expert_offsets), _ptr(problem_sizes1), _ptr(problem_sizes2),
+              _ptr(input_permutation), input_permutation.numel(), _ptr(output_permutation),
+              _ptr(blockscale_offsets), blockscale_align), "prepare_moe_input_noalloc")
 
 
 def shuffle_rows(input: torch.Tensor, dst2src_map: torch.Tensor,

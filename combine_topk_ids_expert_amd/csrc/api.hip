@@ -3,8 +3,19 @@
 // nothing; after the launches the HIP launch status is reported.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "../../include/mxmoe.h"
 #include "launch.h"
+
+// Routing scratch of mx_prepare_moe_input_noalloc: the count table, in a
+// file-scope device array (each GPU the library runs on holds its own copy
+// until the process ends).  Host code never passes the array's name to a
+// kernel (on the host it is only a stand-in for the symbol): each device's
+// address is looked up once with hipGetSymbolAddress, with that device
+// current, and kept in g_scratch_ptr below.
+static __device__ __align__(256) int32_t scratch[MX_NOALLOC_SCRATCH_BYTES / sizeof(int32_t)];
 
 namespace {
 
@@ -29,6 +40,33 @@ int elem_bytes(int32_t dt) {
     case MX_BF16: return 2;
     default: return 0;
     }
+}
+
+constexpr size_t kScratchBytes = MX_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+// This device's address of `scratch`, looked up at the first call on the
+// device.  Returns hipSuccess and sets *ptr, or the HIP error.
+hipError_t scratch_for_current_device(void** ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mutex);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            if (p == nullptr) return hipErrorInvalidSymbol;
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *ptr = p;
+    return hipSuccess;
 }
 
 }  // namespace
@@ -95,7 +133,7 @@ mx_status prepare_moe_input(const void* topk_ids, int32_t ids_dtype, int64_t num
                             int64_t input_permutation_len, int32_t* output_permutation,
                             int32_t* blockscale_offsets, int32_t blockscale_align,
                             void* workspace, size_t workspace_bytes, void* start_event,
-                            void* stop_event, void* stream) {
+                            void* stop_event, void* stream, bool use_scratch = false) {
     if (ids_dtype != MX_I32 && ids_dtype != MX_I64) return MX_ERR_UNSUPPORTED_DTYPE;
     if (num_tokens < 0 || topk < 1 || num_experts < 1 || num_experts > MX_MAX_EXPERTS ||
         row_align < 1)
@@ -119,8 +157,16 @@ mx_status prepare_moe_input(const void* topk_ids, int32_t ids_dtype, int64_t num
         !aligned(blockscale_offsets, 4) || !aligned(workspace, 16))
         return MX_ERR_MISALIGNED;
     const size_t need = mxmoe::route_workspace_bytes(n, num_experts);
-    if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    if (use_scratch) {
+        // the library's own scratch: sizes past it are refused, nothing is allocated
+        if (need > kScratchBytes) return MX_ERR_WORKSPACE_TOO_SMALL;
+        if (need > 0) {
+            const hipError_t e = scratch_for_current_device(&workspace);
+            if (e != hipSuccess) return hip_status(e);
+        }
+    } else if (need > 0 && (workspace == nullptr || workspace_bytes < need)) {
         return MX_ERR_WORKSPACE_TOO_SMALL;
+    }
 
     mxmoe::RouteArgs a{};
     a.ids = topk_ids;
@@ -196,6 +242,22 @@ mx_status mx_prepare_moe_input(const void* topk_ids, int32_t ids_dtype, int64_t 
                              problem_sizes2, input_permutation, input_permutation_len,
                              output_permutation, blockscale_offsets, blockscale_align, workspace,
                              workspace_bytes, nullptr, nullptr, stream);
+}
+
+mx_status mx_prepare_moe_input_noalloc(const void* topk_ids, int32_t ids_dtype,
+                                       int64_t num_tokens, int32_t topk, int32_t num_experts,
+                                       int32_t gemm1_n, int32_t gemm1_k, int32_t gemm2_n,
+                                       int32_t gemm2_k, int32_t row_align,
+                                       int32_t* expert_offsets, int32_t* problem_sizes1,
+                                       int32_t* problem_sizes2, int32_t* input_permutation,
+                                       int64_t input_permutation_len,
+                                       int32_t* output_permutation, int32_t* blockscale_offsets,
+                                       int32_t blockscale_align, void* stream) {
+    return prepare_moe_input(topk_ids, ids_dtype, num_tokens, topk, num_experts, gemm1_n, gemm1_k,
+                             gemm2_n, gemm2_k, row_align, expert_offsets, problem_sizes1,
+                             problem_sizes2, input_permutation, input_permutation_len,
+                             output_permutation, blockscale_offsets, blockscale_align, nullptr,
+                             0, nullptr, nullptr, stream, true);
 }
 
 mx_status mx_prepare_moe_input_timed(const void* topk_ids, int32_t ids_dtype, int64_t num_tokens,

@@ -60,6 +60,11 @@ typedef enum mx_dtype {
 /* Largest expert count prepare_moe_input accepts. */
 #define MX_MAX_EXPERTS 1024
 
+/* Device scratch each GPU holds for mx_prepare_moe_input_noalloc: the
+ * largest routing workspace any accepted size needs (at most 128 tiles x
+ * MX_MAX_EXPERTS counts of 4 bytes). */
+#define MX_NOALLOC_SCRATCH_BYTES (512 * 1024)
+
 /* Text for a status code (static storage). */
 const char* mx_status_string(mx_status status);
 
@@ -130,6 +135,32 @@ mx_status mx_prepare_moe_input(const void* topk_ids, int32_t ids_dtype, int64_t 
                                int32_t* output_permutation,
                                int32_t* blockscale_offsets, int32_t blockscale_align,
                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * prepare_moe_input for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments, checks, work and results as
+ * mx_prepare_moe_input, without the workspace.  The routing count table
+ * lives in a device array of MX_NOALLOC_SCRATCH_BYTES that the library holds
+ * on each GPU until the process ends; its address is looked up at the first
+ * call on a device (hipGetSymbolAddress, with that device current).  The
+ * call allocates and frees nothing.  Sizes whose workspace would exceed the
+ * array return MX_ERR_WORKSPACE_TOO_SMALL (no size this call accepts does).
+ * The kernels write the whole table before reading it, so nothing needs to
+ * be cleared between calls.  Every call on one GPU shares that GPU's array:
+ * calls that overlap on one GPU (on different streams, or from different
+ * threads without ordering) race and give undefined results; calls ordered
+ * on one stream are safe.
+ */
+mx_status mx_prepare_moe_input_noalloc(const void* topk_ids, int32_t ids_dtype,
+                                       int64_t num_tokens, int32_t topk, int32_t num_experts,
+                                       int32_t gemm1_n, int32_t gemm1_k, int32_t gemm2_n,
+                                       int32_t gemm2_k, int32_t row_align,
+                                       int32_t* expert_offsets, int32_t* problem_sizes1,
+                                       int32_t* problem_sizes2, int32_t* input_permutation,
+                                       int64_t input_permutation_len,
+                                       int32_t* output_permutation, int32_t* blockscale_offsets,
+                                       int32_t blockscale_align, void* stream);
 
 /*
  * Timed form of mx_prepare_moe_input: the same arguments, checks, work and

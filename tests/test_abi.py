@@ -232,3 +232,24 @@ def test_dispatch_fp8_rejects(lib):
     assert f(P, BF16, 10, 8, 4096, P + 2, P, P, 80, S) == MISALIGNED
     assert f(P, BF16, 0, 8, 4096, P, P, P, 80, S) == OK
 
+
+
+def test_noalloc_prepare_checks_like_the_plain_call(lib):
+    """The no-alloc routing entry point refuses what the plain call refuses,
+    before any HIP call (so no device address is looked up here)."""
+    def prep_na(**kw):
+        a = dict(ids=P, dt=I32, T=64, k=8, E=256, A=1, inp_len=64 * 8)
+        a.update(kw)
+        return lib.mx_prepare_moe_input_noalloc(a["ids"], a["dt"], a["T"], a["k"], a["E"],
+                                                1, 2, 3, 4, a["A"], P, P, P, P, a["inp_len"], P,
+                                                None, 128, S)
+    assert prep_na(dt=F32) == DTYPE
+    assert prep_na(E=0) == INVALID
+    assert prep_na(E=1025) == INVALID
+    assert prep_na(inp_len=64 * 8 - 1) == CAPACITY
+    assert prep_na(ids=P + 2) == MISALIGNED
+    assert prep_na(T=2**31, k=1) == INVALID
+    # every size the call accepts fits the scratch: the largest workspace is
+    # 128 tiles x 1024 experts x 4 bytes
+    assert lib.mx_prepare_workspace_size(2**31 // 8 - 1, 8, 1024) <= 512 * 1024
+    assert lib.mx_prepare_workspace_size(65536, 8, 1024) <= 512 * 1024
