@@ -206,6 +206,7 @@ const char* mx_status_string(mx_status s) {
     case MX_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case MX_ERR_CAPACITY: return "input_permutation shorter than the dispatch capacity";
     case MX_ERR_HIP: return "HIP launch error";
+    default: break;
     }
     return "unknown status";
 }

@@ -45,7 +45,10 @@ typedef enum mx_status {
     MX_ERR_MISALIGNED = 3,        /* pointer not aligned to its element size    */
     MX_ERR_WORKSPACE_TOO_SMALL = 4,
     MX_ERR_CAPACITY = 5,          /* input_permutation shorter than capacity    */
-    MX_ERR_HIP = 6                /* a HIP launch failed                        */
+    MX_ERR_HIP = 6,               /* a HIP launch failed                        */
+    /* widens the enum's value range to every non-negative 32-bit code, so
+     * mx_status_string is defined for any code a caller passes */
+    MX_STATUS_FORCE_INT32 = 0x7fffffff
 } mx_status;
 
 typedef enum mx_dtype {
