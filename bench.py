@@ -254,15 +254,24 @@ def cpu_baseline(w, budget_s: float, dev) -> dict:
                 t.join()
 
         steps, t_total = 0, 0.0
+        stage_s = {"prepare": [], "dispatch": [], "combine": []}
         while steps == 0 or (t_total < budget_s and steps < 20):
             t0 = time.perf_counter()
             m = oracle.prepare_moe_input(ids, w.E, row_align=w.row_align)
+            t1 = time.perf_counter()
             run_split(rows_part, rows, m["input_permutation"])
+            t2 = time.perf_counter()
             run_split(comb_part, t_sample, m["output_permutation"])
-            t_total += time.perf_counter() - t0
+            t3 = time.perf_counter()
+            stage_s["prepare"].append(t1 - t0)
+            stage_s["dispatch"].append(t2 - t1)
+            stage_s["combine"].append(t3 - t2)
+            t_total += t3 - t0
             steps += 1
         legs[name] = {"value": t_sample * steps / t_total, "threads": n_threads,
-                      "sample_tokens": t_sample, "steps": steps, "seconds": t_total}
+                      "sample_tokens": t_sample, "steps": steps, "seconds": t_total,
+                      "stage_median_ms": {k: float(np.median(v)) * 1e3
+                                          for k, v in stage_s.items()}}
     allc = legs["all_cores"]
     return {"value": allc["value"], "unit": "tokens/s", "cores": allc["threads"],
             "kind": "oracle",

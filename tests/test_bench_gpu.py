@@ -1,0 +1,46 @@
+"""bench.py end to end on the GPU: one small workload through every pass,
+and the JSON line the benchmark contract asks for."""
+
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_bench_json_line_small_workload():
+    print("case: bench.py uniform_T32_H4096_E256_k8", flush=True)
+    proc = subprocess.run(
+        [sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "1", "--steps", "3",
+         "--warmup", "1", "--workload", "uniform_T32_H4096_E256_k8", "--cpu-seconds", "0.2"],
+        cwd=ROOT, capture_output=True, text=True, timeout=300)
+    assert proc.returncode == 0, proc.stderr[-3000:]
+    lines = [ln for ln in proc.stdout.splitlines() if ln.startswith("{")]
+    assert len(lines) == 1
+    d = json.loads(lines[0])
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
+                "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
+                "roofline", "cpu_baseline", "workloads"):
+        assert key in d, key
+    assert d["n_gpus"] == 1 and d["steps"] == 3 and d["warmup"] == 1
+    assert d["value"] > 0 and d["ms_per_step"] > 0
+    assert abs(d["value"] - 32 / (d["ms_per_step"] * 1e-3)) / d["value"] < 1e-6
+    r = d["roofline"]
+    assert r["bound"] == "hbm" and r["peak"] == 8000.0 and r["unit"] == "GB/s"
+    assert abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-9
+    c = d["cpu_baseline"]
+    assert c["kind"] == "oracle" and c["cores"] >= 1 and c["value"] > 0
+    assert set(c["legs"]["all_cores"]["stage_median_ms"]) == {"prepare", "dispatch", "combine"}
+    head = d["headline"]
+    for regime in ("cold", "warm"):
+        for stage in ("e2e_ms", "dispatch_ms", "combine_ms"):
+            st = head[regime][stage]
+            assert st["samples"] == 5 * 3
+            assert st["min"] <= st["p50"] <= st["p90"] <= st["p99"] <= st["p999"]
+        assert head[regime]["e2e_reps"]["reps"] == 5
+    assert d["workloads"]["uniform_T32_H4096_E256_k8"]["step_ms_cold"] == d["ms_per_step"]
