@@ -468,6 +468,18 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(RouteArgs 
     const int iters = (s.E + kRouteWaves * rpi - 1) / (kRouteWaves * rpi);
     const int sub0 = sub < q ? sub : q - 1, sub1 = sub + L < q ? sub + L : q - 1;
     constexpr int kRowBatch = kTableBatch / 2;        // two vectors per row at most
+    // Entry c of this lane's vectors holds tile g_c; it adds to the expert's
+    // total iff g_c < tiles (a row's padding columns are never written) and to
+    // this tile's prefix iff g_c < b.  Both tests depend on the lane alone, so
+    // they become masks once, outside the table loop, which then costs one
+    // AND and one add per entry and total.
+    int mtot[8], mpre[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        const int g = c < 4 ? sub * 4 + c : (sub + L) * 4 + c - 4;
+        mtot[c] = g < tiles ? -1 : 0;
+        mpre[c] = g < b ? -1 : 0;
+    }
     for (int it0 = 0; it0 < iters; it0 += kRowBatch) {
         u32x4 v0[kRowBatch], v1[kRowBatch];
 #pragma unroll
@@ -485,11 +497,18 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(RouteArgs 
             const int e = ((it0 + u) * kRouteWaves + wave) * rpi + slot;
             int tot = 0, before = 0;
 #pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                const int g = c < 4 ? sub * 4 + c : (sub + L) * 4 + c - 4;
-                const int x = g < tiles ? (int)(c < 4 ? v0[u][c] : v1[u][c - 4]) : 0;
-                tot += x;
-                before += g < b ? x : 0;
+            for (int c = 0; c < 4; ++c) {
+                const int x = (int)v0[u][c];
+                tot += x & mtot[c];
+                before += x & mpre[c];
+            }
+            if (two) {                                   // wave-uniform
+#pragma unroll
+                for (int c = 4; c < 8; ++c) {
+                    const int x = (int)v1[u][c - 4];
+                    tot += x & mtot[c];
+                    before += x & mpre[c];
+                }
             }
             tot = group_sum(tot, L);
             before = group_sum(before, L);
