@@ -20,12 +20,13 @@
 //   larger inputs, two launches:
 //     count   -- one workgroup per tile writes the tile's count of every
 //                expert to the workspace, expert-major ([E][tiles]);
-//     scatter -- every workgroup reads the whole count table (a few lanes
-//                per expert row, 16-byte loads issued together, partial sums
-//                added with DPP), scans the padded totals over experts
-//                itself, takes its tile's base per expert, recounts its tile
-//                per wave and writes both permutations; workgroup 0 writes
-//                the offsets and sizes.
+//     scatter -- every workgroup requests its tile's ids, then the whole
+//                count table (a few lanes per expert row, 16-byte loads
+//                issued together), recounts its tile per wave while the
+//                table is in flight, adds each row's partial sums with DPP,
+//                scans the padded totals over experts itself, takes its
+//                tile's base per expert and writes both permutations;
+//                workgroup 0 writes the offsets and sizes.
 #include "device_common.h"
 #include "launch.h"
 
@@ -36,7 +37,7 @@ constexpr int kRouteThreads = 512;
 constexpr int kRouteWaves = kRouteThreads / kWave;
 constexpr int kBatch = 8;                 // 64-pick groups loaded per round
 constexpr int kMaxE = 1024;
-constexpr int kTableBatch = 16;           // 16-byte count-table loads in flight per lane
+constexpr int kTableBatch = 8;            // 16-byte count-table loads in flight per lane
 
 #ifndef MXMOE_FUSED_MAX
 #define MXMOE_FUSED_MAX 2048
@@ -430,7 +431,11 @@ __global__ __launch_bounds__(kRouteThreads) void route_count_kernel(RouteArgs a,
     }
 }
 
-template <typename IdT>
+// kTwo: rows of more than 16 vectors (more than 64 tiles), two vectors per
+// lane.  A template parameter so that every table load of a batch is issued
+// unconditionally: the wait for the ids, requested before the table, can then
+// count the table loads still in flight instead of waiting for all of them.
+template <typename IdT, bool kTwo>
 __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(RouteArgs a, Shape s,
                                                                       int64_t tile, int tiles) {
     __shared__ int rows[kRouteWaves][kMaxE];
@@ -450,6 +455,9 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(RouteArgs 
     const bool one_round = w1 - w0 <= kBatch * kWave;
     IdT raw[kBatch];
     if (one_round) load_raw(ids, w0, w1, raw);
+    for (int e = tid; e < s.E; e += kRouteThreads)
+#pragma unroll
+        for (int w = 0; w < kRouteWaves; ++w) rows[w][e] = 0;
 
     // Expert totals over all tiles and this tile's prefix.  A row of the count
     // table is q = stride / 4 16-byte vectors (at most 32, since tiles <= 128).
@@ -462,17 +470,18 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(RouteArgs 
     const int q = stride / 4;
     int L = 1;
     while (L < q && L < 16) L <<= 1;
-    const bool two = q > L;                           // wave-uniform
+    constexpr bool two = kTwo;                        // q > L
     const int rpi = kWave / L;                        // rows per wave instruction
     const int lane = tid & (kWave - 1), sub = lane & (L - 1), slot = lane / L;
     const int iters = (s.E + kRouteWaves * rpi - 1) / (kRouteWaves * rpi);
     const int sub0 = sub < q ? sub : q - 1, sub1 = sub + L < q ? sub + L : q - 1;
-    constexpr int kRowBatch = kTableBatch / 2;        // two vectors per row at most
+    constexpr int kRowBatch = two ? kTableBatch / 2 : kTableBatch;   // rows per batch
     // Entry c of this lane's vectors holds tile g_c; it adds to the expert's
     // total iff g_c < tiles (a row's padding columns are never written) and to
     // this tile's prefix iff g_c < b.  Both tests depend on the lane alone, so
     // they become masks once, outside the table loop, which then costs one
     // AND and one add per entry and total.
+    int key[kBatch];
     int mtot[8], mpre[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
@@ -480,17 +489,27 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(RouteArgs 
         mtot[c] = g < tiles ? -1 : 0;
         mpre[c] = g < b ? -1 : 0;
     }
-    for (int it0 = 0; it0 < iters; it0 += kRowBatch) {
-        u32x4 v0[kRowBatch], v1[kRowBatch];
+    using Batch = u32x4[kRowBatch];
+    auto issue = [&](int it0, Batch& v0, Batch& v1) {
 #pragma unroll
         for (int u = 0; u < kRowBatch; ++u) {
             const int e = ((it0 + u) * kRouteWaves + wave) * rpi + slot;
             const u32x4* row = reinterpret_cast<const u32x4*>(
                 a.workspace + (int64_t)(e < s.E ? e : s.E - 1) * stride);
+            // Rows past the last are loaded from row E - 1 and then dropped,
+            // so the number of loads in flight does not depend on the data.
             const bool live = it0 + u < iters;           // wave-uniform
-            v0[u] = live ? row[sub0] : u32x4{0u, 0u, 0u, 0u};
-            v1[u] = live && two ? row[sub1] : u32x4{0u, 0u, 0u, 0u};
+            const u32x4 x0 = row[sub0];
+            v0[u] = live ? x0 : u32x4{0u, 0u, 0u, 0u};
+            if constexpr (two) {
+                const u32x4 x1 = row[sub1];
+                v1[u] = live ? x1 : u32x4{0u, 0u, 0u, 0u};
+            } else {
+                v1[u] = u32x4{0u, 0u, 0u, 0u};
+            }
         }
+    };
+    auto fold = [&](int it0, const Batch& v0, const Batch& v1) {
 #pragma unroll
         for (int u = 0; u < kRowBatch; ++u) {
             if (it0 + u >= iters) break;                 // wave-uniform
@@ -502,7 +521,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(RouteArgs 
                 tot += x & mtot[c];
                 before += x & mpre[c];
             }
-            if (two) {                                   // wave-uniform
+            if constexpr (two) {
 #pragma unroll
                 for (int c = 4; c < 8; ++c) {
                     const int x = (int)v1[u][c - 4];
@@ -517,17 +536,24 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(RouteArgs 
                 pre[e] = before;
             }
         }
-    }
-    for (int e = tid; e < s.E; e += kRouteThreads)
-#pragma unroll
-        for (int w = 0; w < kRouteWaves; ++w) rows[w][e] = 0;
+    };
+    Batch v0, v1;
+    issue(0, v0, v1);
+    // The tile's own count per wave needs only the ids, which were requested
+    // before the table and arrive first: it runs while the first batch of the
+    // table is still in flight.
     __syncthreads();
-    const int R = scan_experts(a, cnt, off, tmp, b == 0);
-    int key[kBatch];
     if (one_round) {
         raw_to_keys(raw, w0, w1, s.E, s.id_offset, key);
         count_keys(key, w0, w1, s, rows[wave]);
     } else count_stretch<IdT>(ids, w0, w1, s, rows[wave]);
+    fold(0, v0, v1);
+    for (int it0 = kRowBatch; it0 < iters; it0 += kRowBatch) {
+        issue(it0, v0, v1);
+        fold(it0, v0, v1);
+    }
+    __syncthreads();
+    const int R = scan_experts(a, cnt, off, tmp, b == 0);
     __syncthreads();
     for (int e = tid; e < s.E; e += kRouteThreads) {
         int run = off[e] + pre[e];
@@ -569,8 +595,9 @@ hipError_t launch_typed(const RouteArgs& a, hipStream_t stream, hipEvent_t start
                   nullptr, a, s, tile, tiles);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    launch_kernel(route_scatter_kernel<IdT>, dim3(tiles), dim3(kRouteThreads), 0, stream,
-                  nullptr, stop, a, s, tile, tiles);
+    const bool two = (tiles + 3) / 4 > 16;            // table rows of more than 16 vectors
+    launch_kernel(two ? route_scatter_kernel<IdT, true> : route_scatter_kernel<IdT, false>,
+                  dim3(tiles), dim3(kRouteThreads), 0, stream, nullptr, stop, a, s, tile, tiles);
     return hipGetLastError();
 }
 
