@@ -103,6 +103,8 @@ def parse_args(argv=None):
     p.add_argument("--cpu-seconds", type=float, default=8.0,
                    help="wall-clock budget of each leg of the CPU-oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-reference-ops", action="store_true",
+                   help="skip the PyTorch reference kernels timed over the headline's bytes")
     p.add_argument("--copy-probe", type=int, default=0, metavar="BYTES")
     p.add_argument("--calibrate", action="store_true",
                    help="run dispatch_rows and apply_shuffle_mul_sum on identity maps "
@@ -609,6 +611,58 @@ def copy_probe(nbytes: int, steps: int) -> None:
                       "gbps_read_plus_write": 2 * nbytes / dt / 1e9}), flush=True)
 
 
+def reference_ops(w, dev, steps: int = 10, reps: int = 3) -> dict:
+    """PyTorch's own kernels over the byte counts of workload ``w``, timed
+    with events on the current stream (median of ``reps`` means over
+    ``steps`` launches), as ceilings measured on the same GPU beside the
+    published 8 TB/s: the combine's bytes as a reduction over k contiguous
+    rows (bf16 in, the combine's output dtype out), a fill of a buffer the
+    size of the dispatch output (writes only) and a device copy of half of it
+    (read + write).  None of this is the library's code."""
+    import torch
+    T, k, H = w.T, w.k, w.H
+    odt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[w.out_dtype]
+    y = torch.empty((T * k, H), dtype=torch.bfloat16, device=dev).normal_()
+    out = torch.empty((T, H), dtype=odt, device=dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+    def time_op(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(reps):
+            ev[0].record()
+            for _ in range(steps):
+                fn()
+            ev[1].record()
+            torch.cuda.synchronize()
+            ms.append(ev[0].elapsed_time(ev[1]) / steps)
+        return sorted(ms)[len(ms) // 2]
+
+    res = {}
+
+    def add(name, ms, nbytes, what):
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        res[name] = {"us": ms * 1e3, "bytes": nbytes, "gbps": gbps,
+                     "frac": gbps / HBM_PEAK_GBPS, "what": what}
+
+    yv = y.view(T, k, H)
+    ms = time_op(lambda: torch.sum(yv, dim=1, dtype=odt, out=out))
+    add("sum_over_k", ms, y.numel() * 2 + out.numel() * out.element_size(),
+        "torch.sum of [T, k, H] bf16 over k into the combine's output dtype: the combine's "
+        "bytes, with a token's k rows contiguous")
+    ms = time_op(lambda: y.fill_(0.5))
+    add("fill", ms, y.numel() * 2, "torch fill_ of a buffer the size of the dispatch output")
+    half = (T * k) // 2
+    src, dst = y[:half], y[half:2 * half]
+    ms = time_op(lambda: dst.copy_(src))
+    add("copy", ms, 2 * src.numel() * 2, "torch device copy of half that buffer (read + write)")
+    del y, out, yv, src, dst
+    torch.cuda.empty_cache()
+    return res
+
+
 CALIBRATE_K, CALIBRATE_H = 8, 7168
 
 
@@ -687,6 +741,11 @@ def main(argv=None):
     achieved = head["algorithmic_bytes"][dom] / (kms * 1e-3) / 1e9
     traffic = load_traffic(w.name, kernel_name)
 
+    ref_ops = None
+    if not args.no_reference_ops:
+        print("bench: reference ops ...", file=sys.stderr, flush=True)
+        ref_ops = reference_ops(w, dev)
+
     cpu = None
     if not args.no_cpu_baseline:
         print("bench: cpu baseline ...", file=sys.stderr, flush=True)
@@ -744,6 +803,7 @@ def main(argv=None):
                        "step); kernel times from separate passes through the timed entry "
                        "points",
         "cpu_baseline": cpu,
+        "reference_ops": ref_ops,
         "warm": {"ms_per_step": head["warm"]["step_ms"],
                  "tokens_per_s": head["warm"]["tokens_per_s"],
                  "step_frac_of_peak": head["warm"]["step_frac"]},

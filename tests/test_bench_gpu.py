@@ -44,3 +44,10 @@ def test_bench_json_line_small_workload():
             assert st["min"] <= st["p50"] <= st["p90"] <= st["p99"] <= st["p999"]
         assert head[regime]["e2e_reps"]["reps"] == 5
     assert d["workloads"]["uniform_T32_H4096_E256_k8"]["step_ms_cold"] == d["ms_per_step"]
+    ref = d["reference_ops"]
+    assert set(ref) == {"sum_over_k", "fill", "copy"}
+    for name, op in ref.items():
+        assert op["us"] > 0 and op["bytes"] > 0, name
+        assert abs(op["frac"] - op["gbps"] / 8000.0) < 1e-9, name
+    # T = 32, H = 4096, k = 8: the reduction moves the combine's bytes with bf16 output
+    assert ref["sum_over_k"]["bytes"] == 32 * 8 * 4096 * 2 + 32 * 4096 * 2
