@@ -71,6 +71,10 @@ HEADLINE = "replica288_T65536_H7168_k8_f32out"
 ORDER = (HEADLINE, "uniform_T4096_H7168_E256_k8_pad128", "khot8_T8192_H7168_E256_k8",
          "zipf1.2_T16384_H4096fp8_E128_k8", "uniform_T32_H4096_E256_k8")
 REPS = 5
+# Workloads of at most this many picks also time the step with routing and
+# dispatch in one prepare_dispatch call (the library runs both in one launch
+# up to 2048 picks when the rows allow it).
+ONE_CALL_MAX_PICKS = 2048
 FLUSH_WRITE_BYTES = 512 << 20
 FLUSH_READ_BYTES = 1 << 30
 KERNEL_SOURCES = ("route.hip", "rows.hip", "combine.hip", "device_common.h")
@@ -334,6 +338,12 @@ class Step:
                                r["output_permutation"], E, 2048, H, r["blockscale_offsets"],
                                row_align=w.row_align, workspace=r["workspace"])
         self.dispatch = mx.bind(mx.dispatch_rows, x, r["output_permutation"], k, xd, scales, sd)
+        # routing and dispatch as one call (one launch where the library fuses them)
+        self.prepare_dispatch = mx.bind(
+            mx.prepare_dispatch, self.ids, r["expert_offsets"], r["problem_sizes1"],
+            r["problem_sizes2"], r["input_permutation"], r["output_permutation"], E, 2048, H, x,
+            xd, r["blockscale_offsets"], side_input=scales, side_output=sd,
+            row_align=w.row_align, workspace=r["workspace"])
         self.combine = mx.bind(mx.apply_shuffle_mul_sum, y, out, r["output_permutation"],
                                self.weights)
         self.extras = []
@@ -374,6 +384,11 @@ class Step:
         for name, fn in self.extras:
             if name in ("quantize_dispatch", "zero_padding", "output_memset"):
                 fn()
+        self.combine()
+
+    def run_one_call_dispatch(self):
+        """The step with routing and dispatch through prepare_dispatch."""
+        self.prepare_dispatch()
         self.combine()
 
     def run_timed(self, ev):
@@ -492,6 +507,10 @@ def measure(w, args, dev, flush, extras=()) -> dict:
     warm = warm_pass(step.run, K)
     warm_s = steps_pass(step.run, K, None)
     warm_k = kernels_pass(step, K, None)
+    one_call = None
+    if w.T * w.k <= ONE_CALL_MAX_PICKS:
+        one_call = (steps_pass(step.run_one_call_dispatch, K, flush),
+                    warm_pass(step.run_one_call_dispatch, K))
     graph = None
     if args.graph:
         g = torch.cuda.CUDAGraph()
@@ -560,6 +579,15 @@ def measure(w, args, dev, flush, extras=()) -> dict:
     res["warm"]["reps"] = wm
     res["warm"]["host_wall_ms_per_step_back_to_back"] = float(np.mean(warm["wall"]))
     wm = wm["mean"]
+    if one_call is not None:
+        oc = stats(flat(one_call[0]["e2e"]))["mean"]
+        ow = rep_stats(one_call[1]["per_rep"])["mean"]
+        res["one_call_dispatch"] = {
+            "what": "the same step with routing and dispatch in one prepare_dispatch call (one "
+                    "launch where the library fuses them), then combine",
+            "step_ms_cold": oc, "tokens_per_s_cold": T / (oc * 1e-3),
+            "step_ms_warm": ow, "tokens_per_s_warm": T / (ow * 1e-3),
+            "warm_reps": rep_stats(one_call[1]["per_rep"])}
     if graph is not None:
         gm = rep_stats(graph["per_rep"])["mean"]
         res["warm_graph"] = {"step_ms": gm, "tokens_per_s": T / (gm * 1e-3),
@@ -763,6 +791,9 @@ def main(argv=None):
              "row_kernels_frac_warm": wm["row_kernels_frac"]}
         if "gate_70pct" in r:
             b["gate_70pct"] = r["gate_70pct"]
+        if "one_call_dispatch" in r:
+            b["step_ms_cold_one_call_dispatch"] = r["one_call_dispatch"]["step_ms_cold"]
+            b["step_ms_warm_one_call_dispatch"] = r["one_call_dispatch"]["step_ms_warm"]
         if "warm_graph" in r:
             b["step_ms_warm_graph"] = r["warm_graph"]["step_ms"]
         return b

@@ -28,6 +28,7 @@ import torch  # loads the HIP runtime this library must share; keep before CDLL
 
 __all__ = [
     "prepare_moe_input", "shuffle_rows", "dispatch_rows", "apply_shuffle_mul_sum",
+    "prepare_dispatch",
     "moe_output_memset", "zero_padding_rows", "moe_sort", "dispatch_rows_fp8",
     "prepare_moe_input_noalloc", "dispatch_capacity", "prepare_workspace_size",
     "empty_routing", "MxError",
@@ -48,7 +49,7 @@ EXPORTED_SYMBOLS = (
     "mx_dispatch_rows", "mx_apply_shuffle_mul_sum", "mx_moe_output_memset",
     "mx_zero_padding_rows", "mx_moe_sort", "mx_dispatch_rows_fp8",
     "mx_dispatch_rows_timed", "mx_apply_shuffle_mul_sum_timed", "mx_prepare_moe_input_timed",
-    "mx_prepare_moe_input_noalloc",
+    "mx_prepare_moe_input_noalloc", "mx_prepare_dispatch",
 )
 
 
@@ -99,6 +100,11 @@ def load_library():
     lib.mx_prepare_moe_input_noalloc.argtypes = [
         vp, i32, i64, i32, i32, i32, i32, i32, i32, i32,
         vp, vp, vp, vp, i64, vp, vp, i32, vp]
+    lib.mx_prepare_dispatch.restype = ctypes.c_int
+    lib.mx_prepare_dispatch.argtypes = [
+        vp, i32, i64, i32, i32, i32, i32, i32, i32, i32,
+        vp, vp, vp, vp, i64, vp, vp, i32, vp, sz,
+        vp, i64, vp, i64, vp, i64, vp, vp]
     lib.mx_shuffle_rows.restype = ctypes.c_int
     lib.mx_shuffle_rows.argtypes = [vp, i64, i64, vp, i64, vp, vp]
     lib.mx_dispatch_rows.restype = ctypes.c_int
@@ -225,7 +231,7 @@ def bind(fn, *args, **kwargs) -> BoundCall:
     """Check and marshal ``fn(*args, **kwargs)`` (one of this module's calls)
     once and return a ``BoundCall`` that repeats it without the checks."""
     bindable = (prepare_moe_input, shuffle_rows, dispatch_rows, apply_shuffle_mul_sum,
-                moe_output_memset, zero_padding_rows, dispatch_rows_fp8)
+                moe_output_memset, zero_padding_rows, dispatch_rows_fp8, prepare_dispatch)
     if fn not in bindable:
         raise TypeError(f"cannot bind {getattr(fn, '__name__', fn)!r}")
     return fn(*args, _bind=True, **kwargs)
@@ -292,25 +298,11 @@ def empty_routing(num_tokens: int, topk: int, num_experts: int, device, row_alig
     return out
 
 
-def prepare_moe_input(topk_ids: torch.Tensor, expert_offsets: torch.Tensor,
-                      problem_sizes1: torch.Tensor | None, problem_sizes2: torch.Tensor | None,
-                      input_permutation: torch.Tensor, output_permutation: torch.Tensor,
-                      num_experts: int, n: int, k: int,
-                      blockscale_offsets: torch.Tensor | None = None, *,
-                      row_align: int = 1, blockscale_align: int = 128,
-                      workspace: torch.Tensor | None = None, kernel_events=None,
-                      _bind: bool = False):
-    """Routing metadata for ``topk_ids`` [T, topk] (int32 or int64), in place.
-
-    ``n`` and ``k`` are the expert MLP's intermediate and hidden sizes; the
-    problem sizes are (count, 2n, k) for the gate+up GEMM and (count, k, n)
-    for the down GEMM.  ``input_permutation`` must hold at least
-    ``dispatch_capacity(T, topk, num_experts, row_align)`` entries.
-
-    kernel_events: optional (start, stop) torch.cuda.Event pair, recorded with
-    the begin and end of the routing kernels themselves
-    (mx_prepare_moe_input_timed).
-    """
+def _prepare_args(topk_ids, expert_offsets, problem_sizes1, problem_sizes2, input_permutation,
+                  output_permutation, num_experts, n, k, blockscale_offsets, row_align,
+                  blockscale_align, workspace):
+    """Checked ctypes arguments of mx_prepare_moe_input (without the stream),
+    the device and the tensors they point to."""
     lib = load_library()
     _check_dev("topk_ids", topk_ids)
     dev = topk_ids.device
@@ -340,9 +332,34 @@ def prepare_moe_input(topk_ids: torch.Tensor, expert_offsets: torch.Tensor,
             _ptr(input_permutation), input_permutation.numel(), _ptr(output_permutation),
             _ptr(blockscale_offsets), blockscale_align,
             _ptr(workspace), workspace.numel())
-    return _finish(dev, "mx_prepare_moe_input", args, "prepare_moe_input", _bind, None,
-                   (topk_ids, expert_offsets, problem_sizes1, problem_sizes2, input_permutation,
-                    output_permutation, blockscale_offsets, workspace),
+    keep = (topk_ids, expert_offsets, problem_sizes1, problem_sizes2, input_permutation,
+            output_permutation, blockscale_offsets, workspace)
+    return dev, args, keep
+
+
+def prepare_moe_input(topk_ids: torch.Tensor, expert_offsets: torch.Tensor,
+                      problem_sizes1: torch.Tensor | None, problem_sizes2: torch.Tensor | None,
+                      input_permutation: torch.Tensor, output_permutation: torch.Tensor,
+                      num_experts: int, n: int, k: int,
+                      blockscale_offsets: torch.Tensor | None = None, *,
+                      row_align: int = 1, blockscale_align: int = 128,
+                      workspace: torch.Tensor | None = None, kernel_events=None,
+                      _bind: bool = False):
+    """Routing metadata for ``topk_ids`` [T, topk] (int32 or int64), in place.
+
+    ``n`` and ``k`` are the expert MLP's intermediate and hidden sizes; the
+    problem sizes are (count, 2n, k) for the gate+up GEMM and (count, k, n)
+    for the down GEMM.  ``input_permutation`` must hold at least
+    ``dispatch_capacity(T, topk, num_experts, row_align)`` entries.
+
+    kernel_events: optional (start, stop) torch.cuda.Event pair, recorded with
+    the begin and end of the routing kernels themselves
+    (mx_prepare_moe_input_timed).
+    """
+    dev, args, keep = _prepare_args(topk_ids, expert_offsets, problem_sizes1, problem_sizes2,
+                                    input_permutation, output_permutation, num_experts, n, k,
+                                    blockscale_offsets, row_align, blockscale_align, workspace)
+    return _finish(dev, "mx_prepare_moe_input", args, "prepare_moe_input", _bind, None, keep,
                    "mx_prepare_moe_input_timed", kernel_events)
 
 
@@ -407,17 +424,9 @@ def shuffle_rows(input: torch.Tensor, dst2src_map: torch.Tensor,
                    (input, dst2src_map, output))
 
 
-def dispatch_rows(input: torch.Tensor, output_permutation: torch.Tensor, topk: int,
-                  output: torch.Tensor, side_input: torch.Tensor | None = None,
-                  side_output: torch.Tensor | None = None,
-                  kernel_events=None, _bind: bool = False) -> torch.Tensor:
-    """output[output_permutation[t*topk + j]] = input[t] for every token t and
-    pick j (destinations out of range are skipped); optionally the same for
-    a side row per token (e.g. FP8 block scales).
-
-    kernel_events: optional (start, stop) torch.cuda.Event pair, recorded with
-    the begin and end of the dispatch kernels themselves (mx_dispatch_rows_timed)."""
-    lib = load_library()
+def _dispatch_args(input, output_permutation, topk, output, side_input, side_output):
+    """Checked ctypes arguments of mx_dispatch_rows (without the stream) and
+    the device."""
     _check_dev("input", input)
     dev = input.device
     _check_dev("output_permutation", output_permutation, dev)
@@ -436,13 +445,55 @@ def dispatch_rows(input: torch.Tensor, output_permutation: torch.Tensor, topk: i
             raise ValueError("side rows must match the main rows' counts and each other's shape")
         side_rb = _row_bytes(side_input)
     T = input.shape[0]
-    if not (T and output.shape[0]) and not _bind:
-        return output
     args = (_ptr(input), T, topk, _row_bytes(input), _ptr(output_permutation), _ptr(output),
             output.shape[0], _ptr(side_input), side_rb, _ptr(side_output))
+    return dev, args
+
+
+def dispatch_rows(input: torch.Tensor, output_permutation: torch.Tensor, topk: int,
+                  output: torch.Tensor, side_input: torch.Tensor | None = None,
+                  side_output: torch.Tensor | None = None,
+                  kernel_events=None, _bind: bool = False) -> torch.Tensor:
+    """output[output_permutation[t*topk + j]] = input[t] for every token t and
+    pick j (destinations out of range are skipped); optionally the same for
+    a side row per token (e.g. FP8 block scales).
+
+    kernel_events: optional (start, stop) torch.cuda.Event pair, recorded with
+    the begin and end of the dispatch kernels themselves (mx_dispatch_rows_timed)."""
+    dev, args = _dispatch_args(input, output_permutation, topk, output, side_input, side_output)
+    if not (args[1] and args[6]) and not _bind:
+        return output
     return _finish(dev, "mx_dispatch_rows", args, "dispatch_rows", _bind, output,
                    (input, output_permutation, output, side_input, side_output),
                    "mx_dispatch_rows_timed", kernel_events)
+
+
+def prepare_dispatch(topk_ids: torch.Tensor, expert_offsets: torch.Tensor,
+                     problem_sizes1: torch.Tensor | None, problem_sizes2: torch.Tensor | None,
+                     input_permutation: torch.Tensor, output_permutation: torch.Tensor,
+                     num_experts: int, n: int, k: int, input: torch.Tensor,
+                     output: torch.Tensor, blockscale_offsets: torch.Tensor | None = None, *,
+                     side_input: torch.Tensor | None = None,
+                     side_output: torch.Tensor | None = None, row_align: int = 1,
+                     blockscale_align: int = 128, workspace: torch.Tensor | None = None,
+                     _bind: bool = False) -> torch.Tensor:
+    """prepare_moe_input(...) and then dispatch_rows(input, output_permutation,
+    topk, output, side_input, side_output) in one call (mx_prepare_dispatch),
+    with the same results.  At decode-sized batches the library runs both in
+    one launch.  Returns ``output``."""
+    dev, pargs, pkeep = _prepare_args(topk_ids, expert_offsets, problem_sizes1, problem_sizes2,
+                                      input_permutation, output_permutation, num_experts, n, k,
+                                      blockscale_offsets, row_align, blockscale_align, workspace)
+    if input.shape[0] != topk_ids.shape[0]:
+        raise ValueError("input must have one row per token of topk_ids")
+    ddev, dargs = _dispatch_args(input, output_permutation, topk_ids.shape[1], output,
+                                 side_input, side_output)
+    if ddev != dev:
+        raise ValueError("input is on another device than topk_ids")
+    # mx_dispatch_rows args: src, T, topk, row_bytes, perm, dst, n_dst, side_src, side_rb, side_dst
+    args = pargs + (dargs[0], dargs[3], dargs[5], dargs[6], dargs[7], dargs[8], dargs[9])
+    return _finish(dev, "mx_prepare_dispatch", args, "prepare_dispatch", _bind, output,
+                   pkeep + (input, output, side_input, side_output))
 
 
 def apply_shuffle_mul_sum(input: torch.Tensor, output: torch.Tensor,

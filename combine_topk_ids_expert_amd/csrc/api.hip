@@ -73,12 +73,11 @@ hipError_t scratch_for_current_device(void** ptr) {
 
 namespace {
 
-// The row dispatch and the combine with optional start / stop events (null
-// for the plain entry points).
-mx_status dispatch_rows(const void* src, int64_t num_tokens, int32_t topk, int64_t row_bytes,
-                        const int32_t* output_permutation, void* dst, int64_t num_dst_rows,
-                        const void* side_src, int64_t side_row_bytes, void* side_dst,
-                        void* start_event, void* stop_event, void* stream) {
+// Argument checks of the row dispatch.
+mx_status check_dispatch(const void* src, int64_t num_tokens, int32_t topk, int64_t row_bytes,
+                         const int32_t* output_permutation, const void* dst,
+                         int64_t num_dst_rows, const void* side_src, int64_t side_row_bytes,
+                         const void* side_dst) {
     if (num_tokens < 0 || topk < 1 || row_bytes < 1 || row_bytes > kMaxRowBytes ||
         num_dst_rows < 0 || num_dst_rows > kMax31 || num_tokens > kMax31 / topk)
         return MX_ERR_INVALID_ARGUMENT;
@@ -90,6 +89,19 @@ mx_status dispatch_rows(const void* src, int64_t num_tokens, int32_t topk, int64
                            (num_dst_rows > 0 && dst == nullptr)))
         return MX_ERR_INVALID_ARGUMENT;
     if (!aligned(output_permutation, 4)) return MX_ERR_MISALIGNED;
+    return MX_OK;
+}
+
+// The row dispatch and the combine with optional start / stop events (null
+// for the plain entry points).
+mx_status dispatch_rows(const void* src, int64_t num_tokens, int32_t topk, int64_t row_bytes,
+                        const int32_t* output_permutation, void* dst, int64_t num_dst_rows,
+                        const void* side_src, int64_t side_row_bytes, void* side_dst,
+                        void* start_event, void* stop_event, void* stream) {
+    const mx_status st = check_dispatch(src, num_tokens, topk, row_bytes, output_permutation,
+                                        dst, num_dst_rows, side_src, side_row_bytes, side_dst);
+    if (st != MX_OK) return st;
+    const bool side = side_src != nullptr;
     if (num_tokens == 0 || num_dst_rows == 0) return MX_OK;
     return hip_status(mxmoe::launch_dispatch_rows(
         src, num_tokens, topk, row_bytes, output_permutation, dst, num_dst_rows,
@@ -123,8 +135,20 @@ mx_status apply_shuffle_mul_sum(const void* y, int32_t y_dtype, int64_t num_y_ro
                                             static_cast<hipEvent_t>(stop_event)));
 }
 
+// The dispatch half of prepare_dispatch (arguments already checked).
+struct RowDispatch {
+    const void* src;
+    int64_t row_bytes;
+    void* dst;
+    int64_t num_dst_rows;
+    const void* side_src;
+    int64_t side_row_bytes;
+    void* side_dst;
+};
+
 // The routing metadata call with optional start / stop events (null for the
-// plain entry point).
+// plain entry point); with `rows`, the row dispatch follows on the same
+// stream, in the same launch where route_dispatch_fusable allows.
 mx_status prepare_moe_input(const void* topk_ids, int32_t ids_dtype, int64_t num_tokens,
                             int32_t topk, int32_t num_experts, int32_t gemm1_n, int32_t gemm1_k,
                             int32_t gemm2_n, int32_t gemm2_k, int32_t row_align,
@@ -133,7 +157,8 @@ mx_status prepare_moe_input(const void* topk_ids, int32_t ids_dtype, int64_t num
                             int64_t input_permutation_len, int32_t* output_permutation,
                             int32_t* blockscale_offsets, int32_t blockscale_align,
                             void* workspace, size_t workspace_bytes, void* start_event,
-                            void* stop_event, void* stream, bool use_scratch = false) {
+                            void* stop_event, void* stream, bool use_scratch = false,
+                            const RowDispatch* rows = nullptr) {
     if (ids_dtype != MX_I32 && ids_dtype != MX_I64) return MX_ERR_UNSUPPORTED_DTYPE;
     if (num_tokens < 0 || topk < 1 || num_experts < 1 || num_experts > MX_MAX_EXPERTS ||
         row_align < 1)
@@ -188,9 +213,21 @@ mx_status prepare_moe_input(const void* topk_ids, int32_t ids_dtype, int64_t num
     a.input_perm_len = input_permutation_len;
     a.output_perm = output_permutation;
     a.workspace = static_cast<int32_t*>(workspace);
-    return hip_status(mxmoe::launch_route(a, static_cast<hipStream_t>(stream),
-                                          static_cast<hipEvent_t>(start_event),
-                                          static_cast<hipEvent_t>(stop_event)));
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (rows == nullptr)
+        return hip_status(mxmoe::launch_route(a, st, static_cast<hipEvent_t>(start_event),
+                                              static_cast<hipEvent_t>(stop_event)));
+    if (rows->num_dst_rows > 0 && rows->side_src == nullptr &&
+        mxmoe::route_dispatch_fusable(a, num_tokens, rows->row_bytes, rows->src, rows->dst))
+        return hip_status(mxmoe::launch_route_dispatch(a, num_tokens, rows->src,
+                                                       rows->row_bytes, rows->dst,
+                                                       rows->num_dst_rows, st));
+    const mx_status r = hip_status(mxmoe::launch_route(a, st));
+    if (r != MX_OK || num_tokens == 0 || rows->num_dst_rows == 0) return r;
+    return hip_status(mxmoe::launch_dispatch_rows(
+        rows->src, num_tokens, topk, rows->row_bytes, output_permutation, rows->dst,
+        rows->num_dst_rows, rows->side_src, rows->side_row_bytes, rows->side_dst, st, nullptr,
+        nullptr));
 }
 
 }  // namespace
@@ -276,6 +313,29 @@ mx_status mx_prepare_moe_input_timed(const void* topk_ids, int32_t ids_dtype, in
                              problem_sizes2, input_permutation, input_permutation_len,
                              output_permutation, blockscale_offsets, blockscale_align, workspace,
                              workspace_bytes, start_event, stop_event, stream);
+}
+
+mx_status mx_prepare_dispatch(const void* topk_ids, int32_t ids_dtype, int64_t num_tokens,
+                              int32_t topk, int32_t num_experts, int32_t gemm1_n,
+                              int32_t gemm1_k, int32_t gemm2_n, int32_t gemm2_k,
+                              int32_t row_align, int32_t* expert_offsets,
+                              int32_t* problem_sizes1, int32_t* problem_sizes2,
+                              int32_t* input_permutation, int64_t input_permutation_len,
+                              int32_t* output_permutation, int32_t* blockscale_offsets,
+                              int32_t blockscale_align, void* workspace, size_t workspace_bytes,
+                              const void* src, int64_t row_bytes, void* dst,
+                              int64_t num_dst_rows, const void* side_src,
+                              int64_t side_row_bytes, void* side_dst, void* stream) {
+    const mx_status st = check_dispatch(src, num_tokens, topk, row_bytes, output_permutation,
+                                        dst, num_dst_rows, side_src, side_row_bytes, side_dst);
+    if (st != MX_OK) return st;
+    const RowDispatch rows{src, row_bytes, dst, num_dst_rows, side_src, side_row_bytes,
+                           side_dst};
+    return prepare_moe_input(topk_ids, ids_dtype, num_tokens, topk, num_experts, gemm1_n, gemm1_k,
+                             gemm2_n, gemm2_k, row_align, expert_offsets, problem_sizes1,
+                             problem_sizes2, input_permutation, input_permutation_len,
+                             output_permutation, blockscale_offsets, blockscale_align, workspace,
+                             workspace_bytes, nullptr, nullptr, stream, false, &rows);
 }
 
 mx_status mx_shuffle_rows(const void* src, int64_t num_src_rows, int64_t row_bytes,

@@ -36,6 +36,16 @@ struct RouteArgs {
 
 // Device workspace the routing kernels need for `num_picks` picks.
 size_t route_workspace_bytes(int64_t num_picks, int32_t num_experts);
+// Whether routing and the row dispatch of `num_tokens` rows of `row_bytes`
+// can run as one launch (launch_route_dispatch): inputs the single-workgroup
+// routing takes, 16-byte row widths and bases, a bounded grid.
+bool route_dispatch_fusable(const RouteArgs& a, int64_t num_tokens, int64_t row_bytes,
+                            const void* src, const void* dst);
+// Routing metadata of `a` plus dst[output_perm[t*k+j]] = src[t] in one launch;
+// only for arguments route_dispatch_fusable accepts.
+hipError_t launch_route_dispatch(const RouteArgs& a, int64_t num_tokens, const void* src,
+                                 int64_t row_bytes, void* dst, int64_t num_dst_rows,
+                                 hipStream_t stream);
 // start_event / stop_event (either may be null) are recorded with the begin
 // of the first routing kernel and the end of the last one.
 hipError_t launch_route(const RouteArgs& a, hipStream_t stream, hipEvent_t start_event = nullptr,

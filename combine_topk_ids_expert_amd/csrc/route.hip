@@ -166,6 +166,9 @@ __device__ __forceinline__ void count_keys(const int (&key)[kBatch], int64_t g0,
 // Place a round of keys: row[e] holds the next free dispatched row of expert
 // e for this wave on entry and is advanced as picks are placed (groups past
 // w1 skipped as in count_keys).
+// kLocal: outp is the workgroup's LDS copy of the output permutation (a
+// workgroup that routes for itself only), and inp is not written.
+template <bool kLocal = false>
 __device__ __forceinline__ void scatter_keys(const int (&key)[kBatch], int64_t g0, int64_t w1,
                                              const Shape& s, int* row, int32_t* outp,
                                              int32_t* inp, int64_t inp_len) {
@@ -179,7 +182,8 @@ __device__ __forceinline__ void scatter_keys(const int (&key)[kBatch], int64_t g
         if (key[b] >= 0) {
             const int r = row[key[b]] + rank;   // every lane reads before the update below
             outp[i] = r;
-            if (r < inp_len) inp[r] = s.expanded ? (int32_t)i : (int32_t)((uint32_t)i / (uint32_t)s.k);
+            if (!kLocal && r < inp_len)
+                inp[r] = s.expanded ? (int32_t)i : (int32_t)((uint32_t)i / (uint32_t)s.k);
         } else if (i < w1) {
             outp[i] = -1;
         }
@@ -354,12 +358,13 @@ constexpr int kFusedRounds =
 static_assert(kFusedMax <= kFusedRounds * kRoundPicks * kRouteWaves,
               "single-launch routing keeps at most kFusedRounds rounds per wave");
 
-template <typename IdT>
-__global__ __launch_bounds__(kRouteThreads) void route_fused_kernel(RouteArgs a, Shape s) {
-    __shared__ int rows[kRouteWaves][kMaxE];
-    __shared__ int cnt[kMaxE];
-    __shared__ int off[kMaxE];
-    __shared__ int tmp[160];
+// The single-workgroup routing.  kLocal: the workgroup routes only for
+// itself and leaves the output permutation in lperm (LDS); otherwise it
+// writes every metadata array.
+template <typename IdT, bool kLocal>
+__device__ __forceinline__ void fused_route(const RouteArgs& a, const Shape& s,
+                                            int (&rows)[kRouteWaves][kMaxE], int* cnt, int* off,
+                                            int* tmp, int* lperm) {
     const int tid = threadIdx.x, wave = tid / kWave;
     const IdT* ids = static_cast<const IdT*>(a.ids);
     int64_t w0, w1;
@@ -390,7 +395,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_fused_kernel(RouteArgs a,
         cnt[e] = run;
     }
     __syncthreads();
-    const int R = scan_experts(a, cnt, off, tmp, true);
+    const int R = scan_experts(a, cnt, off, tmp, !kLocal);
     __syncthreads();
     for (int e = tid; e < s.E; e += kRouteThreads)
 #pragma unroll
@@ -398,10 +403,69 @@ __global__ __launch_bounds__(kRouteThreads) void route_fused_kernel(RouteArgs a,
     __syncthreads();
 #pragma unroll
     for (int r = 0; r < kFusedRounds; ++r)
-        scatter_keys(key[r], w0 + r * kRoundPicks, w1, s, rows[wave], a.output_perm,
-                     a.input_perm, a.input_perm_len);
-    fill_unused_rows(a, cnt, off, R, wave, kRouteWaves, tid, kRouteThreads);
-    fill_tiles(a, cnt, off, R, wave, kRouteWaves, tid, kRouteThreads);
+        scatter_keys<kLocal>(key[r], w0 + r * kRoundPicks, w1, s, rows[wave],
+                             kLocal ? lperm : a.output_perm, a.input_perm, a.input_perm_len);
+    if (!kLocal) {
+        fill_unused_rows(a, cnt, off, R, wave, kRouteWaves, tid, kRouteThreads);
+        fill_tiles(a, cnt, off, R, wave, kRouteWaves, tid, kRouteThreads);
+    }
+}
+
+template <typename IdT>
+__global__ __launch_bounds__(kRouteThreads) void route_fused_kernel(RouteArgs a, Shape s) {
+    __shared__ int rows[kRouteWaves][kMaxE];
+    __shared__ int cnt[kMaxE];
+    __shared__ int off[kMaxE];
+    __shared__ int tmp[160];
+    fused_route<IdT, false>(a, s, rows, cnt, off, tmp, nullptr);
+}
+
+// Routing and dispatch in one launch, for inputs the single-workgroup
+// routing takes: one workgroup per token and chunk of 512 16-byte vectors of
+// its row.  Each workgroup requests its vector of the token row first, then
+// runs the whole routing itself (the ids are at most a few KB) with the
+// output permutation kept in LDS, and stores the vector to the token's k
+// rows; workgroup 0, the first to start, also writes every metadata array.
+// This saves a launch and a dependent trip through memory between routing
+// and dispatch at decode-sized batches.
+template <typename IdT, int P>
+__global__ __launch_bounds__(kRouteThreads) void route_dispatch_kernel(
+    RouteArgs a, Shape s, const uint8_t* __restrict__ src, int64_t row_bytes,
+    uint8_t* __restrict__ dst, int64_t num_dst_rows, int32_t chunks) {
+    __shared__ int rows[kRouteWaves][kMaxE];
+    __shared__ int cnt[kMaxE];
+    __shared__ int off[kMaxE];
+    __shared__ int tmp[160];
+    __shared__ int lperm[kFusedMax];
+    int64_t chunk;
+    const int64_t t = chunk_row(chunks, chunk);
+    const int64_t nvec = row_bytes / 16;
+    const int64_t c = chunk * kRouteThreads + threadIdx.x;
+    const bool live = c < nvec;
+    u32x4 v{0u, 0u, 0u, 0u};
+    if (live) v = reinterpret_cast<const u32x4*>(src + t * row_bytes)[c];
+    if (blockIdx.x == 0) {
+        fused_route<IdT, false>(a, s, rows, cnt, off, tmp, nullptr);
+        // This workgroup's own rows: read back what it wrote to output_perm
+        // (the same workgroup, ordered by the barrier).
+        __syncthreads();
+        for (int j = threadIdx.x; j < s.k; j += kRouteThreads)
+            lperm[t * s.k + j] = a.output_perm[t * s.k + j];
+    } else {
+        fused_route<IdT, true>(a, s, rows, cnt, off, tmp, lperm);
+    }
+    __syncthreads();
+    const int lane = threadIdx.x & (kWave - 1);
+    for (int j0 = 0; j0 < s.k; j0 += kWave) {
+        const int nj = s.k - j0 < kWave ? s.k - j0 : kWave;
+        int my_r = lane < nj ? lperm[t * s.k + j0 + lane] : -1;
+        if (my_r >= num_dst_rows) my_r = -1;
+        for (int j = 0; j < nj; ++j) {
+            const int32_t r = __builtin_amdgcn_readlane(my_r, j);
+            if (r < 0 || !live) continue;
+            store16<P>(v, dst + (int64_t)r * row_bytes, row_bytes, c * 16);
+        }
+    }
 }
 
 // ---- two-launch path -------------------------------------------------------
@@ -578,13 +642,27 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(RouteArgs 
 
 int id_bits(int E) { return E <= 1 ? 0 : 32 - __builtin_clz((unsigned)(E - 1)); }
 
+// Inputs the single-workgroup routing takes.
+bool single_launch(const RouteArgs& a) {
+    return a.num_picks <= kFusedAlways ||
+           (a.num_picks <= kFusedMax && a.input_perm_len <= 2 * a.num_picks);
+}
+
+Shape shape_of(const RouteArgs& a) {
+    return Shape{a.num_picks, a.num_experts, id_bits(a.num_experts), a.topk, a.id_offset,
+                 a.inp_expanded};
+}
+
+// Workgroups of route_dispatch_kernel at most: each one routes all picks on
+// its own, so past about two per CU the repeated routing costs more than the
+// launch it saves.
+constexpr int64_t kMaxRouteDispatchGroups = 512;
+
 template <typename IdT>
 hipError_t launch_typed(const RouteArgs& a, hipStream_t stream, hipEvent_t start,
                         hipEvent_t stop) {
-    Shape s{a.num_picks, a.num_experts, id_bits(a.num_experts), a.topk, a.id_offset,
-            a.inp_expanded};
-    if (a.num_picks <= kFusedAlways ||
-        (a.num_picks <= kFusedMax && a.input_perm_len <= 2 * a.num_picks)) {
+    const Shape s = shape_of(a);
+    if (single_launch(a)) {
         launch_kernel(route_fused_kernel<IdT>, dim3(1), dim3(kRouteThreads), 0, stream, start,
                       stop, a, s);
         return hipGetLastError();
@@ -602,6 +680,33 @@ hipError_t launch_typed(const RouteArgs& a, hipStream_t stream, hipEvent_t start
 }
 
 }  // namespace
+
+bool route_dispatch_fusable(const RouteArgs& a, int64_t num_tokens, int64_t row_bytes,
+                            const void* src, const void* dst) {
+    if (num_tokens < 1 || !single_launch(a) || a.inp_expanded || a.tile_group != nullptr)
+        return false;
+    if (row_bytes % 16 != 0 || (reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) % 16 != 0)
+        return false;
+    const int64_t chunks = (row_bytes / 16 + kRouteThreads - 1) / kRouteThreads;
+    return num_tokens * chunks <= kMaxRouteDispatchGroups;
+}
+
+hipError_t launch_route_dispatch(const RouteArgs& a, int64_t num_tokens, const void* src,
+                                 int64_t row_bytes, void* dst, int64_t num_dst_rows,
+                                 hipStream_t stream) {
+    const Shape s = shape_of(a);
+    const int32_t chunks = (int32_t)((row_bytes / 16 + kRouteThreads - 1) / kRouteThreads);
+    const dim3 grid((unsigned)(num_tokens * chunks)), block(kRouteThreads);
+    const uint8_t* sp = static_cast<const uint8_t*>(src);
+    uint8_t* dp = static_cast<uint8_t*>(dst);
+    if (a.ids64)
+        hipLaunchKernelGGL((route_dispatch_kernel<int64_t, kStream>), grid, block, 0, stream, a,
+                           s, sp, row_bytes, dp, num_dst_rows, chunks);
+    else
+        hipLaunchKernelGGL((route_dispatch_kernel<int32_t, kStream>), grid, block, 0, stream, a,
+                           s, sp, row_bytes, dp, num_dst_rows, chunks);
+    return hipGetLastError();
+}
 
 size_t route_workspace_bytes(int64_t num_picks, int32_t num_experts) {
     if (num_picks <= kFusedAlways) return 0;

@@ -184,6 +184,38 @@ mx_status mx_prepare_moe_input_timed(const void* topk_ids, int32_t ids_dtype, in
                                      void* stream);
 
 /*
+ * prepare_dispatch -- prepare_moe_input followed by dispatch_rows (below) on
+ * the same stream, in one call: the routing of the sglang page's "Changes"
+ * item 1 and the rows of its item 2 (dst[output_permutation[t*k+j]] = src[t]).
+ * The first twenty arguments are those of mx_prepare_moe_input, with the
+ * same meaning, layout and checks; src, row_bytes, dst, num_dst_rows,
+ * side_src, side_row_bytes and side_dst are those of mx_dispatch_rows.  The
+ * results are bit-identical to the two calls.  Every argument of both is
+ * checked before anything is launched, so an error status means nothing
+ * was enqueued.
+ *
+ * Inputs that prepare_moe_input routes in one workgroup (up to 1024 picks,
+ * or 2048 when input_permutation_len <= 2*T*k), with row_bytes and both row
+ * bases multiples of 16, no side rows and at most 512 workgroups of 512
+ * 16-byte vectors, run as one launch: every workgroup routes all picks
+ * itself and copies its chunk of one token row, and the first also writes
+ * the metadata.  This saves a launch and a dependent trip through memory at
+ * decode-sized batches.  Other inputs run the kernels of the two calls.
+ * Caller-owned memory as in both calls; nothing is allocated or freed.
+ */
+mx_status mx_prepare_dispatch(const void* topk_ids, int32_t ids_dtype, int64_t num_tokens,
+                              int32_t topk, int32_t num_experts, int32_t gemm1_n,
+                              int32_t gemm1_k, int32_t gemm2_n, int32_t gemm2_k,
+                              int32_t row_align, int32_t* expert_offsets,
+                              int32_t* problem_sizes1, int32_t* problem_sizes2,
+                              int32_t* input_permutation, int64_t input_permutation_len,
+                              int32_t* output_permutation, int32_t* blockscale_offsets,
+                              int32_t blockscale_align, void* workspace, size_t workspace_bytes,
+                              const void* src, int64_t row_bytes, void* dst,
+                              int64_t num_dst_rows, const void* side_src,
+                              int64_t side_row_bytes, void* side_dst, void* stream);
+
+/*
  * shuffle_rows -- dtype-agnostic row gather (sglang page, "Changes" item 2):
  *
  *   dst[r] = src[dst2src[r]]   (row_bytes bytes) for r < num_dst_rows

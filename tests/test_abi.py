@@ -253,3 +253,37 @@ def test_noalloc_prepare_checks_like_the_plain_call(lib):
     # 128 tiles x 1024 experts x 4 bytes
     assert lib.mx_prepare_workspace_size(2**31 // 8 - 1, 8, 1024) <= 512 * 1024
     assert lib.mx_prepare_workspace_size(65536, 8, 1024) <= 512 * 1024
+
+
+def test_prepare_dispatch_checks_both_halves(lib):
+    """prepare_dispatch refuses what prepare_moe_input or dispatch_rows would
+    refuse, before anything is launched."""
+    def pd(**kw):
+        a = dict(ids=P, dt=I32, T=64, k=8, E=256, A=1, inp_len=64 * 8, outp=P, ws=P,
+                 src=P, rb=16, dst=P, nd=64 * 8, ss=None, srb=0, sd=None)
+        a.update(kw)
+        return lib.mx_prepare_dispatch(a["ids"], a["dt"], a["T"], a["k"], a["E"], 1, 2, 3, 4,
+                                       a["A"], P, P, P, P, a["inp_len"], a["outp"], None, 128,
+                                       a["ws"], 1 << 20, a["src"], a["rb"], a["dst"], a["nd"],
+                                       a["ss"], a["srb"], a["sd"], S)
+    # the routing half
+    assert pd(dt=F32) == DTYPE
+    assert pd(E=0) == INVALID
+    assert pd(E=1025) == INVALID
+    assert pd(A=0) == INVALID
+    assert pd(ids=None) == INVALID
+    assert pd(inp_len=64 * 8 - 1) == CAPACITY
+    assert pd(ids=P + 2) == MISALIGNED
+    assert pd(T=65536, inp_len=65536 * 8, nd=65536 * 8, ws=None) == WORKSPACE
+    assert pd(T=65536, inp_len=65536 * 8, nd=65536 * 8, ws=P + 4) == MISALIGNED
+    # the dispatch half
+    assert pd(rb=0) == INVALID
+    assert pd(rb=65535 * 1024 + 1) == INVALID
+    assert pd(src=None) == INVALID
+    assert pd(dst=None) == INVALID
+    assert pd(nd=-1) == INVALID
+    assert pd(outp=None) == INVALID
+    assert pd(outp=P + 1) == MISALIGNED
+    assert pd(ss=P, srb=0, sd=P) == INVALID                  # side rows of 0 bytes
+    assert pd(ss=P, srb=16, sd=None) == INVALID              # side without destination
+    assert pd(srb=16) == INVALID                             # side bytes without arrays

@@ -51,3 +51,5 @@ def test_bench_json_line_small_workload():
         assert abs(op["frac"] - op["gbps"] / 8000.0) < 1e-9, name
     # T = 32, H = 4096, k = 8: the reduction moves the combine's bytes with bf16 output
     assert ref["sum_over_k"]["bytes"] == 32 * 8 * 4096 * 2 + 32 * 4096 * 2
+    oc = d["workloads"]["uniform_T32_H4096_E256_k8"]
+    assert oc["step_ms_cold_one_call_dispatch"] > 0 and oc["step_ms_warm_one_call_dispatch"] > 0
