@@ -117,6 +117,10 @@ def parse_args(argv=None):
                    help="tokens of the --calibrate run (rows of 14 KiB, k = 8)")
     p.add_argument("--calibrate-out", choices=("bf16", "f32"), default="bf16",
                    help="combine output dtype of the --calibrate run")
+    p.add_argument("--one-call-sweep", action="store_true",
+                   help="time routing + dispatch as prepare_dispatch (one call) against "
+                        "prepare_moe_input + dispatch_rows (two calls) at decode-sized batches, "
+                        "eager and as HIP-graph replays, and print one JSON line per size")
     p.add_argument("--graph", action="store_true",
                    help="also time K replays of a HIP graph of one step (warm)")
     p.add_argument("--with", dest="extras", default="",
@@ -691,6 +695,63 @@ def reference_ops(w, dev, steps: int = 10, reps: int = 3) -> dict:
     return res
 
 
+def one_call_sweep(sizes=(1, 8, 32, 64, 128, 192, 256), hiddens=(4096, 7168), E=256, k=8,
+                   calls=200, reps=5) -> None:
+    """prepare_dispatch against prepare_moe_input + dispatch_rows on uniform
+    routing, bf16 rows: microseconds per call pair, the minimum over ``reps``
+    means of ``calls`` bound calls back to back (eager, host included), and
+    of graphs of 20 call pairs replayed (GPU time only)."""
+    import numpy as np
+    import torch
+    import combine_topk_ids_expert_amd as mx
+    from workloads import routing
+    dev = torch.device("cuda:0")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+    def per_call(fn, n, div=1):
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        best = float("inf")
+        for _ in range(reps):
+            ev[0].record()
+            for _ in range(n):
+                fn()
+            ev[1].record()
+            torch.cuda.synchronize()
+            best = min(best, ev[0].elapsed_time(ev[1]) * 1e3 / (n * div))
+        return best
+
+    for H in hiddens:
+        for T in sizes:
+            ids = torch.from_numpy(routing.uniform_topk(np.random.default_rng(T), T, E, k)).to(dev)
+            x = routing.normal_rows(T, H, "bf16", seed=T, device=dev)
+            r = mx.empty_routing(T, k, E, dev)
+            xd = torch.empty((r["input_permutation"].numel(), H), dtype=x.dtype, device=dev)
+            meta = (ids, r["expert_offsets"], r["problem_sizes1"], r["problem_sizes2"],
+                    r["input_permutation"], r["output_permutation"], E, 2048, H)
+            one = mx.bind(mx.prepare_dispatch, *meta, x, xd, workspace=r["workspace"])
+            prep = mx.bind(mx.prepare_moe_input, *meta, workspace=r["workspace"])
+            disp = mx.bind(mx.dispatch_rows, x, r["output_permutation"], k, xd)
+
+            def two():
+                prep()
+                disp()
+
+            graphs = []
+            for fn in (one, two):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    for _ in range(20):
+                        fn()
+                graphs.append(g)
+            print(json.dumps({"one_call_sweep": {
+                "T": T, "H": H, "E": E, "topk": k,
+                "eager_one_call_us": per_call(one, calls), "eager_two_calls_us": per_call(two, calls),
+                "graph_one_call_us": per_call(graphs[0].replay, 10, 20),
+                "graph_two_calls_us": per_call(graphs[1].replay, 10, 20)}}), flush=True)
+
+
 CALIBRATE_K, CALIBRATE_H = 8, 7168
 
 
@@ -744,6 +805,9 @@ def main(argv=None):
         return
     if args.calibrate:
         calibrate(max(args.steps, 1), args.calibrate_tokens, args.calibrate_out)
+        return
+    if args.one_call_sweep:
+        one_call_sweep()
         return
 
     from workloads import get_workload

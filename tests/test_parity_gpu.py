@@ -486,15 +486,17 @@ def test_timed_forms_match_and_time_the_kernels():
         assert s0.elapsed_time(a) >= 0.0 and b.elapsed_time(s1) >= 0.0
 
 
-def test_graph_capture_replays_match_eager():
+@pytest.mark.parametrize("T,one_call", [(1500, False), (1500, True), (100, True)])
+def test_graph_capture_replays_match_eager(T, one_call):
     """The calls enqueue kernels only (no allocation, no memset), so a HIP
-    graph can capture prepare, dispatch and combine.  The graph is replayed
-    three times on new inputs copied into its static tensors, with eager work
-    and synchronisations between replays; every replay must equal the eager
-    calls on the same inputs, bit for bit."""
-    _print_case("graph capture")
+    graph can capture prepare, dispatch and combine (with one_call, routing
+    and dispatch through prepare_dispatch, one launch at T = 100).  The graph
+    is replayed three times on new inputs copied into its static tensors,
+    with eager work and synchronisations between replays; every replay must
+    equal the eager calls on the same inputs, bit for bit."""
+    _print_case("graph capture", T, one_call)
     dev = torch.device(DEV)
-    T, E, k, H, A = 1500, 64, 8, 1024, 16
+    E, k, H, A = 64, 8, 1024, 16
     r = mx.empty_routing(T, k, E, dev, row_align=A)
     cap = r["input_permutation"].numel()
     ids = torch.empty(T, k, dtype=torch.int64, device=dev)
@@ -505,10 +507,17 @@ def test_graph_capture_replays_match_eager():
     out = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
 
     def step():
-        mx.prepare_moe_input(ids, r["expert_offsets"], r["problem_sizes1"], r["problem_sizes2"],
-                             r["input_permutation"], r["output_permutation"], E, 64, 32,
-                             row_align=A, workspace=r["workspace"])
-        mx.dispatch_rows(x, r["output_permutation"], k, xd)
+        if one_call:
+            mx.prepare_dispatch(ids, r["expert_offsets"], r["problem_sizes1"],
+                                r["problem_sizes2"], r["input_permutation"],
+                                r["output_permutation"], E, 64, 32, x, xd, row_align=A,
+                                workspace=r["workspace"])
+        else:
+            mx.prepare_moe_input(ids, r["expert_offsets"], r["problem_sizes1"],
+                                 r["problem_sizes2"], r["input_permutation"],
+                                 r["output_permutation"], E, 64, 32, row_align=A,
+                                 workspace=r["workspace"])
+            mx.dispatch_rows(x, r["output_permutation"], k, xd)
         mx.apply_shuffle_mul_sum(y, out, r["output_permutation"], w)
 
     def load(seed):
