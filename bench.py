@@ -758,7 +758,7 @@ CALIBRATE_K, CALIBRATE_H = 8, 7168
 def calibrate(steps: int, T: int, out_dtype: str = "bf16") -> None:
     """The row kernels on identity maps: dispatch reads T rows and writes
     token t to rows t*k .. t*k+k-1; combine reads those T*k rows once each
-    (unit weights) and writes T rows.  Prints the algorithmic bytes of each
+    (unit fp32 weights) and writes T rows.  Prints the algorithmic bytes of each
     launch, which the FETCH_SIZE / WRITE_SIZE counters of the same launches
     are divided by."""
     import torch
@@ -771,8 +771,10 @@ def calibrate(steps: int, T: int, out_dtype: str = "bf16") -> None:
     xd = torch.empty((T * k, H), dtype=torch.bfloat16, device=dev)
     ob = 4 if out_dtype == "f32" else 2
     out = torch.empty((T, H), dtype=torch.float32 if ob == 4 else torch.bfloat16, device=dev)
+    ones = torch.ones((T, k), dtype=torch.float32, device=dev)
     disp = mx.bind(mx.dispatch_rows, x, perm, k, xd)
-    comb = mx.bind(mx.apply_shuffle_mul_sum, xd, out, perm)
+    # fp32 unit weights: the same kernel instantiation as the benchmark's combine
+    comb = mx.bind(mx.apply_shuffle_mul_sum, xd, out, perm, ones)
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
     for e in evs:
         e.record()
@@ -786,7 +788,7 @@ def calibrate(steps: int, T: int, out_dtype: str = "bf16") -> None:
     row = H * 2
     print(json.dumps({"calibrate": {
         "dispatch_rows_kernel": {"read_bytes": T * row + T * k * 4, "write_bytes": T * k * row},
-        "combine_vec_kernel": {"read_bytes": T * k * row + T * k * 4, "write_bytes": T * H * ob},
+        "combine_vec_kernel": {"read_bytes": T * k * row + T * k * 8, "write_bytes": T * H * ob},
         "launches": steps, "tokens": T,
         "kernel_ms": {"dispatch_rows_kernel": sorted(td)[len(td) // 2],
                       "combine_vec_kernel": sorted(tc)[len(tc) // 2]}}}), flush=True)
