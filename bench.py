@@ -75,6 +75,8 @@ REPS = 5
 # dispatch in one prepare_dispatch call (the library runs both in one launch
 # up to 2048 picks when the rows allow it).
 ONE_CALL_MAX_PICKS = 2048
+# Steps per HIP graph in the graph-replay passes.
+GRAPH_STEPS = 20
 FLUSH_WRITE_BYTES = 512 << 20
 FLUSH_READ_BYTES = 1 << 30
 KERNEL_SOURCES = ("route.hip", "rows.hip", "combine.hip", "device_common.h")
@@ -122,7 +124,8 @@ def parse_args(argv=None):
                         "prepare_moe_input + dispatch_rows (two calls) at decode-sized batches, "
                         "eager and as HIP-graph replays, and print one JSON line per size")
     p.add_argument("--graph", action="store_true",
-                   help="also time K replays of a HIP graph of one step (warm)")
+                   help="also time the step replayed from a HIP graph of 20 steps (warm) on "
+                        "workloads of more than 2048 picks (smaller ones always do)")
     p.add_argument("--with", dest="extras", default="",
                    help="comma-separated extra stages added to each step of the first "
                         "workload and reported separately: zero_padding (zero-fill the "
@@ -511,18 +514,30 @@ def measure(w, args, dev, flush, extras=()) -> dict:
     warm = warm_pass(step.run, K)
     warm_s = steps_pass(step.run, K, None)
     warm_k = kernels_pass(step, K, None)
+    small = w.T * w.k <= ONE_CALL_MAX_PICKS
     one_call = None
-    if w.T * w.k <= ONE_CALL_MAX_PICKS:
+    if small:
         one_call = (steps_pass(step.run_one_call_dispatch, K, flush),
                     warm_pass(step.run_one_call_dispatch, K))
-    graph = None
-    if args.graph:
+
+    def graph_pass(fn):
+        # One graph holds GRAPH_STEPS steps, so a replay's own launch cost is
+        # spread over them; per-step times divide by it.
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            step.run()
-        for _ in range(args.warmup):
+            for _ in range(GRAPH_STEPS):
+                fn()
+        for _ in range(max(args.warmup // GRAPH_STEPS, 1)):
             g.replay()
-        graph = warm_pass(g.replay, K)
+        reps = max(K // GRAPH_STEPS, 1)
+        r = warm_pass(g.replay, reps)
+        return {"per_rep": [[v / GRAPH_STEPS for v in rep] for rep in r["per_rep"]],
+                "wall": [v / GRAPH_STEPS for v in r["wall"]]}
+
+    # Small workloads are bound by host time per call; replaying steps from a
+    # HIP graph shows what the GPU takes.
+    graph = graph_pass(step.run) if args.graph or small else None
+    graph_one = graph_pass(step.run_one_call_dispatch) if small else None
 
     counts = step.r["problem_sizes1"][:, 0].cpu().numpy()
     n_valid = int(counts.sum())
@@ -594,8 +609,17 @@ def measure(w, args, dev, flush, extras=()) -> dict:
             "warm_reps": rep_stats(one_call[1]["per_rep"])}
     if graph is not None:
         gm = rep_stats(graph["per_rep"])["mean"]
-        res["warm_graph"] = {"step_ms": gm, "tokens_per_s": T / (gm * 1e-3),
+        res["warm_graph"] = {"what": "steps replayed back to back from a HIP graph of "
+                                     f"{GRAPH_STEPS} steps",
+                             "step_ms": gm, "tokens_per_s": T / (gm * 1e-3),
                              "reps": rep_stats(graph["per_rep"])}
+    if graph_one is not None:
+        go = rep_stats(graph_one["per_rep"])["mean"]
+        res["warm_graph_one_call_dispatch"] = {
+            "what": f"steps replayed from a HIP graph of {GRAPH_STEPS} steps, routing and "
+                    "dispatch in one prepare_dispatch call", "step_ms": go,
+            "tokens_per_s": T / (go * 1e-3),
+            "reps": rep_stats(graph_one["per_rep"])}
     g = gate_ms(w, step_bytes)
     if g is not None:
         res["gate_70pct"] = {"step_ms_max": g, "met_cold": res["cold"]["step_ms"] <= g,
@@ -862,6 +886,8 @@ def main(argv=None):
             b["step_ms_warm_one_call_dispatch"] = r["one_call_dispatch"]["step_ms_warm"]
         if "warm_graph" in r:
             b["step_ms_warm_graph"] = r["warm_graph"]["step_ms"]
+        if "warm_graph_one_call_dispatch" in r:
+            b["step_ms_warm_graph_one_call_dispatch"] = r["warm_graph_one_call_dispatch"]["step_ms"]
         return b
 
     for r in results:

@@ -53,3 +53,4 @@ def test_bench_json_line_small_workload():
     assert ref["sum_over_k"]["bytes"] == 32 * 8 * 4096 * 2 + 32 * 4096 * 2
     oc = d["workloads"]["uniform_T32_H4096_E256_k8"]
     assert oc["step_ms_cold_one_call_dispatch"] > 0 and oc["step_ms_warm_one_call_dispatch"] > 0
+    assert oc["step_ms_warm_graph"] > 0 and oc["step_ms_warm_graph_one_call_dispatch"] > 0
