@@ -123,6 +123,9 @@ def parse_args(argv=None):
                    help="time routing + dispatch as prepare_dispatch (one call) against "
                         "prepare_moe_input + dispatch_rows (two calls) at decode-sized batches, "
                         "eager and as HIP-graph replays, and print one JSON line per size")
+    p.add_argument("--routing-sweep", action="store_true",
+                   help="time prepare_moe_input alone at T = 128 to 4096 under several routings "
+                        "and print one JSON line per case")
     p.add_argument("--graph", action="store_true",
                    help="also time the step replayed from a HIP graph of 20 steps (warm) on "
                         "workloads of more than 2048 picks (smaller ones always do)")
@@ -776,6 +779,57 @@ def one_call_sweep(sizes=(1, 8, 32, 64, 128, 192, 256), hiddens=(4096, 7168), E=
                 "graph_two_calls_us": per_call(graphs[1].replay, 10, 20)}}), flush=True)
 
 
+ROUTING_SWEEP = [  # (T, E, k, row_align, routing)
+    (128, 256, 8, 1, "uniform"), (300, 256, 8, 1, "uniform"), (512, 256, 8, 1, "uniform"),
+    (1024, 256, 8, 1, "uniform"), (1024, 256, 8, 128, "uniform"), (1024, 256, 8, 1, "k_hot"),
+    (1024, 128, 8, 1, "zipf"), (1024, 1024, 8, 1, "uniform"), (1000, 8, 8, 1, "dups"),
+    (1000, 1, 8, 1, "dups"), (1025, 256, 8, 1, "uniform"), (2048, 256, 8, 1, "uniform"),
+    (2048, 256, 8, 1, "k_hot"), (4096, 256, 8, 128, "uniform")]
+
+
+def routing_sweep(calls=200, reps=5) -> None:
+    """prepare_moe_input alone, bound and called back to back on one stream:
+    microseconds per call, the minimum and median of ``reps`` means of
+    ``calls`` calls, for the cases of ROUTING_SWEEP (seeded ids)."""
+    import numpy as np
+    import torch
+    import combine_topk_ids_expert_amd as mx
+    from workloads import routing
+    dev = torch.device("cuda:0")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for T, E, k, A, mode in ROUTING_SWEEP:
+        rng = np.random.default_rng(T * 31 + E)
+        if mode == "uniform":
+            ids = routing.uniform_topk(rng, T, E, k)
+        elif mode == "k_hot":
+            ids = routing.k_hot_topk(rng, T, E, k, 8, 0.8)
+        elif mode == "zipf":
+            ids = routing.zipf_topk(rng, T, E, k, 1.2)
+        else:
+            ids = rng.integers(0, E, (T, k))
+        t_ids = torch.from_numpy(ids).to(dev)
+        r = mx.empty_routing(T, k, E, dev, row_align=A)
+        call = mx.bind(mx.prepare_moe_input, t_ids, r["expert_offsets"], r["problem_sizes1"],
+                       r["problem_sizes2"], r["input_permutation"], r["output_permutation"], E,
+                       2048, 7168, row_align=A, workspace=r["workspace"])
+        for _ in range(20):
+            call()
+        torch.cuda.synchronize()
+        us = []
+        for _ in range(reps):
+            ev[0].record()
+            for _ in range(calls):
+                call()
+            ev[1].record()
+            torch.cuda.synchronize()
+            us.append(ev[0].elapsed_time(ev[1]) * 1e3 / calls)
+        us.sort()
+        print(json.dumps({"routing_sweep": {"T": T, "E": E, "topk": k, "row_align": A,
+                                            "routing": mode, "picks": T * k,
+                                            "us_min": us[0], "us_median": us[len(us) // 2]}}),
+              flush=True)
+
+
 CALIBRATE_K, CALIBRATE_H = 8, 7168
 
 
@@ -834,6 +888,9 @@ def main(argv=None):
         return
     if args.one_call_sweep:
         one_call_sweep()
+        return
+    if args.routing_sweep:
+        routing_sweep()
         return
 
     from workloads import get_workload

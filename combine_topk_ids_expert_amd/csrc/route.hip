@@ -17,6 +17,9 @@
 //   small inputs (up to 1024 picks, or 2048 with little padding, where it
 //                measured faster): one workgroup counts, scans and scatters
 //                (one launch);
+//   medium inputs (up to 8192 picks): one launch of one workgroup per tile;
+//                every workgroup counts every pick itself (totals, and the
+//                picks before its tile), then places its tile's picks;
 //   larger inputs, two launches:
 //     count   -- one workgroup per tile writes the tile's count of every
 //                expert to the workspace, expert-major ([E][tiles]);
@@ -468,6 +471,136 @@ __global__ __launch_bounds__(kRouteThreads) void route_dispatch_kernel(
     }
 }
 
+// ---- one launch, every workgroup counting every pick ------------------------
+
+#ifndef MXMOE_SPREAD_MAX
+#define MXMOE_SPREAD_MAX 8192
+#endif
+// Picks up to which the medium path below replaces the two launches.  Every
+// workgroup counts every pick, so its cost grows with the picks: measured on
+// MI355X it saves 16-35% up to 8192 picks under uniform, K-hot, Zipf and
+// one-expert routing and 4% with 8 experts (5.4-7.6 against 7.6-10.9 us back
+// to back), about breaks even at 16384 and loses at 32768.
+constexpr int64_t kSpreadMax = MXMOE_SPREAD_MAX;
+static_assert(kSpreadMax == 0 || kSpreadMax >= kFusedMax,
+              "the medium path starts where the single-workgroup path ends");
+
+// Medium inputs: tiles as in the two-launch path, but each workgroup counts
+// every pick itself (totals per expert, and the picks before its tile), so
+// no count table passes between launches.  The picks outside the tile are
+// strided over all threads, kSpreadBatch loads per thread in flight, and
+// counted with workgroup-wide LDS atomics; the tile's own picks are counted
+// per wave, placed as in route_scatter_kernel.
+constexpr int kSpreadBatch = 8;
+
+template <typename IdT>
+__global__ __launch_bounds__(kRouteThreads) void route_spread_kernel(RouteArgs a, Shape s,
+                                                                     int64_t tile, int tiles) {
+    __shared__ int rows[kRouteWaves][kMaxE];
+    __shared__ int cnt[kMaxE];
+    __shared__ int pre[kMaxE];
+    __shared__ int off[kMaxE];
+    __shared__ int tmp[160];
+    const int tid = threadIdx.x, wave = tid / kWave;
+    const int b = blockIdx.x;
+    const IdT* ids = static_cast<const IdT*>(a.ids);
+    const int64_t t0 = (int64_t)b * tile;
+    const int64_t t1 = t0 + tile < s.n ? t0 + tile : s.n;
+    int64_t w0, w1;
+    wave_stretch(t0, t1, wave, w0, w1);
+    const bool one_round = w1 - w0 <= kBatch * kWave;
+    IdT raw[kBatch];
+    if (one_round) load_raw(ids, w0, w1, raw);
+    for (int e = tid; e < s.E; e += kRouteThreads) {
+        cnt[e] = 0;
+        pre[e] = 0;
+#pragma unroll
+        for (int w = 0; w < kRouteWaves; ++w) rows[w][e] = 0;
+    }
+    __syncthreads();
+    // Picks outside [t0, t1): thread tid takes i = tid + j * kRouteThreads.
+    // Indices past n (or inside the tile) load the last pick and drop it, so
+    // every batch issues all its loads before the first use.
+    const int64_t outside = s.n - (t1 - t0);
+    for (int64_t j0 = 0; j0 * kRouteThreads < outside; j0 += kSpreadBatch) {
+        IdT v[kSpreadBatch];
+        int64_t idx[kSpreadBatch];
+#pragma unroll
+        for (int u = 0; u < kSpreadBatch; ++u) {
+            const int64_t q = (j0 + u) * kRouteThreads + tid;      // q-th pick outside the tile
+            idx[u] = q < t0 ? q : q + (t1 - t0);
+            v[u] = ids[q < outside ? idx[u] : s.n - 1];
+        }
+        int key8[kSpreadBatch];
+        bool one = true;
+#pragma unroll
+        for (int u = 0; u < kSpreadBatch; ++u) {
+            const int64_t q = (j0 + u) * kRouteThreads + tid;
+            const int64_t x = (int64_t)v[u] - s.id_offset;
+            key8[u] = q < outside && x >= 0 && x < s.E ? (int)x : -1;
+        }
+        // A batch whose valid picks all hold one expert is added with one
+        // atomic per total: with every pick on one expert, per-lane atomics
+        // on one address would serialize across the whole workgroup.
+        const int k0 = __builtin_amdgcn_readfirstlane(key8[0]);
+#pragma unroll
+        for (int u = 0; u < kSpreadBatch; ++u) one = one && (key8[u] == k0 || key8[u] < 0);
+        if (__ballot(!one) == 0ull) {                    // wave-uniform
+            if (k0 >= 0) {
+                int all = 0, before = 0;
+#pragma unroll
+                for (int u = 0; u < kSpreadBatch; ++u) {
+                    all += __popcll(__ballot(key8[u] == k0));
+                    before += __popcll(__ballot(key8[u] == k0 && idx[u] < t0));
+                }
+                if (lane_id() == 0) {
+                    atomicAdd(&cnt[k0], all);
+                    if (before) atomicAdd(&pre[k0], before);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < kSpreadBatch; ++u) {
+                if (key8[u] < 0) continue;
+                atomicAdd(&cnt[key8[u]], 1);
+                if (idx[u] < t0) atomicAdd(&pre[key8[u]], 1);
+            }
+        }
+    }
+    int key[kBatch];
+    if (one_round) {
+        raw_to_keys(raw, w0, w1, s.E, s.id_offset, key);
+        count_keys(key, w0, w1, s, rows[wave]);
+    } else count_stretch<IdT>(ids, w0, w1, s, rows[wave]);
+    __syncthreads();
+    for (int e = tid; e < s.E; e += kRouteThreads) {
+        int run = 0;
+#pragma unroll
+        for (int w = 0; w < kRouteWaves; ++w) {
+            const int c = rows[w][e];
+            rows[w][e] = run;
+            run += c;
+        }
+        cnt[e] += run;
+    }
+    __syncthreads();
+    const int R = scan_experts(a, cnt, off, tmp, b == 0);
+    __syncthreads();
+    for (int e = tid; e < s.E; e += kRouteThreads)
+#pragma unroll
+        for (int w = 0; w < kRouteWaves; ++w) rows[w][e] += off[e] + pre[e];
+    __syncthreads();
+    if (one_round)
+        scatter_keys(key, w0, w1, s, rows[wave], a.output_perm, a.input_perm, a.input_perm_len);
+    else
+        scatter_stretch<IdT>(ids, w0, w1, s, rows[wave], a.output_perm, a.input_perm,
+                             a.input_perm_len);
+    fill_unused_rows(a, cnt, off, R, b * kRouteWaves + wave, tiles * kRouteWaves,
+                     (int64_t)b * kRouteThreads + tid, (int64_t)tiles * kRouteThreads);
+    fill_tiles(a, cnt, off, R, b * kRouteWaves + wave, tiles * kRouteWaves,
+               (int64_t)b * kRouteThreads + tid, (int64_t)tiles * kRouteThreads);
+}
+
 // ---- two-launch path -------------------------------------------------------
 
 // Tile counts per expert, expert-major: workspace[e * stride + tile] with the
@@ -669,6 +802,11 @@ hipError_t launch_typed(const RouteArgs& a, hipStream_t stream, hipEvent_t start
     }
     const int64_t tile = tile_picks(a.num_picks, a.num_experts);
     const int tiles = (int)((a.num_picks + tile - 1) / tile);
+    if (a.num_picks <= kSpreadMax) {
+        launch_kernel(route_spread_kernel<IdT>, dim3(tiles), dim3(kRouteThreads), 0, stream,
+                      start, stop, a, s, tile, tiles);
+        return hipGetLastError();
+    }
     launch_kernel(route_count_kernel<IdT>, dim3(tiles), dim3(kRouteThreads), 0, stream, start,
                   nullptr, a, s, tile, tiles);
     hipError_t err = hipGetLastError();
@@ -709,7 +847,7 @@ hipError_t launch_route_dispatch(const RouteArgs& a, int64_t num_tokens, const v
 }
 
 size_t route_workspace_bytes(int64_t num_picks, int32_t num_experts) {
-    if (num_picks <= kFusedAlways) return 0;
+    if (num_picks <= kFusedAlways || num_picks <= kSpreadMax) return 0;
     const int64_t tile = tile_picks(num_picks, num_experts);
     const int64_t tiles = (num_picks + tile - 1) / tile;
     return (size_t)((tiles + 3) / 4 * 4 * (int64_t)num_experts * (int64_t)sizeof(int32_t));

@@ -38,11 +38,14 @@ def _print_case(*args):
     (7, 5, 3, 4, "dups", 0.2),
     (32, 256, 8, 1, "uniform", 0.0),
     (128, 256, 8, 128, "uniform", 0.0),         # one launch, padded: 1024 picks
-    (129, 256, 8, 128, "uniform", 0.0),         # two launches, padded: 1032 picks, 3 tiles
+    (129, 256, 8, 128, "uniform", 0.0),         # medium path, heavy padding: 1032 picks, 3 tiles
     (256, 256, 8, 1, "uniform", 0.0),           # one launch, unpadded: 2048 picks
-    (257, 256, 8, 1, "uniform", 0.0),           # two launches: 2056 picks, 5 tiles
-    (1000, 256, 8, 128, "uniform", 0.0),        # 16 tiles, padded
-    (1025, 256, 8, 1, "uniform", 0.0),          # ragged last tile
+    (257, 256, 8, 1, "uniform", 0.0),           # medium path: 2056 picks, 5 tiles
+    (1000, 256, 8, 128, "uniform", 0.0),        # medium path, 16 tiles, padded
+    (1024, 1024, 8, 1, "uniform", 0.05),       # medium path at its limit: 8192 picks, E = 1024
+    (1000, 1, 8, 1, "dups", 0.0),               # medium path, every pick on one expert
+    (900, 8, 8, 2, "dups", 0.02),               # medium path, 8 experts
+    (1025, 256, 8, 1, "uniform", 0.0),          # two launches from 8200 picks, ragged last tile
     (8192, 256, 8, 1, "uniform", 0.0),          # 65536 picks, E = 256: 64 tiles of 1024
     (8193, 256, 8, 128, "uniform", 0.02),       # tiles grow past 1024 picks
     (8192, 128, 8, 1, "uniform", 0.0),          # 65536 picks, E = 128: 128 tiles of 512
