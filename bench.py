@@ -878,6 +878,10 @@ def main(argv=None):
         print(f"bench.py measures one GPU: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus}); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if os.environ.get("MXMOE_LIBRARY", "") not in ("", "product"):
+        print("bench.py measures libmxmoe.so: unset MXMOE_LIBRARY (the bounds-checked "
+              "library synchronises around every call)", file=sys.stderr)
+        sys.exit(2)
     import torch
 
     if args.copy_probe:

@@ -16,6 +16,11 @@ Outputs are written in place, as the page's custom-op registration marks.
 once and returns a ``BoundCall``; calling that enqueues the same work again
 with no Python-side checks, for small batches where a call is bound by host
 time.
+
+With ``MXMOE_LIBRARY=checked`` in the environment the binding loads
+``libmxmoe_checked.so`` instead: the same kernels with every global access
+checked against the call's arrays (``bounds_checked``, ``bounds_report``), a
+debugging library that synchronises around every call.
 """
 
 from __future__ import annotations
@@ -32,11 +37,26 @@ __all__ = [
     "moe_output_memset", "zero_padding_rows", "moe_sort", "dispatch_rows_fp8",
     "prepare_moe_input_noalloc", "dispatch_capacity", "prepare_workspace_size",
     "empty_routing", "MxError",
-    "library_path", "load_library", "EXPORTED_SYMBOLS", "bind", "BoundCall",
+    "library_path", "load_library", "open_library", "EXPORTED_SYMBOLS", "bind", "BoundCall",
+    "bounds_checked", "bounds_report", "bounds_shrink_outputs",
+    "PRODUCT_LIBRARY", "CHECKED_LIBRARY",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_PKG, "libmxmoe.so")
+PRODUCT_LIBRARY = os.path.join(_PKG, "libmxmoe.so")
+CHECKED_LIBRARY = os.path.join(_PKG, "libmxmoe_checked.so")
+
+
+def _library_from_env() -> str:
+    which = os.environ.get("MXMOE_LIBRARY", "")
+    if which in ("", "product"):
+        return PRODUCT_LIBRARY
+    if which == "checked":
+        return CHECKED_LIBRARY
+    raise ImportError(f"MXMOE_LIBRARY={which!r}: expected 'checked' or 'product'")
+
+
+_LIB_PATH = _library_from_env()
 
 # mx_dtype codes of mxmoe.h
 MX_F32, MX_F16, MX_BF16, MX_FP8_E4M3, MX_I32, MX_I64 = range(6)
@@ -50,6 +70,7 @@ EXPORTED_SYMBOLS = (
     "mx_zero_padding_rows", "mx_moe_sort", "mx_dispatch_rows_fp8",
     "mx_dispatch_rows_timed", "mx_apply_shuffle_mul_sum_timed", "mx_prepare_moe_input_timed",
     "mx_prepare_moe_input_noalloc", "mx_prepare_dispatch",
+    "mx_bounds_checked", "mx_bounds_report", "mx_bounds_shrink_outputs",
 )
 
 
@@ -71,14 +92,22 @@ def library_path() -> str:
 
 
 def load_library():
-    """Load libmxmoe.so (built by ``python -m combine_topk_ids_expert_amd.build``)."""
+    """Load libmxmoe.so (built by ``python -m combine_topk_ids_expert_amd.build``),
+    or libmxmoe_checked.so with ``MXMOE_LIBRARY=checked``; every call of this
+    module goes to the library loaded here."""
     global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(_LIB_PATH):
-        raise ImportError(f"{_LIB_PATH} is missing: build it with "
+    if _lib is None:
+        _lib = open_library(_LIB_PATH)
+    return _lib
+
+
+def open_library(path: str):
+    """A ctypes handle of the library at ``path`` (libmxmoe.so or its checked
+    twin) with every entry point's argument types set."""
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with "
                           "`python -m combine_topk_ids_expert_amd.build`; there is no fallback")
-    lib = ctypes.CDLL(_LIB_PATH)
+    lib = ctypes.CDLL(path)
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     lib.mx_status_string.restype = ctypes.c_char_p
     lib.mx_status_string.argtypes = [ctypes.c_int]
@@ -125,8 +154,34 @@ def load_library():
     lib.mx_moe_sort.restype = ctypes.c_int
     lib.mx_moe_sort.argtypes = [vp, i32, i64, i32, i32, i32, i32, i32, vp, vp, i64, vp, vp, i64,
                                 vp, vp, vp, vp, sz, vp]
-    _lib = lib
+    lib.mx_bounds_checked.restype = i32
+    lib.mx_bounds_checked.argtypes = []
+    lib.mx_bounds_report.restype = ctypes.c_int
+    lib.mx_bounds_report.argtypes = [ctypes.POINTER(ctypes.c_uint64), i32]
+    lib.mx_bounds_shrink_outputs.restype = ctypes.c_int
+    lib.mx_bounds_shrink_outputs.argtypes = [i64]
     return lib
+
+
+def bounds_checked() -> bool:
+    """Whether the loaded library is the bounds-checked one."""
+    return bool(load_library().mx_bounds_checked())
+
+
+def bounds_report(clear: bool = True) -> dict:
+    """Out-of-bounds accesses the checked library's kernels counted since the
+    last clear: loads, stores, and the address (or on-chip index) and site
+    code of the first one (all zero with libmxmoe.so)."""
+    r = (ctypes.c_uint64 * 4)()
+    _call(load_library().mx_bounds_report(r, 1 if clear else 0), "bounds_report")
+    return {"loads": int(r[0]), "stores": int(r[1]), "first_address": int(r[2]),
+            "first_site": int(r[3])}
+
+
+def bounds_shrink_outputs(nbytes: int) -> None:
+    """Checked library: describe every output array to the kernels as
+    ``nbytes`` shorter than it is, from the next call on (0 restores)."""
+    _call(load_library().mx_bounds_shrink_outputs(int(nbytes)), "bounds_shrink_outputs")
 
 
 def _ptr(t: torch.Tensor | None):

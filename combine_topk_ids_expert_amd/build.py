@@ -1,8 +1,12 @@
-"""Build libmxmoe.so (the HIP kernels and the C ABI) for gfx950 with hipcc.
+"""Build libmxmoe.so (the HIP kernels and the C ABI) for gfx950 with hipcc,
+and its bounds-checked twin libmxmoe_checked.so (the same sources with
+MXMOE_CHECKED defined: every kernel access is checked against the call's
+arrays; a debugging library, see mx_bounds_checked in include/mxmoe.h).
 
-    python -m combine_topk_ids_expert_amd.build
+    python -m combine_topk_ids_expert_amd.build            # both
+    python -m combine_topk_ids_expert_amd.build --product  # libmxmoe.so only
 
-The library is written next to this file, where the binding loads it.
+The libraries are written next to this file, where the binding loads them.
 """
 
 from __future__ import annotations
@@ -17,6 +21,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmxmoe.so")
+LIB_CHECKED = os.path.join(PKG, "libmxmoe_checked.so")
+CHECKED_FLAGS = ["-DMXMOE_CHECKED=1"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -49,5 +55,21 @@ def build(out_path: str = LIB, extra_flags: list[str] | None = None, verbose: bo
     return out_path
 
 
+def build_checked(out_path: str = LIB_CHECKED, verbose: bool = False) -> str:
+    return build(out_path, CHECKED_FLAGS, verbose)
+
+
+def build_all(verbose: bool = False) -> list[str]:
+    """Both libraries, compiled side by side."""
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(2) as pool:
+        jobs = [pool.submit(build, LIB, None, verbose), pool.submit(build_checked, LIB_CHECKED, verbose)]
+        return [j.result() for j in jobs]
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    v = "-v" in sys.argv
+    if "--product" in sys.argv:
+        print(build(verbose=v))
+    else:
+        print("\n".join(build_all(verbose=v)))

@@ -4,10 +4,15 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <initializer_list>
 #include <mutex>
+#include <vector>
 
 #include "../../include/mxmoe.h"
 #include "launch.h"
+#ifdef MXMOE_CHECKED
+#include "device_common.h"
+#endif
 
 // Routing scratch of mx_prepare_moe_input_noalloc: the count table, in a
 // file-scope device array (each GPU the library runs on holds its own copy
@@ -71,6 +76,85 @@ hipError_t scratch_for_current_device(void** ptr) {
 
 }  // namespace
 
+// ---- bounds-checked build: the host side -----------------------------------
+// Every launching entry point runs its launches through MX_BOUNDED(stream,
+// call, arrays...), naming each array the call's kernels may touch with its
+// extent in bytes and whether they may write it.  In the normal build that is
+// just `call`.  In the checked build (MXMOE_CHECKED) it waits for the device,
+// writes the arrays into the check table of every translation unit with
+// kernels, runs the call, waits again and collects what the kernels counted.
+#ifdef MXMOE_CHECKED
+namespace mxmoe {
+std::vector<CheckHooks>& check_hooks() {
+    static std::vector<CheckHooks> hooks;
+    return hooks;
+}
+int register_check_hooks(const CheckHooks& hooks) {
+    check_hooks().push_back(hooks);
+    return (int)check_hooks().size();
+}
+}  // namespace mxmoe
+
+namespace {
+
+struct Buf {
+    const void* p;
+    int64_t bytes;
+    bool writable;
+};
+
+std::mutex g_bounds_mutex;
+int64_t g_bounds_shrink = 0;
+uint64_t g_bounds_report[mxmoe::kCheckReportWords];
+
+template <typename F>
+mx_status bounded(void* stream, std::initializer_list<Buf> bufs, F&& call) {
+    std::lock_guard<std::mutex> lock(g_bounds_mutex);
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(st, &cs);
+    if (e != hipSuccess) return hip_status(e);
+    if (cs != hipStreamCaptureStatusNone) return hip_status(hipErrorStreamCaptureUnsupported);
+    mxmoe::CheckTable t{};
+    for (const Buf& b : bufs) {
+        if (b.p == nullptr || b.bytes <= 0) continue;
+        if (t.n == (uint32_t)mxmoe::kMaxCheckRanges) return MX_ERR_INVALID_ARGUMENT;
+        int64_t n = b.bytes;
+        if (b.writable) n = n > g_bounds_shrink ? n - g_bounds_shrink : 0;
+        const uint64_t lo = (uint64_t)(uintptr_t)b.p;
+        t.r[t.n++] = mxmoe::CheckRange{lo, lo + (uint64_t)n, b.writable ? 1u : 0u, 0u};
+    }
+    // No kernel of an earlier call may still read the table being replaced.
+    if ((e = hipDeviceSynchronize()) != hipSuccess) return hip_status(e);
+    for (const mxmoe::CheckHooks& h : mxmoe::check_hooks()) {
+        unsigned long long stale[mxmoe::kCheckReportWords];
+        if ((e = h.set_table(t)) != hipSuccess || (e = h.take_report(stale)) != hipSuccess)
+            return hip_status(e);
+    }
+    const mx_status status = call();
+    if ((e = hipDeviceSynchronize()) != hipSuccess) return hip_status(e);
+    uint64_t bad = 0;
+    for (const mxmoe::CheckHooks& h : mxmoe::check_hooks()) {
+        unsigned long long r[mxmoe::kCheckReportWords];
+        if ((e = h.take_report(r)) != hipSuccess) return hip_status(e);
+        g_bounds_report[0] += r[0];
+        g_bounds_report[1] += r[1];
+        if (g_bounds_report[3] == 0 && r[3] != 0) {
+            g_bounds_report[2] = r[2];
+            g_bounds_report[3] = r[3];
+        }
+        bad += r[0] + r[1];
+    }
+    return status == MX_OK && bad != 0 ? MX_ERR_OUT_OF_BOUNDS : status;
+}
+
+}  // namespace
+#define MX_BOUNDED(stream, call, ...) \
+    bounded((stream), {__VA_ARGS__}, [&]() -> mx_status { return (call); })
+#else
+#define MX_BOUNDED(stream, call, ...) (call)
+#endif
+
 namespace {
 
 // Argument checks of the row dispatch.
@@ -103,11 +187,18 @@ mx_status dispatch_rows(const void* src, int64_t num_tokens, int32_t topk, int64
     if (st != MX_OK) return st;
     const bool side = side_src != nullptr;
     if (num_tokens == 0 || num_dst_rows == 0) return MX_OK;
-    return hip_status(mxmoe::launch_dispatch_rows(
-        src, num_tokens, topk, row_bytes, output_permutation, dst, num_dst_rows,
-        side ? side_src : nullptr, side ? side_row_bytes : 0, side ? side_dst : nullptr,
-        static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(start_event),
-        static_cast<hipEvent_t>(stop_event)));
+    return MX_BOUNDED(
+        stream,
+        hip_status(mxmoe::launch_dispatch_rows(
+            src, num_tokens, topk, row_bytes, output_permutation, dst, num_dst_rows,
+            side ? side_src : nullptr, side ? side_row_bytes : 0, side ? side_dst : nullptr,
+            static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(start_event),
+            static_cast<hipEvent_t>(stop_event))),
+        Buf{src, num_tokens * row_bytes, false},
+        Buf{output_permutation, num_tokens * topk * 4, false},
+        Buf{dst, num_dst_rows * row_bytes, true},
+        Buf{side ? side_src : nullptr, num_tokens * side_row_bytes, false},
+        Buf{side ? side_dst : nullptr, num_dst_rows * side_row_bytes, true});
 }
 
 mx_status apply_shuffle_mul_sum(const void* y, int32_t y_dtype, int64_t num_y_rows,
@@ -128,11 +219,17 @@ mx_status apply_shuffle_mul_sum(const void* y, int32_t y_dtype, int64_t num_y_ro
         (factors != nullptr && !aligned(factors, (size_t)elem_bytes(factors_dtype))))
         return MX_ERR_MISALIGNED;
     if (num_tokens == 0 || hidden == 0) return MX_OK;
-    return hip_status(mxmoe::launch_combine(y, y_dtype, num_y_rows, hidden, permutation, factors,
-                                            factors_dtype, num_tokens, topk, out, out_dtype,
-                                            static_cast<hipStream_t>(stream),
-                                            static_cast<hipEvent_t>(start_event),
-                                            static_cast<hipEvent_t>(stop_event)));
+    return MX_BOUNDED(
+        stream,
+        hip_status(mxmoe::launch_combine(y, y_dtype, num_y_rows, hidden, permutation, factors,
+                                         factors_dtype, num_tokens, topk, out, out_dtype,
+                                         static_cast<hipStream_t>(stream),
+                                         static_cast<hipEvent_t>(start_event),
+                                         static_cast<hipEvent_t>(stop_event))),
+        Buf{y, num_y_rows * hidden * yb, false},
+        Buf{permutation, num_tokens * topk * 4, false},
+        Buf{factors, factors ? num_tokens * topk * elem_bytes(factors_dtype) : 0, false},
+        Buf{out, num_tokens * hidden * ob, true});
 }
 
 // The dispatch half of prepare_dispatch (arguments already checked).
@@ -214,20 +311,39 @@ mx_status prepare_moe_input(const void* topk_ids, int32_t ids_dtype, int64_t num
     a.output_perm = output_permutation;
     a.workspace = static_cast<int32_t*>(workspace);
     const hipStream_t st = static_cast<hipStream_t>(stream);
-    if (rows == nullptr)
-        return hip_status(mxmoe::launch_route(a, st, static_cast<hipEvent_t>(start_event),
-                                              static_cast<hipEvent_t>(stop_event)));
-    if (rows->num_dst_rows > 0 && rows->side_src == nullptr &&
-        mxmoe::route_dispatch_fusable(a, num_tokens, rows->row_bytes, rows->src, rows->dst))
-        return hip_status(mxmoe::launch_route_dispatch(a, num_tokens, rows->src,
-                                                       rows->row_bytes, rows->dst,
-                                                       rows->num_dst_rows, st));
-    const mx_status r = hip_status(mxmoe::launch_route(a, st));
-    if (r != MX_OK || num_tokens == 0 || rows->num_dst_rows == 0) return r;
-    return hip_status(mxmoe::launch_dispatch_rows(
-        rows->src, num_tokens, topk, rows->row_bytes, output_permutation, rows->dst,
-        rows->num_dst_rows, rows->side_src, rows->side_row_bytes, rows->side_dst, st, nullptr,
-        nullptr));
+    auto run = [&]() -> mx_status {
+        if (rows == nullptr)
+            return hip_status(mxmoe::launch_route(a, st, static_cast<hipEvent_t>(start_event),
+                                                  static_cast<hipEvent_t>(stop_event)));
+        if (rows->num_dst_rows > 0 && rows->side_src == nullptr &&
+            mxmoe::route_dispatch_fusable(a, num_tokens, rows->row_bytes, rows->src, rows->dst))
+            return hip_status(mxmoe::launch_route_dispatch(a, num_tokens, rows->src,
+                                                           rows->row_bytes, rows->dst,
+                                                           rows->num_dst_rows, st));
+        const mx_status r = hip_status(mxmoe::launch_route(a, st));
+        if (r != MX_OK || num_tokens == 0 || rows->num_dst_rows == 0) return r;
+        return hip_status(mxmoe::launch_dispatch_rows(
+            rows->src, num_tokens, topk, rows->row_bytes, output_permutation, rows->dst,
+            rows->num_dst_rows, rows->side_src, rows->side_row_bytes, rows->side_dst, st,
+            nullptr, nullptr));
+    };
+    [[maybe_unused]] const int64_t meta = ((int64_t)num_experts + 1) * 4;
+    return MX_BOUNDED(
+        stream, run(),
+        Buf{topk_ids, n * (ids_dtype == MX_I64 ? 8 : 4), false},
+        Buf{expert_offsets, meta, true},
+        Buf{problem_sizes1, (int64_t)num_experts * 12, true},
+        Buf{problem_sizes2, (int64_t)num_experts * 12, true},
+        Buf{input_permutation, input_permutation_len * 4, true},
+        Buf{output_permutation, n * 4, true},
+        Buf{blockscale_offsets, meta, true},
+        Buf{need > 0 ? workspace : nullptr, (int64_t)need, true},
+        Buf{rows ? rows->src : nullptr, rows ? num_tokens * rows->row_bytes : 0, false},
+        Buf{rows ? rows->dst : nullptr, rows ? rows->num_dst_rows * rows->row_bytes : 0, true},
+        Buf{rows ? rows->side_src : nullptr, rows ? num_tokens * rows->side_row_bytes : 0,
+            false},
+        Buf{rows ? rows->side_dst : nullptr,
+            rows ? rows->num_dst_rows * rows->side_row_bytes : 0, true});
 }
 
 }  // namespace
@@ -243,12 +359,46 @@ const char* mx_status_string(mx_status s) {
     case MX_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case MX_ERR_CAPACITY: return "input_permutation shorter than the dispatch capacity";
     case MX_ERR_HIP: return "HIP launch error";
+    case MX_ERR_OUT_OF_BOUNDS: return "a kernel access fell outside the call's arrays";
     default: break;
     }
     return "unknown status";
 }
 
 int mx_last_hip_error(void) { return g_last_hip_error; }
+
+#ifdef MXMOE_CHECKED
+int32_t mx_bounds_checked(void) { return 1; }
+
+mx_status mx_bounds_report(uint64_t* report, int32_t clear) {
+    if (report == nullptr) return MX_ERR_INVALID_ARGUMENT;
+    std::lock_guard<std::mutex> lock(g_bounds_mutex);
+    for (int i = 0; i < mxmoe::kCheckReportWords; ++i) report[i] = g_bounds_report[i];
+    if (clear)
+        for (int i = 0; i < mxmoe::kCheckReportWords; ++i) g_bounds_report[i] = 0;
+    return MX_OK;
+}
+
+mx_status mx_bounds_shrink_outputs(int64_t bytes) {
+    if (bytes < 0) return MX_ERR_INVALID_ARGUMENT;
+    std::lock_guard<std::mutex> lock(g_bounds_mutex);
+    g_bounds_shrink = bytes;
+    return MX_OK;
+}
+#else
+int32_t mx_bounds_checked(void) { return 0; }
+
+mx_status mx_bounds_report(uint64_t* report, int32_t clear) {
+    (void)clear;
+    if (report == nullptr) return MX_ERR_INVALID_ARGUMENT;
+    for (int i = 0; i < 4; ++i) report[i] = 0;
+    return MX_OK;
+}
+
+mx_status mx_bounds_shrink_outputs(int64_t bytes) {
+    return bytes == 0 ? MX_OK : MX_ERR_INVALID_ARGUMENT;
+}
+#endif
 
 int64_t mx_dispatch_capacity(int64_t num_tokens, int32_t topk, int32_t num_experts,
                              int32_t row_align) {
@@ -349,9 +499,13 @@ mx_status mx_shuffle_rows(const void* src, int64_t num_src_rows, int64_t row_byt
         return MX_ERR_INVALID_ARGUMENT;
     if (!aligned(dst2src, 4)) return MX_ERR_MISALIGNED;
     if (num_dst_rows == 0) return MX_OK;
-    return hip_status(mxmoe::launch_shuffle_rows(src, num_src_rows, row_bytes, dst2src,
-                                                 num_dst_rows, dst,
-                                                 static_cast<hipStream_t>(stream)));
+    return MX_BOUNDED(stream,
+                      hip_status(mxmoe::launch_shuffle_rows(src, num_src_rows, row_bytes,
+                                                            dst2src, num_dst_rows, dst,
+                                                            static_cast<hipStream_t>(stream))),
+                      Buf{src, num_src_rows * row_bytes, false},
+                      Buf{dst2src, num_dst_rows * 4, false},
+                      Buf{dst, num_dst_rows * row_bytes, true});
 }
 
 
@@ -402,9 +556,12 @@ mx_status mx_moe_output_memset(void* out, int64_t num_tokens, int32_t topk, int6
         return MX_ERR_INVALID_ARGUMENT;
     if (!aligned(output_permutation, 4)) return MX_ERR_MISALIGNED;
     if (num_tokens == 0) return MX_OK;
-    return hip_status(mxmoe::launch_output_memset(out, num_tokens, topk, row_bytes,
-                                                  output_permutation,
-                                                  static_cast<hipStream_t>(stream)));
+    return MX_BOUNDED(stream,
+                      hip_status(mxmoe::launch_output_memset(out, num_tokens, topk, row_bytes,
+                                                             output_permutation,
+                                                             static_cast<hipStream_t>(stream))),
+                      Buf{out, num_tokens * row_bytes, true},
+                      Buf{output_permutation, num_tokens * topk * 4, false});
 }
 
 mx_status mx_zero_padding_rows(void* rows, int64_t num_rows, int64_t row_bytes,
@@ -418,9 +575,14 @@ mx_status mx_zero_padding_rows(void* rows, int64_t num_rows, int64_t row_bytes,
         return MX_ERR_INVALID_ARGUMENT;
     if (!aligned(input_permutation, 4) || !aligned(expert_offsets, 4)) return MX_ERR_MISALIGNED;
     if (num_rows == 0) return MX_OK;
-    return hip_status(mxmoe::launch_zero_padding(rows, num_rows, row_bytes, input_permutation,
-                                                 expert_offsets, num_experts,
-                                                 static_cast<hipStream_t>(stream)));
+    return MX_BOUNDED(stream,
+                      hip_status(mxmoe::launch_zero_padding(rows, num_rows, row_bytes,
+                                                            input_permutation, expert_offsets,
+                                                            num_experts,
+                                                            static_cast<hipStream_t>(stream))),
+                      Buf{rows, num_rows * row_bytes, true},
+                      Buf{input_permutation, num_rows * 4, false},
+                      Buf{expert_offsets, ((int64_t)num_experts + 1) * 4, false});
 }
 
 mx_status mx_moe_sort(const void* topk_ids, int32_t ids_dtype, int64_t num_tokens, int32_t topk,
@@ -478,7 +640,16 @@ mx_status mx_moe_sort(const void* topk_ids, int32_t ids_dtype, int64_t num_token
     a.max_tiles = max_tiles;
     a.padded_total = total_num_padded_tokens;
     a.tile_count = num_non_exiting_tiles;
-    return hip_status(mxmoe::launch_route(a, static_cast<hipStream_t>(stream)));
+    return MX_BOUNDED(stream, hip_status(mxmoe::launch_route(a, static_cast<hipStream_t>(stream))),
+                      Buf{topk_ids, n * (ids_dtype == MX_I64 ? 8 : 4), false},
+                      Buf{expanded_idx_to_permuted_idx, n * 4, true},
+                      Buf{permuted_idx_to_expanded_idx, permuted_capacity * 4, true},
+                      Buf{tile_idx_to_group_idx, max_tiles * 4, true},
+                      Buf{tile_idx_to_mn_limit, max_tiles * 4, true},
+                      Buf{total_num_padded_tokens, 4, true},
+                      Buf{num_non_exiting_tiles, 4, true},
+                      Buf{expert_offsets, ((int64_t)num_local_experts + 1) * 4, true},
+                      Buf{need > 0 ? workspace : nullptr, (int64_t)need, true});
 }
 
 mx_status mx_dispatch_rows_fp8(const void* src, int32_t src_dtype, int64_t num_tokens,
@@ -497,10 +668,14 @@ mx_status mx_dispatch_rows_fp8(const void* src, int32_t src_dtype, int64_t num_t
         !aligned(output_permutation, 4))
         return MX_ERR_MISALIGNED;
     if (num_tokens == 0 || num_dst_rows == 0) return MX_OK;
-    return hip_status(mxmoe::launch_dispatch_quant_fp8(src, num_tokens, topk, hidden,
-                                                       output_permutation, dst_q, dst_scales,
-                                                       num_dst_rows,
-                                                       static_cast<hipStream_t>(stream)));
+    return MX_BOUNDED(stream,
+                      hip_status(mxmoe::launch_dispatch_quant_fp8(
+                          src, num_tokens, topk, hidden, output_permutation, dst_q, dst_scales,
+                          num_dst_rows, static_cast<hipStream_t>(stream))),
+                      Buf{src, num_tokens * hidden * 2, false},
+                      Buf{output_permutation, num_tokens * topk * 4, false},
+                      Buf{dst_q, num_dst_rows * hidden, true},
+                      Buf{dst_scales, num_dst_rows * (hidden / 128) * 4, true});
 }
 
 }  // extern "C"

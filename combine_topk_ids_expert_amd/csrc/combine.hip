@@ -64,6 +64,7 @@ struct Cols {
 template <typename TY, int N>
 __device__ __forceinline__ Cols<TY, N> load_cols(const typename TY::storage* p) {
     Cols<TY, N> v;
+    if (!MX_CAN_LOAD(p, (Cols<TY, N>::kBytes), kSiteCombineY)) return Cols<TY, N>{};
     if constexpr (Cols<TY, N>::kBytes == 16) {
         const u32x4 q = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 #pragma unroll
@@ -97,10 +98,11 @@ __device__ __forceinline__ void store_cols(typename TO::storage* row, int64_t hi
     if constexpr (kBytes == 16) {
         const u32x4 q = {w[0], w[1], w[2], w[3]};
         store16<P>(q, reinterpret_cast<uint8_t*>(row), hidden * (int64_t)sizeof(SO),
-                   col * (int64_t)sizeof(SO));
+                   col * (int64_t)sizeof(SO), kSiteCombineOut);
     } else {
         const u32x2 q = {w[0], w[1]};
-        __builtin_nontemporal_store(q, reinterpret_cast<u32x2*>(row + col));
+        if (MX_CAN_STORE(row + col, 8, kSiteCombineOut))
+            __builtin_nontemporal_store(q, reinterpret_cast<u32x2*>(row + col));
     }
 }
 
@@ -124,9 +126,11 @@ __device__ __forceinline__ float load_factor(const void* f, int64_t idx) {
     if constexpr (FDT < 0) {
         return 1.0f;
     } else if constexpr (FDT == 0) {
-        return static_cast<const float*>(f)[idx];
+        const float* q = static_cast<const float*>(f) + idx;
+        return MX_CAN_LOAD(q, 4, kSiteCombineFactor) ? *q : 0.0f;
     } else {
-        const uint16_t h = static_cast<const uint16_t*>(f)[idx];
+        const uint16_t* q = static_cast<const uint16_t*>(f) + idx;
+        const uint16_t h = MX_CAN_LOAD(q, 2, kSiteCombineFactor) ? *q : (uint16_t)0;
         if constexpr (FDT == 1) return to_f32(F16{}, h);
         else return to_f32(BF16{}, h);
     }
@@ -176,7 +180,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_vec_kernel(
         int my_r = -1;
         float my_w = 0.0f;
         if (lane < nj) {
-            my_r = rows[j0 + lane];
+            my_r = MX_CAN_LOAD(rows + j0 + lane, 4, kSiteCombineIndex) ? rows[j0 + lane] : -1;
             if (my_r >= num_y_rows) my_r = -1;
             my_w = load_factor<FDT>(factors, t * topk + j0 + lane);
         }
@@ -255,12 +259,16 @@ __global__ __launch_bounds__(kCombineThreads) void combine_scalar_kernel(
     const int32_t* rows = perm + t * topk;
     float acc = 0.0f;
     for (int j = 0; j < topk; ++j) {
-        const int32_t r = rows[j];
+        const int32_t r = MX_CAN_LOAD(rows + j, 4, kSiteCombineIndex) ? rows[j] : -1;
         if (r < 0 || r >= num_y_rows) continue;
         const float w = load_factor<FDT>(factors, t * topk + j);
-        acc = __builtin_fmaf(to_f32(TY{}, y[(int64_t)r * hidden + h]), w, acc);
+        const typename TY::storage* q = y + (int64_t)r * hidden + h;
+        const typename TY::storage x =
+            MX_CAN_LOAD(q, sizeof(*q), kSiteCombineY) ? *q : typename TY::storage{};
+        acc = __builtin_fmaf(to_f32(TY{}, x), w, acc);
     }
-    out[t * hidden + h] = from_f32(TO{}, acc);
+    if (MX_CAN_STORE(out + t * hidden + h, sizeof(*out), kSiteCombineOut))
+        out[t * hidden + h] = from_f32(TO{}, acc);
 }
 
 template <typename TY, typename TO, int FDT>

@@ -102,13 +102,122 @@ inline StorePolicy dispatch_store_policy(int64_t source_bytes) {
     return source_bytes > kCacheResidentBytes ? kKeep : kStream;
 }
 
+// ---- bounds-checked build ----------------------------------------------------
+// Built with MXMOE_CHECKED defined (libmxmoe_checked.so), every global load
+// and store of the kernels is first checked against the buffers of the call
+// that launched it, which the C ABI writes into this translation unit's
+// g_check_table before its launches.  An access that does not lie wholly
+// inside one of them (or that stores into a read-only one) is counted in
+// g_check_report and skipped, a load giving zeros, so the kernel still ends
+// normally; the entry point then returns MX_ERR_OUT_OF_BOUNDS.  Indices into
+// LDS arrays that come from data are checked against the array's length the
+// same way.  In the normal build every check is the constant `true` and the
+// kernels compile to the same code as without them.
+enum CheckSite : int {
+    kSiteIds = 1,          // routing: topk ids
+    kSiteTableLoad,        // routing: count table, loads
+    kSiteTableStore,       // routing: count table, stores
+    kSiteOutPerm,          // routing: output permutation
+    kSiteInPerm,           // routing: input permutation (scatter and unused rows)
+    kSiteMeta,             // routing: offsets, problem sizes, block-scale offsets
+    kSiteTiles,            // routing: tile maps and totals
+    kSiteLocal,            // routing: LDS arrays indexed by data
+    kSiteRowSrc,           // row copies: source vectors
+    kSiteRowIndex,         // row copies: destination / source row indices
+    kSiteRowDst,           // row copies: destination vectors
+    kSiteCombineIndex,     // combine: row indices
+    kSiteCombineFactor,    // combine: weights
+    kSiteCombineY,         // combine: expert output rows
+    kSiteCombineOut,       // combine: output rows
+    kSiteZeroIndex,        // zeroing: permutation entries and expert offsets
+    kSiteZeroRows,         // zeroing: zeroed rows
+    kSiteQuantSrc,         // fp8 dispatch: source rows
+    kSiteQuantIndex,       // fp8 dispatch: destination row indices
+    kSiteQuantCodes,       // fp8 dispatch: code rows
+    kSiteQuantScales,      // fp8 dispatch: scale rows
+};
+
+#ifdef MXMOE_CHECKED
+struct CheckRange {
+    uint64_t lo, hi;       // [lo, hi) in bytes
+    uint32_t writable, pad;
+};
+constexpr int kMaxCheckRanges = 16;
+struct CheckTable {
+    uint32_t n, pad;
+    CheckRange r[kMaxCheckRanges];
+};
+// [0] loads outside, [1] stores outside, [2] the address and [3] the site of
+// the first access counted (site 0: none yet).
+constexpr int kCheckReportWords = 4;
+
+static __device__ CheckTable g_check_table;
+static __device__ unsigned long long g_check_report[kCheckReportWords];
+
+[[maybe_unused]] static __device__ __noinline__ bool check_access(uint64_t lo, uint64_t bytes, bool store, int site) {
+    const uint32_t n = g_check_table.n < kMaxCheckRanges ? g_check_table.n : kMaxCheckRanges;
+    for (uint32_t i = 0; i < n; ++i) {
+        const CheckRange& r = g_check_table.r[i];
+        if (lo >= r.lo && lo + bytes <= r.hi && (r.writable || !store)) return true;
+    }
+    atomicAdd(&g_check_report[store ? 1 : 0], 1ull);
+    if (atomicCAS(&g_check_report[3], 0ull, (unsigned long long)site) == 0ull)
+        atomicExch(&g_check_report[2], (unsigned long long)lo);
+    return false;
+}
+
+[[maybe_unused]] static __device__ __noinline__ bool check_index(int64_t i, int64_t n, int site) {
+    if (i >= 0 && i < n) return true;
+    atomicAdd(&g_check_report[1], 1ull);
+    if (atomicCAS(&g_check_report[3], 0ull, (unsigned long long)site) == 0ull)
+        atomicExch(&g_check_report[2], (unsigned long long)i);
+    return false;
+}
+
+#define MX_CAN_LOAD(p, bytes, site) \
+    ::mxmoe::check_access((uint64_t)(uintptr_t)(p), (uint64_t)(bytes), false, (site))
+#define MX_CAN_STORE(p, bytes, site) \
+    ::mxmoe::check_access((uint64_t)(uintptr_t)(p), (uint64_t)(bytes), true, (site))
+#define MX_IN_RANGE(i, n, site) ::mxmoe::check_index((int64_t)(i), (int64_t)(n), (site))
+
+// Host side: the C ABI sets the table and collects the report of every
+// translation unit that launches kernels, through the hooks each one
+// registers at load time (a `static __device__` variable is one per
+// translation unit).
+struct CheckHooks {
+    hipError_t (*set_table)(const CheckTable&);
+    hipError_t (*take_report)(unsigned long long (&)[kCheckReportWords]);
+};
+int register_check_hooks(const CheckHooks& hooks);   // api.hip
+
+namespace {
+hipError_t set_check_table(const CheckTable& t) {
+    return hipMemcpyToSymbol(HIP_SYMBOL(g_check_table), &t, sizeof(t));
+}
+hipError_t take_check_report(unsigned long long (&r)[kCheckReportWords]) {
+    hipError_t e = hipMemcpyFromSymbol(r, HIP_SYMBOL(g_check_report), sizeof(r));
+    if (e != hipSuccess) return e;
+    static const unsigned long long zero[kCheckReportWords] = {};
+    return hipMemcpyToSymbol(HIP_SYMBOL(g_check_report), zero, sizeof(zero));
+}
+const int g_check_hooks_registered =
+    register_check_hooks(CheckHooks{&set_check_table, &take_check_report});
+}  // namespace
+#else
+#define MX_CAN_LOAD(p, bytes, site) true
+#define MX_CAN_STORE(p, bytes, site) true
+#define MX_IN_RANGE(i, n, site) true
+#endif
+
 // 16-byte store of vector v at byte offset `off` of a row that starts at
 // `row` (the row base wave-uniform, the offset per lane), through a raw
 // buffer store with cache policy P.  The buffer's extent is the row, so a
 // store past row_bytes would be dropped by the hardware; callers only store
 // inside it.  0x00020000 is the gfx9 raw-buffer format word.
 template <int P>
-__device__ __forceinline__ void store16(u32x4 v, uint8_t* row, int64_t row_bytes, int64_t off) {
+__device__ __forceinline__ void store16(u32x4 v, uint8_t* row, int64_t row_bytes, int64_t off,
+                                        int site) {
+    if (!MX_CAN_STORE(row + off, 16, site)) return;
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc(row, (short)0, (int)row_bytes, 0x00020000);
     __builtin_amdgcn_raw_buffer_store_b128(v, rs, (int)off, 0, P);

@@ -79,7 +79,7 @@ __global__ __launch_bounds__(kQuantThreads) void dispatch_quant_fp8_kernel(
     const int64_t col = (chunk * blockDim.x + threadIdx.x) * kElemsPerThread;
     const bool live = col < hidden;                    // whole groups: a group is live or not
     u32x4 v0 = {0u, 0u, 0u, 0u}, v1 = {0u, 0u, 0u, 0u};
-    if (live) {
+    if (live && MX_CAN_LOAD(src + t * hidden + col, 32, kSiteQuantSrc)) {
         const u32x4* p = reinterpret_cast<const u32x4*>(src + t * hidden + col);
         v0 = __builtin_nontemporal_load(p);
         v1 = __builtin_nontemporal_load(p + 1);
@@ -111,14 +111,16 @@ __global__ __launch_bounds__(kQuantThreads) void dispatch_quant_fp8_kernel(
     const int32_t* rows = output_perm + t * topk;
     for (int j0 = 0; j0 < topk; j0 += kWave) {         // wave-uniform
         const int nj = topk - j0 < kWave ? topk - j0 : kWave;
-        int my_r = lane < nj ? rows[j0 + lane] : -1;
+        int my_r = -1;
+        if (lane < nj && MX_CAN_LOAD(rows + j0 + lane, 4, kSiteQuantIndex)) my_r = rows[j0 + lane];
         if (my_r >= num_dst_rows) my_r = -1;
         for (int j = 0; j < nj; ++j) {
             const int32_t r = __builtin_amdgcn_readlane(my_r, j);
             if (r < 0) continue;
             if (live)
-                store16<kStream>(codes, dst_q + (int64_t)r * hidden, hidden, col);
-            if (scale_lane)
+                store16<kStream>(codes, dst_q + (int64_t)r * hidden, hidden, col, kSiteQuantCodes);
+            if (scale_lane &&
+                MX_CAN_STORE(dst_scales + (int64_t)r * groups + wave_group0 + lane, 4, kSiteQuantScales))
                 __builtin_nontemporal_store(wave_scale, dst_scales + (int64_t)r * groups + wave_group0 + lane);
         }
     }

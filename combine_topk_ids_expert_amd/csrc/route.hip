@@ -127,7 +127,8 @@ __device__ __forceinline__ void load_raw(const IdT* ids, int64_t g0, int64_t w1,
 #pragma unroll
     for (int b = 0; b < kBatch; ++b) {
         const int64_t i = g0 + b * kWave + lane;
-        v[b] = g0 + b * kWave < w1 ? ids[i < w1 ? i : w1 - 1] : IdT(0);
+        const IdT* p = ids + (i < w1 ? i : w1 - 1);
+        v[b] = g0 + b * kWave < w1 && MX_CAN_LOAD(p, sizeof(IdT), kSiteIds) ? *p : IdT(0);
     }
 }
 
@@ -162,7 +163,7 @@ __device__ __forceinline__ void count_keys(const int (&key)[kBatch], int64_t g0,
 #pragma unroll
     for (int b = 0; b < kBatch; ++b) {
         if (g0 + b * kWave >= w1) break;                // wave-uniform
-        if (key[b] >= 0) atomicAdd(&row[key[b]], 1);
+        if (key[b] >= 0 && MX_IN_RANGE(key[b], s.E, kSiteLocal)) atomicAdd(&row[key[b]], 1);
     }
 }
 
@@ -182,15 +183,19 @@ __device__ __forceinline__ void scatter_keys(const int (&key)[kBatch], int64_t g
         const int64_t i = g0 + b * kWave + lane;
         const uint64_t m = match_key(key[b], s.nbits);
         const int rank = lanes_below(m);
-        if (key[b] >= 0) {
+        const bool key_ok = key[b] >= 0 && MX_IN_RANGE(key[b], s.E, kSiteLocal);
+        if (key_ok) {
             const int r = row[key[b]] + rank;   // every lane reads before the update below
-            outp[i] = r;
-            if (!kLocal && r < inp_len)
+            if (kLocal ? MX_IN_RANGE(i, kFusedMax, kSiteLocal)
+                       : MX_CAN_STORE(outp + i, 4, kSiteOutPerm))
+                outp[i] = r;
+            if (!kLocal && r < inp_len && MX_CAN_STORE(inp + r, 4, kSiteInPerm))
                 inp[r] = s.expanded ? (int32_t)i : (int32_t)((uint32_t)i / (uint32_t)s.k);
-        } else if (i < w1) {
+        } else if (i < w1 && (kLocal ? MX_IN_RANGE(i, kFusedMax, kSiteLocal)
+                                     : MX_CAN_STORE(outp + i, 4, kSiteOutPerm))) {
             outp[i] = -1;
         }
-        if (key[b] >= 0 && rank == 0) row[key[b]] += __popcll(m);
+        if (key_ok && rank == 0) row[key[b]] += __popcll(m);
     }
 }
 
@@ -252,22 +257,26 @@ __device__ int scan_experts(const RouteArgs& a, const int* cnt, int* off, int* t
         return tmp[128];
     }
     if (tid == 0) {
-        if (a.expert_offsets) a.expert_offsets[0] = 0;
-        if (a.blockscale_offsets) a.blockscale_offsets[0] = 0;
+        if (a.expert_offsets && MX_CAN_STORE(a.expert_offsets, 4, kSiteMeta))
+            a.expert_offsets[0] = 0;
+        if (a.blockscale_offsets && MX_CAN_STORE(a.blockscale_offsets, 4, kSiteMeta))
+            a.blockscale_offsets[0] = 0;
     }
     for (int e = e0; e < e1; ++e) {
         const int c = cnt[e];
         off[e] = xr;
         xr += round_up_i(c, a.row_align);
         xb += round_up_i(c, a.bs_align);
-        if (a.expert_offsets) a.expert_offsets[e + 1] = xr;
-        if (a.blockscale_offsets) a.blockscale_offsets[e + 1] = xb;
-        if (a.problem_sizes1) {
+        if (a.expert_offsets && MX_CAN_STORE(a.expert_offsets + e + 1, 4, kSiteMeta))
+            a.expert_offsets[e + 1] = xr;
+        if (a.blockscale_offsets && MX_CAN_STORE(a.blockscale_offsets + e + 1, 4, kSiteMeta))
+            a.blockscale_offsets[e + 1] = xb;
+        if (a.problem_sizes1 && MX_CAN_STORE(a.problem_sizes1 + 3 * e, 12, kSiteMeta)) {
             a.problem_sizes1[3 * e] = c;
             a.problem_sizes1[3 * e + 1] = a.gemm[0];
             a.problem_sizes1[3 * e + 2] = a.gemm[1];
         }
-        if (a.problem_sizes2) {
+        if (a.problem_sizes2 && MX_CAN_STORE(a.problem_sizes2 + 3 * e, 12, kSiteMeta)) {
             a.problem_sizes2[3 * e] = c;
             a.problem_sizes2[3 * e + 1] = a.gemm[2];
             a.problem_sizes2[3 * e + 2] = a.gemm[3];
@@ -299,11 +308,13 @@ __device__ void fill_unused_rows(const RouteArgs& a, const int* cnt, const int* 
             const int l = __builtin_ctzll(todo);
             todo &= todo - 1;
             const int p0 = __builtin_amdgcn_readlane(r0, l), pn = __builtin_amdgcn_readlane(n, l);
-            for (int q = lane; q < pn; q += kWave) a.input_perm[(int64_t)p0 + q] = -1;
+            for (int q = lane; q < pn; q += kWave)
+                if (MX_CAN_STORE(a.input_perm + (int64_t)p0 + q, 4, kSiteInPerm))
+                    a.input_perm[(int64_t)p0 + q] = -1;
         }
     }
     for (int64_t r = R + first_thread; r < a.input_perm_len; r += thread_stride)
-        a.input_perm[r] = -1;
+        if (MX_CAN_STORE(a.input_perm + r, 4, kSiteInPerm)) a.input_perm[r] = -1;
 }
 
 // Tile maps of the tile-padded sort: the tiles [off[e], off[e] + padded
@@ -334,18 +345,20 @@ __device__ void fill_tiles(const RouteArgs& a, const int* cnt, const int* off, i
             const int pl = __builtin_amdgcn_readlane(lim, l);
             const int pe = first_wave + (j0 + l) * wave_stride;
             for (int q = lane; q < pn; q += kWave) {
-                a.tile_group[(int64_t)p0 + q] = pe;
-                a.tile_limit[(int64_t)p0 + q] = pl;
+                if (MX_CAN_STORE(a.tile_group + (int64_t)p0 + q, 4, kSiteTiles))
+                    a.tile_group[(int64_t)p0 + q] = pe;
+                if (MX_CAN_STORE(a.tile_limit + (int64_t)p0 + q, 4, kSiteTiles))
+                    a.tile_limit[(int64_t)p0 + q] = pl;
             }
         }
     }
     for (int64_t q = R / S + first_thread; q < a.max_tiles; q += thread_stride) {
-        a.tile_group[q] = -1;
-        a.tile_limit[q] = -1;
+        if (MX_CAN_STORE(a.tile_group + q, 4, kSiteTiles)) a.tile_group[q] = -1;
+        if (MX_CAN_STORE(a.tile_limit + q, 4, kSiteTiles)) a.tile_limit[q] = -1;
     }
     if (first_thread == 0) {
-        if (a.padded_total) a.padded_total[0] = R;
-        if (a.tile_count) a.tile_count[0] = R / S;
+        if (a.padded_total && MX_CAN_STORE(a.padded_total, 4, kSiteTiles)) a.padded_total[0] = R;
+        if (a.tile_count && MX_CAN_STORE(a.tile_count, 4, kSiteTiles)) a.tile_count[0] = R / S;
     }
 }
 
@@ -446,14 +459,18 @@ __global__ __launch_bounds__(kRouteThreads) void route_dispatch_kernel(
     const int64_t c = chunk * kRouteThreads + threadIdx.x;
     const bool live = c < nvec;
     u32x4 v{0u, 0u, 0u, 0u};
-    if (live) v = reinterpret_cast<const u32x4*>(src + t * row_bytes)[c];
+    if (live && MX_CAN_LOAD(src + t * row_bytes + c * 16, 16, kSiteRowSrc))
+        v = reinterpret_cast<const u32x4*>(src + t * row_bytes)[c];
     if (blockIdx.x == 0) {
         fused_route<IdT, false>(a, s, rows, cnt, off, tmp, nullptr);
         // This workgroup's own rows: read back what it wrote to output_perm
         // (the same workgroup, ordered by the barrier).
         __syncthreads();
         for (int j = threadIdx.x; j < s.k; j += kRouteThreads)
-            lperm[t * s.k + j] = a.output_perm[t * s.k + j];
+            if (MX_IN_RANGE(t * s.k + j, kFusedMax, kSiteLocal))
+                lperm[t * s.k + j] = MX_CAN_LOAD(a.output_perm + t * s.k + j, 4, kSiteOutPerm)
+                                         ? a.output_perm[t * s.k + j]
+                                         : -1;
     } else {
         fused_route<IdT, true>(a, s, rows, cnt, off, tmp, lperm);
     }
@@ -461,12 +478,14 @@ __global__ __launch_bounds__(kRouteThreads) void route_dispatch_kernel(
     const int lane = threadIdx.x & (kWave - 1);
     for (int j0 = 0; j0 < s.k; j0 += kWave) {
         const int nj = s.k - j0 < kWave ? s.k - j0 : kWave;
-        int my_r = lane < nj ? lperm[t * s.k + j0 + lane] : -1;
+        int my_r = -1;
+        if (lane < nj && MX_IN_RANGE(t * s.k + j0 + lane, kFusedMax, kSiteLocal))
+            my_r = lperm[t * s.k + j0 + lane];
         if (my_r >= num_dst_rows) my_r = -1;
         for (int j = 0; j < nj; ++j) {
             const int32_t r = __builtin_amdgcn_readlane(my_r, j);
             if (r < 0 || !live) continue;
-            store16<P>(v, dst + (int64_t)r * row_bytes, row_bytes, c * 16);
+            store16<P>(v, dst + (int64_t)r * row_bytes, row_bytes, c * 16, kSiteRowDst);
         }
     }
 }
@@ -529,7 +548,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_spread_kernel(RouteArgs a
         for (int u = 0; u < kSpreadBatch; ++u) {
             const int64_t q = (j0 + u) * kRouteThreads + tid;      // q-th pick outside the tile
             idx[u] = q < t0 ? q : q + (t1 - t0);
-            v[u] = ids[q < outside ? idx[u] : s.n - 1];
+            const IdT* p = ids + (q < outside ? idx[u] : s.n - 1);
+            v[u] = MX_CAN_LOAD(p, sizeof(IdT), kSiteIds) ? *p : IdT(0);
         }
         int key8[kSpreadBatch];
         bool one = true;
@@ -624,7 +644,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_count_kernel(RouteArgs a,
         int sum = 0;
 #pragma unroll
         for (int w = 0; w < kRouteWaves; ++w) sum += rows[w][e];
-        a.workspace[(int64_t)e * round_up_i(tiles, 4) + blockIdx.x] = sum;
+        int32_t* slot = a.workspace + (int64_t)e * round_up_i(tiles, 4) + blockIdx.x;
+        if (MX_CAN_STORE(slot, 4, kSiteTableStore)) *slot = sum;
     }
 }
 
@@ -696,10 +717,14 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(RouteArgs 
             // Rows past the last are loaded from row E - 1 and then dropped,
             // so the number of loads in flight does not depend on the data.
             const bool live = it0 + u < iters;           // wave-uniform
-            const u32x4 x0 = row[sub0];
+            const u32x4 x0 = MX_CAN_LOAD(row + sub0, 16, kSiteTableLoad)
+                                 ? row[sub0]
+                                 : u32x4{0u, 0u, 0u, 0u};
             v0[u] = live ? x0 : u32x4{0u, 0u, 0u, 0u};
             if constexpr (two) {
-                const u32x4 x1 = row[sub1];
+                const u32x4 x1 = MX_CAN_LOAD(row + sub1, 16, kSiteTableLoad)
+                                     ? row[sub1]
+                                     : u32x4{0u, 0u, 0u, 0u};
                 v1[u] = live ? x1 : u32x4{0u, 0u, 0u, 0u};
             } else {
                 v1[u] = u32x4{0u, 0u, 0u, 0u};

@@ -58,18 +58,21 @@ __device__ __forceinline__ void copy_vector_to(const T* __restrict__ in, int64_t
     const int lane = threadIdx.x & (kWave - 1);
     const bool live = c < nvec;
     T v{};
-    if (live) v = in[c];
+    if (live && MX_CAN_LOAD(in + c, sizeof(T), kSiteRowSrc)) v = in[c];
     for (int j0 = 0; j0 < n; j0 += kWave) {
         const int nj = n - j0 < kWave ? n - j0 : kWave;
-        int my_r = lane < nj ? (rows ? rows[j0 + lane] : single_row) : -1;
+        int my_r = -1;
+        if (lane < nj)
+            my_r = rows ? (MX_CAN_LOAD(rows + j0 + lane, 4, kSiteRowIndex) ? rows[j0 + lane] : -1)
+                        : single_row;
         if (my_r >= num_dst_rows) my_r = -1;
         for (int j = 0; j < nj; ++j) {
             const int32_t r = __builtin_amdgcn_readlane(my_r, j);
             if (r < 0 || !live) continue;
             uint8_t* row = dst + (int64_t)r * row_bytes;
             if constexpr (sizeof(T) == 16)
-                store16<P>(v, row, row_bytes, c * 16);
-            else
+                store16<P>(v, row, row_bytes, c * 16, kSiteRowDst);
+            else if (MX_CAN_STORE(reinterpret_cast<T*>(row) + c, sizeof(T), kSiteRowDst))
                 __builtin_nontemporal_store(v, reinterpret_cast<T*>(row) + c);
         }
     }
@@ -84,7 +87,7 @@ __global__ __launch_bounds__(kRowThreads) void shuffle_rows_kernel(
     using T = typename Vec<V>::T;
     int64_t chunk;
     const int64_t r = chunk_row(chunks, chunk);
-    const int32_t s = dst2src[r];
+    const int32_t s = MX_CAN_LOAD(dst2src + r, 4, kSiteRowIndex) ? dst2src[r] : -1;
     if (s < 0 || s >= num_src_rows) return;
     const int64_t c = chunk * blockDim.x + threadIdx.x;
     const T* in = reinterpret_cast<const T*>(src + (int64_t)s * row_bytes);

@@ -34,7 +34,8 @@ template <> struct ZVec<1> { using T = uint8_t; };
 template <int V>
 __device__ __forceinline__ void zero_vector(uint8_t* row, int64_t c, int64_t nvec) {
     using T = typename ZVec<V>::T;
-    if (c < nvec) __builtin_nontemporal_store(T{}, reinterpret_cast<T*>(row) + c);
+    if (c < nvec && MX_CAN_STORE(reinterpret_cast<T*>(row) + c, sizeof(T), kSiteZeroRows))
+        __builtin_nontemporal_store(T{}, reinterpret_cast<T*>(row) + c);
 }
 
 // Without expert offsets: row r is zeroed iff its source index is negative
@@ -46,7 +47,7 @@ __global__ __launch_bounds__(kZeroThreads) void zero_padding_kernel(
     int32_t chunks) {
     int64_t chunk;
     const int64_t r = chunk_row(chunks, chunk);
-    if (input_perm[r] >= 0) return;
+    if (!MX_CAN_LOAD(input_perm + r, 4, kSiteZeroIndex) || input_perm[r] >= 0) return;
     zero_vector<V>(rows + r * row_bytes, chunk * blockDim.x + threadIdx.x, row_bytes / V);
 }
 
@@ -77,15 +78,17 @@ __global__ __launch_bounds__(kZeroThreads) void zero_padding_expert_kernel(
     const int e = (int)(es / kSlices);
     const int slice = (int)(es - (int64_t)e * kSlices);
     const int lane = threadIdx.x & (kWave - 1);
-    int64_t seg0 = expert_offsets[e];
-    int64_t seg1 = expert_offsets[e + 1];
+    const bool seg_ok = MX_CAN_LOAD(expert_offsets + e, 8, kSiteZeroIndex);
+    int64_t seg0 = seg_ok ? expert_offsets[e] : 0;
+    int64_t seg1 = seg_ok ? expert_offsets[e + 1] : 0;
     if (seg0 < 0) seg0 = 0;
     if (seg1 > num_rows) seg1 = num_rows;
     const int64_t nvec = row_bytes / V;
     const int64_t c = chunk * blockDim.x + threadIdx.x;
     for (int64_t base = seg0 + slice; base < seg1; base += (int64_t)kSlices * kWave) {
         const int64_t r = base + (int64_t)lane * kSlices;
-        const bool pad = r < seg1 && input_perm[r] < 0;
+        const bool pad =
+            r < seg1 && MX_CAN_LOAD(input_perm + r, 4, kSiteZeroIndex) && input_perm[r] < 0;
         uint64_t m = __ballot(pad);                    // wave-uniform from here on
         while (m != 0ull) {
             const int l = __builtin_ctzll(m);
@@ -107,7 +110,9 @@ __global__ __launch_bounds__(kZeroThreads) void output_memset_kernel(
     bool any = false;
     for (int j0 = 0; j0 < topk; j0 += kWave) {       // wave-uniform
         const int j = j0 + lane;
-        const bool valid = j < topk && expanded_to_permuted[t * topk + j] >= 0;
+        const bool valid = j < topk &&
+                           MX_CAN_LOAD(expanded_to_permuted + t * topk + j, 4, kSiteZeroIndex) &&
+                           expanded_to_permuted[t * topk + j] >= 0;
         any = any || __ballot(valid) != 0ull;
     }
     if (!any) return;

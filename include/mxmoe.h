@@ -46,6 +46,9 @@ typedef enum mx_status {
     MX_ERR_WORKSPACE_TOO_SMALL = 4,
     MX_ERR_CAPACITY = 5,          /* input_permutation shorter than capacity    */
     MX_ERR_HIP = 6,               /* a HIP launch failed                        */
+    MX_ERR_OUT_OF_BOUNDS = 7,     /* bounds-checked library only: a kernel
+                                     access fell outside the call's arrays
+                                     (see mx_bounds_checked)                   */
     /* widens the enum's value range to every non-negative 32-bit code, so
      * mx_status_string is defined for any code a caller passes */
     MX_STATUS_FORCE_INT32 = 0x7fffffff
@@ -73,6 +76,45 @@ const char* mx_status_string(mx_status status);
 
 /* hipError_t of the last launch that returned MX_ERR_HIP on this thread. */
 int mx_last_hip_error(void);
+
+/*
+ * Bounds-checked build.  The same sources built with MXMOE_CHECKED defined
+ * give libmxmoe_checked.so, a debugging library with every entry point of
+ * this header.  Each call there describes its arrays to its kernels (the
+ * extents stated for each call below), and every global load and store of
+ * the kernels is checked against them before it is made: an access that does
+ * not lie wholly inside one array, or a store into an input, is counted and
+ * skipped (a load yields zeros), so the kernel still ends normally, and the
+ * call returns MX_ERR_OUT_OF_BOUNDS.  Indices into the kernels' on-chip
+ * arrays that come from data are checked the same way.  Every call of the
+ * checked library synchronises the device before and after its work and
+ * serialises with other calls; under stream capture it returns MX_ERR_HIP
+ * (hipErrorStreamCaptureUnsupported) and enqueues nothing.  libmxmoe.so
+ * checks nothing and never returns MX_ERR_OUT_OF_BOUNDS.
+ */
+
+/* 1 in the bounds-checked library, 0 in libmxmoe.so. */
+int32_t mx_bounds_checked(void);
+
+/*
+ * Out-of-bounds accesses counted since the last clear:
+ *   report[0] loads, report[1] stores (and data-dependent on-chip indices),
+ *   report[2] the byte address (or the index) of the first one counted,
+ *   report[3] a code naming the access that made it (0: none), one of the
+ *             CheckSite values of the library's sources.
+ * report: host array of 4 (else MX_ERR_INVALID_ARGUMENT); clear != 0 resets
+ * the counts after reading.  All zero in libmxmoe.so.
+ */
+mx_status mx_bounds_report(uint64_t* report, int32_t clear);
+
+/*
+ * Testing the checks themselves: from the next call on, every array a call
+ * writes is described to its kernels as `bytes` shorter at its end than it
+ * is (0 restores the true extents), so a kernel that writes the last bytes of
+ * an output is caught and skipped while no access leaves the real arrays.
+ * bytes >= 0 (else MX_ERR_INVALID_ARGUMENT).  libmxmoe.so accepts only 0.
+ */
+mx_status mx_bounds_shrink_outputs(int64_t bytes);
 
 /*
  * Rows a dispatched buffer (and input_permutation) needs for ANY routing of

@@ -1,7 +1,9 @@
 """The C ABI on the host (no GPU): the library loads, exports every entry
 point include/mxmoe.h declares, and rejects bad arguments with the
 documented status before making any HIP call (fake device addresses are
-never dereferenced on these paths)."""
+never dereferenced on these paths).  Every test runs against the loaded
+library and against the bounds-checked build, whose host checks are the
+same code."""
 
 import ctypes
 import os
@@ -14,15 +16,17 @@ import combine_topk_ids_expert_amd as mx
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mxmoe.h")
 
-OK, INVALID, DTYPE, MISALIGNED, WORKSPACE, CAPACITY, HIP = range(7)
+OK, INVALID, DTYPE, MISALIGNED, WORKSPACE, CAPACITY, HIP, OUT_OF_BOUNDS = range(8)
 F32, F16, BF16, FP8, I32, I64 = range(6)
 P = 0x10000          # a fake, 64 KiB-aligned "device" address, never dereferenced
 S = None             # stream (never reached)
 
 
-@pytest.fixture(scope="module")
-def lib():
-    return mx.load_library()
+@pytest.fixture(scope="module", params=["loaded", "checked"])
+def lib(request):
+    if request.param == "loaded":
+        return mx.load_library()
+    return mx.open_library(mx.CHECKED_LIBRARY)
 
 
 def test_exports_every_declared_symbol(lib):
@@ -31,15 +35,29 @@ def test_exports_every_declared_symbol(lib):
     assert declared == set(mx.EXPORTED_SYMBOLS)
     for name in declared:
         assert hasattr(lib, name), name
-    ext = ctypes.CDLL(mx.library_path())
-    for name in declared:
-        getattr(ext, name)
+    for path in (mx.library_path(), mx.CHECKED_LIBRARY):
+        ext = ctypes.CDLL(path)
+        for name in declared:
+            getattr(ext, name)
 
 
 def test_status_strings(lib):
-    for code in range(7):
-        assert lib.mx_status_string(code)
+    for code in range(8):
+        assert lib.mx_status_string(code) != b"unknown status"
     assert lib.mx_status_string(99) == b"unknown status"
+
+
+def test_bounds_check_calls(lib):
+    checked = lib.mx_bounds_checked()
+    assert checked == (1 if lib._name == mx.CHECKED_LIBRARY else 0)
+    report = (ctypes.c_uint64 * 4)(7, 7, 7, 7)
+    assert lib.mx_bounds_report(report, 1) == OK
+    assert list(report) == [0, 0, 0, 0]          # no kernel ran
+    assert lib.mx_bounds_report(None, 0) == INVALID
+    assert lib.mx_bounds_shrink_outputs(-1) == INVALID
+    assert lib.mx_bounds_shrink_outputs(0) == OK
+    assert lib.mx_bounds_shrink_outputs(16) == (OK if checked else INVALID)
+    assert lib.mx_bounds_shrink_outputs(0) == OK
 
 
 def test_capacity_and_workspace(lib):

@@ -497,6 +497,8 @@ def test_graph_capture_replays_match_eager(T, one_call):
     is replayed three times on new inputs copied into its static tensors,
     with eager work and synchronisations between replays; every replay must
     equal the eager calls on the same inputs, bit for bit."""
+    if mx.library_path() == mx.CHECKED_LIBRARY:
+        pytest.skip("the bounds-checked library refuses stream capture")
     _print_case("graph capture", T, one_call)
     dev = torch.device(DEV)
     E, k, H, A = 64, 8, 1024, 16
