@@ -879,8 +879,8 @@ def main(argv=None):
               f"(asked for --gpus {args.gpus}); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     if os.environ.get("MXMOE_LIBRARY", "") not in ("", "product"):
-        print("bench.py measures libmxmoe.so: unset MXMOE_LIBRARY (the bounds-checked "
-              "library synchronises around every call)", file=sys.stderr)
+        print("bench.py measures libmxmoe.so: unset MXMOE_LIBRARY (the test builds are "
+              "not the measured library)", file=sys.stderr)
         sys.exit(2)
     import torch
 

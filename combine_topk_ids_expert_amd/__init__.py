@@ -20,7 +20,9 @@ time.
 With ``MXMOE_LIBRARY=checked`` in the environment the binding loads
 ``libmxmoe_checked.so`` instead: the same kernels with every global access
 checked against the call's arrays (``bounds_checked``, ``bounds_report``), a
-debugging library that synchronises around every call.
+debugging library that synchronises around every call.  ``MXMOE_LIBRARY=
+altgrid`` loads ``libmxmoe_altgrid.so``, the same sources built with other
+tile sizes and workgroup widths, whose results must be the same bits.
 """
 
 from __future__ import annotations
@@ -39,12 +41,13 @@ __all__ = [
     "empty_routing", "MxError",
     "library_path", "load_library", "open_library", "EXPORTED_SYMBOLS", "bind", "BoundCall",
     "bounds_checked", "bounds_report", "bounds_shrink_outputs",
-    "PRODUCT_LIBRARY", "CHECKED_LIBRARY",
+    "PRODUCT_LIBRARY", "CHECKED_LIBRARY", "ALTGRID_LIBRARY",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 PRODUCT_LIBRARY = os.path.join(_PKG, "libmxmoe.so")
 CHECKED_LIBRARY = os.path.join(_PKG, "libmxmoe_checked.so")
+ALTGRID_LIBRARY = os.path.join(_PKG, "libmxmoe_altgrid.so")
 
 
 def _library_from_env() -> str:
@@ -53,7 +56,9 @@ def _library_from_env() -> str:
         return PRODUCT_LIBRARY
     if which == "checked":
         return CHECKED_LIBRARY
-    raise ImportError(f"MXMOE_LIBRARY={which!r}: expected 'checked' or 'product'")
+    if which == "altgrid":
+        return ALTGRID_LIBRARY
+    raise ImportError(f"MXMOE_LIBRARY={which!r}: expected 'product', 'checked' or 'altgrid'")
 
 
 _LIB_PATH = _library_from_env()

@@ -1,9 +1,14 @@
 """Build libmxmoe.so (the HIP kernels and the C ABI) for gfx950 with hipcc,
-and its bounds-checked twin libmxmoe_checked.so (the same sources with
-MXMOE_CHECKED defined: every kernel access is checked against the call's
-arrays; a debugging library, see mx_bounds_checked in include/mxmoe.h).
+and two test builds of the same sources:
 
-    python -m combine_topk_ids_expert_amd.build            # both
+  libmxmoe_checked.so  MXMOE_CHECKED defined: every kernel access is checked
+                       against the call's arrays (a debugging library, see
+                       mx_bounds_checked in include/mxmoe.h);
+  libmxmoe_altgrid.so  other tile sizes, path limits and workgroup widths, so
+                       every call runs on other grids; its results must be
+                       the same bits.
+
+    python -m combine_topk_ids_expert_amd.build            # all three
     python -m combine_topk_ids_expert_amd.build --product  # libmxmoe.so only
 
 The libraries are written next to this file, where the binding loads them.
@@ -22,7 +27,16 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmxmoe.so")
 LIB_CHECKED = os.path.join(PKG, "libmxmoe_checked.so")
+LIB_ALTGRID = os.path.join(PKG, "libmxmoe_altgrid.so")
 CHECKED_FLAGS = ["-DMXMOE_CHECKED=1"]
+# Routing: single-workgroup path up to 512 picks (1024 with little padding),
+# no medium path, at most 16 tiles and a quarter of the table budget; row
+# kernels: 256-thread copies, 128-thread combine chunks, 64-thread zeroing,
+# 256-thread FP8 chunks, 8 padding-fill slices.
+ALTGRID_FLAGS = ["-DMXMOE_FUSED_MAX=1024", "-DMXMOE_FUSED_ALWAYS=512", "-DMXMOE_SPREAD_MAX=0",
+                 "-DMXMOE_MAX_TILES=16", "-DMXMOE_TABLE_BUDGET=4096", "-DMXMOE_ZERO_SLICES=8",
+                 "-DMXMOE_ROW_THREADS=256", "-DMXMOE_COMBINE_THREADS=128",
+                 "-DMXMOE_ZERO_THREADS=64", "-DMXMOE_QUANT_THREADS=256"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -59,11 +73,17 @@ def build_checked(out_path: str = LIB_CHECKED, verbose: bool = False) -> str:
     return build(out_path, CHECKED_FLAGS, verbose)
 
 
+def build_altgrid(out_path: str = LIB_ALTGRID, verbose: bool = False) -> str:
+    return build(out_path, ALTGRID_FLAGS, verbose)
+
+
 def build_all(verbose: bool = False) -> list[str]:
-    """Both libraries, compiled side by side."""
+    """The three libraries, compiled side by side."""
     from concurrent.futures import ThreadPoolExecutor
-    with ThreadPoolExecutor(2) as pool:
-        jobs = [pool.submit(build, LIB, None, verbose), pool.submit(build_checked, LIB_CHECKED, verbose)]
+    with ThreadPoolExecutor(3) as pool:
+        jobs = [pool.submit(build, LIB, None, verbose),
+                pool.submit(build_checked, LIB_CHECKED, verbose),
+                pool.submit(build_altgrid, LIB_ALTGRID, verbose)]
         return [j.result() for j in jobs]
 
 

@@ -23,7 +23,11 @@ namespace {
 
 constexpr int kGroup = 8;      // columns per thread in the vector path
 constexpr int kPickBatch = 8;  // picks whose loads are issued together
-constexpr int kCombineThreads = 64;   // workgroup width; longer rows are cut into chunks
+#ifndef MXMOE_COMBINE_THREADS
+#define MXMOE_COMBINE_THREADS 64
+#endif
+constexpr int kCombineThreads = MXMOE_COMBINE_THREADS;   // workgroup width; longer rows are cut into chunks
+static_assert(kCombineThreads % kWave == 0 && kCombineThreads <= 1024, "whole waves, at most 1024");
 
 // LDS reserved per workgroup of the vector path, which caps the one-wave
 // workgroups per CU (32 without a cap): fewer gathers in flight per CU ran

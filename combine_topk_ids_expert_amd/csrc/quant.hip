@@ -35,7 +35,11 @@ constexpr int kGroupsPerWave = kWave / kThreadsPerGroup;          // 8
 // Workgroup width limit: a row of up to 16384 elements is one workgroup (448
 // threads at 7168).  Chunks of 64 to 256 threads, which suit the plain row
 // copies, made this kernel 1-10% slower on MI355X.
-constexpr int kQuantThreads = 1024;
+#ifndef MXMOE_QUANT_THREADS
+#define MXMOE_QUANT_THREADS 1024
+#endif
+constexpr int kQuantThreads = MXMOE_QUANT_THREADS;
+static_assert(kQuantThreads % kWave == 0 && kQuantThreads <= 1024, "whole waves, at most 1024");
 
 // LDS reserved per workgroup so that about 21 waves share a CU (3 workgroups
 // of the 7-wave rows of H = 7168, where the registers allow 4): 56.6 -> 55.6

@@ -24,7 +24,11 @@ namespace {
 // Workgroup width of the row copies: rows of more than 128 vectors are cut
 // into column chunks.  Two-wave workgroups copied 1-2% faster than one
 // workgroup per 14 KiB row (896 threads).
-constexpr int kRowThreads = 128;
+#ifndef MXMOE_ROW_THREADS
+#define MXMOE_ROW_THREADS 128
+#endif
+constexpr int kRowThreads = MXMOE_ROW_THREADS;
+static_assert(kRowThreads % kWave == 0 && kRowThreads <= 1024, "whole waves, at most 1024");
 
 // LDS reserved per workgroup of the row dispatch: at most 8 of its
 // workgroups per CU (16 waves) instead of 16.  Fewer scattered destination

@@ -14,7 +14,11 @@
 namespace mxmoe {
 namespace {
 
-constexpr int kZeroThreads = 128;       // workgroup width (longer rows are cut into column chunks)
+#ifndef MXMOE_ZERO_THREADS
+#define MXMOE_ZERO_THREADS 128
+#endif
+constexpr int kZeroThreads = MXMOE_ZERO_THREADS;   // workgroup width (longer rows are cut into column chunks)
+static_assert(kZeroThreads % kWave == 0 && kZeroThreads <= 1024, "whole waves, at most 1024");
 
 // LDS reserved per workgroup of the per-segment padding fill: at most 10 of
 // its two-wave workgroups per CU instead of 16.  At T = 4096 (event times on

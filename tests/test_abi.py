@@ -35,10 +35,11 @@ def test_exports_every_declared_symbol(lib):
     assert declared == set(mx.EXPORTED_SYMBOLS)
     for name in declared:
         assert hasattr(lib, name), name
-    for path in (mx.library_path(), mx.CHECKED_LIBRARY):
+    for path in (mx.library_path(), mx.CHECKED_LIBRARY, mx.ALTGRID_LIBRARY):
         ext = ctypes.CDLL(path)
         for name in declared:
             getattr(ext, name)
+    assert mx.open_library(mx.ALTGRID_LIBRARY).mx_bounds_checked() == 0
 
 
 def test_status_strings(lib):

@@ -1,17 +1,21 @@
-"""The bounds-checked library (libmxmoe_checked.so) on the GPU.
+"""The two test builds of the library on the GPU, against libmxmoe.so.
 
-In the checked build every global load and store of the kernels is checked
-against the arrays of the call that launched them (include/mxmoe.h,
-mx_bounds_checked).  A call whose kernels stayed inside them returns MX_OK;
-one whose kernels did not returns MX_ERR_OUT_OF_BOUNDS after skipping the
-accesses outside.  These tests run every entry point through the checked
-library on inputs that reach each kernel path (each routing path, the tile
-sort, the no-allocation routing, routing and dispatch in one launch, each
-vector width of the row copies, side rows, both combine paths, both zeroing
-kernels, the FP8 dispatch), with ragged tails and invalid ids, and require
-MX_OK and outputs byte-identical to the normal library's.  Then they describe
-the outputs as shorter than they are, to show that the checks catch a write
-past an end, skip it and report where it was.
+libmxmoe_checked.so checks every global load and store of the kernels against
+the arrays of the call that launched them (include/mxmoe.h,
+mx_bounds_checked): a call whose kernels stayed inside them returns MX_OK, one
+whose kernels did not returns MX_ERR_OUT_OF_BOUNDS after skipping the
+accesses outside.  libmxmoe_altgrid.so is built with other tile sizes, path
+limits and workgroup widths (build.py), so the same calls run on other grids
+and, for routing, other paths; deterministic kernels give the same bits.
+
+Every entry point runs through both builds on inputs that reach each kernel
+path (each routing path, the tile sort, the no-allocation routing, routing
+and dispatch in one launch, each vector width of the row copies, side rows,
+both combine paths, both zeroing kernels, the FP8 dispatch), with ragged
+tails and invalid ids, and must return MX_OK with outputs byte-identical to
+libmxmoe.so's.  Last, the checked build is shown outputs described as shorter
+than they are: it catches a write past an end, skips it and reports where it
+was.
 """
 
 import contextlib
@@ -33,7 +37,13 @@ SITE_COMBINE_OUT = 15
 
 @pytest.fixture(scope="module")
 def libs():
-    return {"product": mx.load_library(), "checked": mx.open_library(mx.CHECKED_LIBRARY)}
+    return {"product": mx.load_library(), "checked": mx.open_library(mx.CHECKED_LIBRARY),
+            "altgrid": mx.open_library(mx.ALTGRID_LIBRARY)}
+
+
+@pytest.fixture(params=["checked", "altgrid"])
+def variant(request):
+    return request.param
 
 
 @contextlib.contextmanager
@@ -46,16 +56,16 @@ def _using(lib):
         mx._lib = saved
 
 
-def _both(libs, make, run):
+def _both(libs, variant, make, run):
     """make() returns a dict of fresh tensors (seeded inputs, sentinel-filled
-    outputs); run(bufs) calls the binding.  Runs both libraries on their own
-    copies, checks that the checked one counted nothing, and returns the two
-    dicts."""
+    outputs); run(bufs) calls the binding.  Runs libmxmoe.so and the variant
+    build on their own copies (the checked build must count nothing) and
+    returns the two dicts."""
     results = []
-    for name in ("product", "checked"):
-        bufs = make()
-        torch.cuda.synchronize()
-        with _using(libs[name]):
+    for name in ("product", variant):
+        with _using(libs[name]):       # workspace sizes come from the library that runs
+            bufs = make()
+            torch.cuda.synchronize()
             if name == "checked":
                 assert mx.bounds_checked()
                 mx.bounds_report(clear=True)
@@ -75,6 +85,8 @@ def _both(libs, make, run):
 
 def _same(a: dict, b: dict):
     for key in a:
+        if key == "workspace":          # scratch: its size and use depend on the build
+            continue
         if isinstance(a[key], torch.Tensor):
             ua = a[key].contiguous().view(torch.uint8)
             ub = b[key].contiguous().view(torch.uint8)
@@ -121,17 +133,17 @@ def _prepare(r, E, A, noalloc=False):
     (100, 1000, 8, 16, "uniform", 0.1, torch.int64),   # 1000 experts
     (20, 33, 70, 3, "dups", 0.1, torch.int64),         # topk 70
 ])
-def test_checked_prepare_moe_input(libs, T, E, k, A, mode, bad, ids_dtype):
-    print("case: checked prepare_moe_input", T, E, k, A, mode, flush=True)
-    a, b = _both(libs, lambda: _routing(T, k, E, A, _ids(T, E, k, mode, bad, T, ids_dtype)),
+def test_variant_prepare_moe_input(libs, variant, T, E, k, A, mode, bad, ids_dtype):
+    print(f"case: {variant} prepare_moe_input", T, E, k, A, mode, flush=True)
+    a, b = _both(libs, variant, lambda: _routing(T, k, E, A, _ids(T, E, k, mode, bad, T, ids_dtype)),
                  lambda r: _prepare(r, E, A))
     _same(a, b)
 
 
-def test_checked_prepare_noalloc(libs):
+def test_variant_prepare_noalloc(libs, variant):
     T, E, k = 8192, 128, 8
-    print("case: checked prepare_moe_input_noalloc", T, E, k, flush=True)
-    a, b = _both(libs, lambda: _routing(T, k, E, 1, _ids(T, E, k, "uniform", 0.0, 3)),
+    print(f"case: {variant} prepare_moe_input_noalloc", T, E, k, flush=True)
+    a, b = _both(libs, variant, lambda: _routing(T, k, E, 1, _ids(T, E, k, "uniform", 0.0, 3)),
                  lambda r: _prepare(r, E, 1, noalloc=True))
     _same(a, b)
 
@@ -140,8 +152,8 @@ def test_checked_prepare_noalloc(libs):
     (64, 8, 4, 2, 4, 16),        # one workgroup, ids outside the window
     (4096, 288, 8, 36, 36, 128),  # two launches
 ])
-def test_checked_moe_sort(libs, T, E, k, off, n_local, tile):
-    print("case: checked moe_sort", T, E, k, off, n_local, tile, flush=True)
+def test_variant_moe_sort(libs, variant, T, E, k, off, n_local, tile):
+    print(f"case: {variant} moe_sort", T, E, k, off, n_local, tile, flush=True)
 
     def make():
         cap = mx.dispatch_capacity(T, k, n_local, tile)
@@ -155,14 +167,14 @@ def test_checked_moe_sort(libs, T, E, k, off, n_local, tile):
             out[name] = torch.full((numel,), -7, dtype=torch.int32, device=DEV)
         return out
 
-    a, b = _both(libs, make, lambda r: mx.moe_sort(
+    a, b = _both(libs, variant, make, lambda r: mx.moe_sort(
         r["ids"], E, off, n_local, tile, out={k_: v for k_, v in r.items() if k_ != "ids"}))
     _same(a, b)
 
 
 @pytest.mark.parametrize("T,E,k,H", [(32, 256, 8, 4096), (257, 256, 8, 4096)])
-def test_checked_prepare_dispatch(libs, T, E, k, H):
-    print("case: checked prepare_dispatch", T, E, k, H, flush=True)
+def test_variant_prepare_dispatch(libs, variant, T, E, k, H):
+    print(f"case: {variant} prepare_dispatch", T, E, k, H, flush=True)
     cap = mx.dispatch_capacity(T, k, E, 1)
 
     def make():
@@ -174,7 +186,7 @@ def test_checked_prepare_dispatch(libs, T, E, k, H):
         r["xd"].view(torch.uint8).fill_(gu.SENTINEL)
         return r
 
-    a, b = _both(libs, make, lambda r: mx.prepare_dispatch(
+    a, b = _both(libs, variant, make, lambda r: mx.prepare_dispatch(
         r["ids"], r["expert_offsets"], r["problem_sizes1"], r["problem_sizes2"],
         r["input_permutation"], r["output_permutation"], E, 64, 32, r["x"], r["xd"],
         r["blockscale_offsets"], workspace=r["workspace"]))
@@ -190,10 +202,10 @@ def _routed(T, E, k, A, seed):
 
 
 @pytest.mark.parametrize("row_bytes", [14336, 200, 100, 50, 25])
-def test_checked_row_copies(libs, row_bytes):
+def test_variant_row_copies(libs, variant, row_bytes):
     # 16-, 8-, 4-, 2- and 1-byte vectors; a ragged token count
     T, E, k, A = 77, 16, 4, 8
-    print("case: checked dispatch_rows / shuffle_rows, row bytes", row_bytes, flush=True)
+    print(f"case: {variant} dispatch_rows / shuffle_rows, row bytes", row_bytes, flush=True)
     r = _routed(T, E, k, A, 21)
     cap = r["input_permutation"].numel()
 
@@ -209,13 +221,13 @@ def test_checked_row_copies(libs, row_bytes):
         mx.dispatch_rows(b["x"], r["output_permutation"], k, b["xd"])
         mx.shuffle_rows(b["x"], r["input_permutation"], b["xs"])
 
-    a, b = _both(libs, make, run)
+    a, b = _both(libs, variant, make, run)
     _same(a, b)
 
 
-def test_checked_dispatch_with_side_rows_and_fp8(libs):
+def test_variant_dispatch_with_side_rows_and_fp8(libs, variant):
     T, E, k, H = 48, 64, 8, 1024
-    print("case: checked dispatch with scale rows, fp8 dispatch", flush=True)
+    print(f"case: {variant} dispatch with scale rows, fp8 dispatch", flush=True)
     r = _routed(T, E, k, 1, 31)
     cap = r["input_permutation"].numel()
 
@@ -235,7 +247,7 @@ def test_checked_dispatch_with_side_rows_and_fp8(libs):
                          side_output=b["sd"])
         mx.dispatch_rows_fp8(b["xb"], r["output_permutation"], k, b["q"], b["qs"])
 
-    a, b = _both(libs, make, run)
+    a, b = _both(libs, variant, make, run)
     _same(a, b)
 
 
@@ -245,9 +257,9 @@ def test_checked_dispatch_with_side_rows_and_fp8(libs):
     (torch.bfloat16, torch.float32, None, 2048),             # unit weights
     (torch.float16, torch.float16, torch.float16, 1000),     # scalar path
 ])
-def test_checked_combine(libs, ydt, odt, fdt, H):
+def test_variant_combine(libs, variant, ydt, odt, fdt, H):
     T, E, k = 61, 32, 8
-    print("case: checked combine", ydt, odt, fdt, H, flush=True)
+    print(f"case: {variant} combine", ydt, odt, fdt, H, flush=True)
     r = _routed(T, E, k, 4, 41)
     cap = r["input_permutation"].numel()
 
@@ -259,14 +271,14 @@ def test_checked_combine(libs, ydt, odt, fdt, H):
         out = torch.full((T, H), float("nan"), device=DEV).to(odt)
         return {"y": y, "w": w, "out": out}
 
-    a, b = _both(libs, make, lambda b: mx.apply_shuffle_mul_sum(
+    a, b = _both(libs, variant, make, lambda b: mx.apply_shuffle_mul_sum(
         b["y"], b["out"], r["output_permutation"], b["w"]))
     _same(a, b)
 
 
-def test_checked_zeroing(libs):
+def test_variant_zeroing(libs, variant):
     T, E, k, A, H = 90, 16, 4, 32, 1024
-    print("case: checked zero_padding_rows, moe_output_memset", flush=True)
+    print(f"case: {variant} zero_padding_rows, moe_output_memset", flush=True)
     r = _routed(T, E, k, A, 51)
     cap = r["input_permutation"].numel()
     outp = r["output_permutation"].clone()
@@ -282,7 +294,7 @@ def test_checked_zeroing(libs):
         mx.zero_padding_rows(b["rows2"], r["input_permutation"])
         mx.moe_output_memset(b["out"], outp, k)
 
-    a, b = _both(libs, make, run)
+    a, b = _both(libs, variant, make, run)
     _same(a, b)
 
 
