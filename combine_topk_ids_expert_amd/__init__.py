@@ -391,7 +391,7 @@ def _prepare_args(topk_ids, expert_offsets, problem_sizes1, problem_sizes2, inpu
             _ptr(expert_offsets), _ptr(problem_sizes1), _ptr(problem_sizes2),
             _ptr(input_permutation), input_permutation.numel(), _ptr(output_permutation),
             _ptr(blockscale_offsets), blockscale_align,
-            _ptr(workspace), workspace.numel())
+            _ptr(workspace), workspace.numel() * workspace.element_size())
     keep = (topk_ids, expert_offsets, problem_sizes1, problem_sizes2, input_permutation,
             output_permutation, blockscale_offsets, workspace)
     return dev, args, keep
@@ -679,7 +679,7 @@ def moe_sort(topk_ids: torch.Tensor, num_experts: int, local_expert_offset: int,
         res["permuted_idx_to_expanded_idx"].numel(), _ptr(res["tile_idx_to_group_idx"]),
         _ptr(res["tile_idx_to_mn_limit"]), nt, _ptr(res["total_num_padded_tokens"]),
         _ptr(res["num_non_exiting_tiles"]), _ptr(res["expert_offsets"]),
-        _ptr(workspace), workspace.numel()), "moe_sort")
+        _ptr(workspace), workspace.numel() * workspace.element_size()), "moe_sort")
     return res
 
 

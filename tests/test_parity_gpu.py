@@ -98,6 +98,33 @@ def test_prepare_deterministic_across_calls():
         np.testing.assert_array_equal(a[key], b[key])
 
 
+def test_prepare_workspace_of_another_dtype():
+    """A workspace tensor is sized in bytes whatever its dtype: an int32
+    tensor of exactly the bytes mx_prepare_workspace_size asks for is enough,
+    and one byte fewer is refused."""
+    _print_case("prepare with an int32 workspace")
+    T, E, k = 4096, 256, 8
+    need = mx.prepare_workspace_size(T, k, E)
+    assert need > 0 and need % 4 == 0
+    rng = np.random.default_rng(12)
+    ids = routing.uniform_topk(rng, T, E, k).astype(np.int64)
+    t_ids = torch.from_numpy(ids).to(DEV)
+    r = mx.empty_routing(T, k, E, DEV)
+    ws = torch.empty(need // 4, dtype=torch.int32, device=DEV)
+    mx.prepare_moe_input(t_ids, r["expert_offsets"], r["problem_sizes1"], r["problem_sizes2"],
+                         r["input_permutation"], r["output_permutation"], E, 64, 32,
+                         workspace=ws)
+    torch.cuda.synchronize()
+    o = oracle.prepare_moe_input(ids, E)
+    np.testing.assert_array_equal(r["output_permutation"].cpu().numpy(), o["output_permutation"])
+    np.testing.assert_array_equal(r["input_permutation"].cpu().numpy(), o["input_permutation"])
+    short = torch.empty(need - 1, dtype=torch.uint8, device=DEV)
+    with pytest.raises(mx.MxError) as err:
+        mx.prepare_moe_input(t_ids, r["expert_offsets"], None, None, r["input_permutation"],
+                             r["output_permutation"], E, 64, 32, workspace=short)
+    assert err.value.status == 4
+
+
 # --------------------------------------------------------------------------
 # dispatch rows (scatter and gather)
 # --------------------------------------------------------------------------
