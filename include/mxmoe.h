@@ -91,6 +91,12 @@ int mx_last_hip_error(void);
  * serialises with other calls; under stream capture it returns MX_ERR_HIP
  * (hipErrorStreamCaptureUnsupported) and enqueues nothing.  libmxmoe.so
  * checks nothing and never returns MX_ERR_OUT_OF_BOUNDS.
+ *
+ * A second test build, libmxmoe_altgrid.so, has other tile sizes, path
+ * limits and workgroup widths: the one-launch thresholds and workspace sizes
+ * stated below are those of libmxmoe.so and differ there (ask
+ * mx_prepare_workspace_size of the library in use), while every result is
+ * the same bits.
  */
 
 /* 1 in the bounds-checked library, 0 in libmxmoe.so. */
