@@ -123,6 +123,8 @@ def parse_args(argv=None):
                    help="time routing + dispatch as prepare_dispatch (one call) against "
                         "prepare_moe_input + dispatch_rows (two calls) at decode-sized batches, "
                         "eager and as HIP-graph replays, and print one JSON line per size")
+    p.add_argument("--kernel-sweep", action="store_true",
+                   help="each call alone at T = 32 to 65536 (H = 7168): us, GB/s, fraction of peak")
     p.add_argument("--routing-sweep", action="store_true",
                    help="time prepare_moe_input alone at T = 128 to 4096 under several routings "
                         "and print one JSON line per case")
@@ -779,6 +781,94 @@ def one_call_sweep(sizes=(1, 8, 32, 64, 128, 192, 256), hiddens=(4096, 7168), E=
                 "graph_two_calls_us": per_call(graphs[1].replay, 10, 20)}}), flush=True)
 
 
+KERNEL_SWEEP = (32, 128, 512, 2048, 8192, 32768, 65536)
+
+
+def kernel_sweep(sizes=KERNEL_SWEEP, H=7168, E=256, k=8, reps=5) -> None:
+    """Each call of the path alone, from decode-sized batches to the largest
+    workload: uniform routing over E experts, bf16 rows of H, fp32 weights,
+    bf16 combine output.  Per call: microseconds back to back (bound calls on
+    one stream, the minimum over ``reps`` means; data left in the caches by
+    the previous call of the same kind stays there where it fits), and the
+    kernels' own time from the timed entry points (median of single calls)
+    where the call has one.  GB/s and the fraction of 8 TB/s use the
+    algorithmic bytes of the call (shuffle_rows: those of the dispatch it
+    equals)."""
+    import types
+    import numpy as np
+    import torch
+    import combine_topk_ids_expert_amd as mx
+    from workloads import routing
+    dev = torch.device("cuda:0")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    kev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for e in kev:
+        e.record()
+    torch.cuda.synchronize()
+
+    def back_to_back(fn, n):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        best = float("inf")
+        for _ in range(reps):
+            ev[0].record()
+            for _ in range(n):
+                fn()
+            ev[1].record()
+            torch.cuda.synchronize()
+            best = min(best, ev[0].elapsed_time(ev[1]) * 1e3 / n)
+        return best
+
+    def kernel_time(fn):
+        us = []
+        for _ in range(4 * reps):
+            fn(kernel_events=kev)
+            torch.cuda.synchronize()
+            us.append(kev[0].elapsed_time(kev[1]) * 1e3)
+        return float(np.median(us))
+
+    for T in sizes:
+        rng = np.random.default_rng(T)
+        ids = torch.from_numpy(routing.uniform_topk(rng, T, E, k)).to(dev)
+        wts = torch.from_numpy(routing.softmax_weights(rng, T, k)).to(dev)
+        x = routing.normal_rows(T, H, "bf16", seed=T, device=dev)
+        r = mx.empty_routing(T, k, E, dev)
+        cap = r["input_permutation"].numel()
+        xd = torch.empty((cap, H), dtype=x.dtype, device=dev)
+        y = routing.normal_rows(cap, H, "bf16", seed=T + 1, device=dev)
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        calls = {
+            "prepare_moe_input": mx.bind(mx.prepare_moe_input, ids, r["expert_offsets"],
+                                         r["problem_sizes1"], r["problem_sizes2"],
+                                         r["input_permutation"], r["output_permutation"], E,
+                                         2048, H, workspace=r["workspace"]),
+            "dispatch_rows": mx.bind(mx.dispatch_rows, x, r["output_permutation"], k, xd),
+            "shuffle_rows": mx.bind(mx.shuffle_rows, x, r["input_permutation"], xd),
+            "apply_shuffle_mul_sum": mx.bind(mx.apply_shuffle_mul_sum, y, out,
+                                             r["output_permutation"], wts),
+        }
+        calls["prepare_moe_input"]()
+        torch.cuda.synchronize()
+        w = types.SimpleNamespace(T=T, k=k, E=E, H=H, x_elem_bytes=2, scale_width=0,
+                                  y_dtype="bf16", out_dtype="bf16")
+        ab = algorithmic_bytes(w, T * k, cap, 8)
+        nbytes = {"prepare_moe_input": ab["prepare"], "dispatch_rows": ab["dispatch"],
+                  "shuffle_rows": ab["dispatch"], "apply_shuffle_mul_sum": ab["combine"]}
+        n = max(10, min(200, 20000 // T))
+        for name, fn in calls.items():
+            us = back_to_back(fn, n)
+            kus = kernel_time(fn) if name != "shuffle_rows" else None
+            t = kus if kus is not None else us
+            print(json.dumps({"kernel_sweep": {
+                "call": name, "T": T, "H": H, "E": E, "topk": k, "bytes": nbytes[name],
+                "us_back_to_back": us, "kernel_us": kus,
+                "gbps": nbytes[name] / t / 1e3, "frac": nbytes[name] / t / 1e3 / HBM_PEAK_GBPS}}),
+                flush=True)
+        del calls, x, xd, y, out, r
+        torch.cuda.empty_cache()
+
+
 ROUTING_SWEEP = [  # (T, E, k, row_align, routing)
     (128, 256, 8, 1, "uniform"), (300, 256, 8, 1, "uniform"), (512, 256, 8, 1, "uniform"),
     (1024, 256, 8, 1, "uniform"), (1024, 256, 8, 128, "uniform"), (1024, 256, 8, 1, "k_hot"),
@@ -895,6 +985,9 @@ def main(argv=None):
         return
     if args.routing_sweep:
         routing_sweep()
+        return
+    if args.kernel_sweep:
+        kernel_sweep()
         return
 
     from workloads import get_workload

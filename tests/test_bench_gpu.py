@@ -56,3 +56,25 @@ def test_bench_json_line_small_workload():
     oc = d["workloads"]["uniform_T32_H4096_E256_k8"]
     assert oc["step_ms_cold_one_call_dispatch"] > 0 and oc["step_ms_warm_one_call_dispatch"] > 0
     assert oc["step_ms_warm_graph"] > 0 and oc["step_ms_warm_graph_one_call_dispatch"] > 0
+
+
+def test_kernel_sweep_lines():
+    if os.environ.get("MXMOE_LIBRARY", "") not in ("", "product"):
+        pytest.skip("bench.py measures the normal library only")
+    print("case: bench.py kernel sweep at T = 32 and 2048", flush=True)
+    code = ("import bench; bench.kernel_sweep(sizes=(32, 2048), reps=2)")
+    proc = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
+                          timeout=300)
+    assert proc.returncode == 0, proc.stderr[-3000:]
+    rows = [json.loads(ln)["kernel_sweep"] for ln in proc.stdout.splitlines()
+            if ln.startswith('{"kernel_sweep"')]
+    calls = ("prepare_moe_input", "dispatch_rows", "shuffle_rows", "apply_shuffle_mul_sum")
+    assert [(r["T"], r["call"]) for r in rows] == [(T, c) for T in (32, 2048) for c in calls]
+    for r in rows:
+        assert r["us_back_to_back"] > 0 and r["bytes"] > 0
+        t = r["kernel_us"] if r["kernel_us"] is not None else r["us_back_to_back"]
+        assert abs(r["gbps"] - r["bytes"] / t / 1e3) < 1e-6 * r["gbps"]
+        assert (r["kernel_us"] is None) == (r["call"] == "shuffle_rows")
+    # T = 2048, H = 7168, k = 8: combine reads 8 bf16 rows and writes one per token
+    comb = [r for r in rows if r["T"] == 2048 and r["call"] == "apply_shuffle_mul_sum"][0]
+    assert comb["bytes"] == 2048 * 8 * 7168 * 2 + 2048 * 7168 * 2 + 2048 * 8 * 8
