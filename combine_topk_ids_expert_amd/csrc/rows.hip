@@ -37,6 +37,14 @@ static_assert(kRowThreads % kWave == 0 && kRowThreads <= 1024, "whole waves, at 
 // 167 us at K-hot T = 8192 and 94 -> 92.7 us at T = 4096.  18-20 KiB
 // measured alike; from 16 KiB down, or 21 KiB up, some workload lost.
 constexpr size_t kDispatchLds = 19 * 1024;
+// While the source rows fit the Infinity Cache (streaming stores), rows of
+// 8 KiB and more wrote faster at 6 workgroups per CU: T = 4096, H = 7168 cold
+// 202.1 -> 199.3-199.9 us per step and warm 188.0-188.7 -> 187.6, K-hot T =
+// 8192 warm 334.5-335.4 -> 331.5 (cold level).  The FP8 rows of the Zipf
+// workload (4 KiB) lost 3-18 us at 6 per CU, and the 288-slot rows, whose
+// source exceeds the cache, 80 us; 5 or 4 per CU lost up to 50 us cold.
+constexpr size_t kDispatchLdsWide = 26 * 1024;
+constexpr int64_t kWideRowBytes = 8192;
 
 
 template <int V> struct Vec;
@@ -134,15 +142,16 @@ int vec_width(int64_t row_bytes, const void* a, const void* b) {
 }
 
 template <int V, int P>
-void launch_dispatch_v(dim3 grid, dim3 block, int32_t chunks, int side_vec, const uint8_t* s,
-                       int64_t row_bytes, int32_t topk, const int32_t* output_perm, uint8_t* d,
-                       int64_t num_dst_rows, const uint8_t* ss, int64_t side_row_bytes,
-                       uint8_t* sd, hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
+void launch_dispatch_v(dim3 grid, dim3 block, size_t lds, int32_t chunks, int side_vec,
+                       const uint8_t* s, int64_t row_bytes, int32_t topk,
+                       const int32_t* output_perm, uint8_t* d, int64_t num_dst_rows,
+                       const uint8_t* ss, int64_t side_row_bytes, uint8_t* sd,
+                       hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
     switch (side_vec) {
-    case 0: launch_kernel(dispatch_rows_kernel<V, 0, P>, grid, block, kDispatchLds, stream, e0, e1, s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd, chunks); break;
-    case 16: launch_kernel(dispatch_rows_kernel<V, 16, P>, grid, block, kDispatchLds, stream, e0, e1, s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd, chunks); break;
-    case 4: launch_kernel(dispatch_rows_kernel<V, 4, P>, grid, block, kDispatchLds, stream, e0, e1, s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd, chunks); break;
-    default: launch_kernel(dispatch_rows_kernel<V, 1, P>, grid, block, kDispatchLds, stream, e0, e1, s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd, chunks); break;
+    case 0: launch_kernel(dispatch_rows_kernel<V, 0, P>, grid, block, lds, stream, e0, e1, s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd, chunks); break;
+    case 16: launch_kernel(dispatch_rows_kernel<V, 16, P>, grid, block, lds, stream, e0, e1, s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd, chunks); break;
+    case 4: launch_kernel(dispatch_rows_kernel<V, 4, P>, grid, block, lds, stream, e0, e1, s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd, chunks); break;
+    default: launch_kernel(dispatch_rows_kernel<V, 1, P>, grid, block, lds, stream, e0, e1, s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd, chunks); break;
     }
 }
 
@@ -184,6 +193,7 @@ hipError_t launch_dispatch_rows(const void* src, int64_t num_tokens, int32_t top
     }
     const RowShape sh = row_shape(row_bytes / v, kRowThreads);
     const bool keep = dispatch_store_policy(num_tokens * (row_bytes + side_row_bytes)) == kKeep;
+    const size_t lds = !keep && row_bytes >= kWideRowBytes ? kDispatchLdsWide : kDispatchLds;
     const uint8_t* s = static_cast<const uint8_t*>(src);
     uint8_t* d = static_cast<uint8_t*>(dst);
     const uint8_t* ss = static_cast<const uint8_t*>(side_src);
@@ -195,13 +205,13 @@ hipError_t launch_dispatch_rows(const void* src, int64_t num_tokens, int32_t top
         const uint8_t* sst = ss ? ss + t0 * side_row_bytes : nullptr;
         switch (v) {
         case 16:
-            if (keep) launch_dispatch_v<16, kKeep>(grid, block, sh.chunks, side_vec, st, row_bytes, topk, pt, d, num_dst_rows, sst, side_row_bytes, sd, stream, e0, e1);
-            else launch_dispatch_v<16, kStream>(grid, block, sh.chunks, side_vec, st, row_bytes, topk, pt, d, num_dst_rows, sst, side_row_bytes, sd, stream, e0, e1);
+            if (keep) launch_dispatch_v<16, kKeep>(grid, block, lds, sh.chunks, side_vec, st, row_bytes, topk, pt, d, num_dst_rows, sst, side_row_bytes, sd, stream, e0, e1);
+            else launch_dispatch_v<16, kStream>(grid, block, lds, sh.chunks, side_vec, st, row_bytes, topk, pt, d, num_dst_rows, sst, side_row_bytes, sd, stream, e0, e1);
             break;
-        case 8: launch_dispatch_v<8, kStream>(grid, block, sh.chunks, side_vec, st, row_bytes, topk, pt, d, num_dst_rows, sst, side_row_bytes, sd, stream, e0, e1); break;
-        case 4: launch_dispatch_v<4, kStream>(grid, block, sh.chunks, side_vec, st, row_bytes, topk, pt, d, num_dst_rows, sst, side_row_bytes, sd, stream, e0, e1); break;
-        case 2: launch_dispatch_v<2, kStream>(grid, block, sh.chunks, side_vec, st, row_bytes, topk, pt, d, num_dst_rows, sst, side_row_bytes, sd, stream, e0, e1); break;
-        default: launch_dispatch_v<1, kStream>(grid, block, sh.chunks, side_vec, st, row_bytes, topk, pt, d, num_dst_rows, sst, side_row_bytes, sd, stream, e0, e1); break;
+        case 8: launch_dispatch_v<8, kStream>(grid, block, lds, sh.chunks, side_vec, st, row_bytes, topk, pt, d, num_dst_rows, sst, side_row_bytes, sd, stream, e0, e1); break;
+        case 4: launch_dispatch_v<4, kStream>(grid, block, lds, sh.chunks, side_vec, st, row_bytes, topk, pt, d, num_dst_rows, sst, side_row_bytes, sd, stream, e0, e1); break;
+        case 2: launch_dispatch_v<2, kStream>(grid, block, lds, sh.chunks, side_vec, st, row_bytes, topk, pt, d, num_dst_rows, sst, side_row_bytes, sd, stream, e0, e1); break;
+        default: launch_dispatch_v<1, kStream>(grid, block, lds, sh.chunks, side_vec, st, row_bytes, topk, pt, d, num_dst_rows, sst, side_row_bytes, sd, stream, e0, e1); break;
         }
     }, start_event, stop_event);
 }
