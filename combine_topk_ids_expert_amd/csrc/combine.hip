@@ -39,10 +39,16 @@ static_assert(kCombineThreads % kWave == 0 && kCombineThreads <= 1024, "whole wa
 //     (Uncapped, one-wave chunks had been slower than two-wave ones.)
 //   Allocating stores: 13 per CU.  Against 12: 85.4 -> 84.1 us at T = 4096,
 //     159.9 -> 157.3 us at K-hot T = 8192, 185.3 -> 184.3 us on the Zipf
-//     workload; 14 per CU was faster at T = 4096 only, 11 and fewer slower
-//     everywhere.
+//     workload; 11 and fewer slower everywhere.
+//   Allocating stores, at most 4096 tokens: 16 per CU.  Combine alone was
+//     1-7% faster than at 13 per CU from 1024 to 4096 tokens under uniform,
+//     K-hot and Zipf routing, and the T = 4096, H = 7168 step 186.7-187.0 ->
+//     184.4-185.2 us warm; at K-hot T = 8192 and the Zipf workload (16384
+//     tokens) 16 per CU lost 3-5 us within the step.
 constexpr size_t kCombineLdsStream = 13 * 1024;  // 12 per CU
 constexpr size_t kCombineLdsKeep = 12 * 1024;    // 13 per CU
+constexpr size_t kCombineLdsKeepSmall = 10 * 1024;  // 16 per CU
+constexpr int64_t kSmallCombineTokens = 4096;
 
 
 // N consecutive elements of a row, moved with one 8- or 16-byte access.
@@ -285,6 +291,7 @@ hipError_t launch_typed(const void* y, int64_t num_y_rows, int64_t hidden, const
     const RowShape sh = row_shape(vec ? hidden / kGroup : hidden, kCombineThreads);
     const int64_t factor_bytes = FDT == 0 ? 4 : 2;
     const bool keep = combine_store_policy(T * hidden * (int64_t)sizeof(SO)) == kKeep;
+    const size_t keep_lds = T <= kSmallCombineTokens ? kCombineLdsKeepSmall : kCombineLdsKeep;
     return for_row_batches(T, sh, [&](int64_t t0, int64_t, dim3 grid, dim3 block,
                                       hipEvent_t e0, hipEvent_t e1) {
         const int32_t* p = perm + t0 * topk;
@@ -292,7 +299,7 @@ hipError_t launch_typed(const void* y, int64_t num_y_rows, int64_t hidden, const
                                 : nullptr;
         SO* o = static_cast<SO*>(out) + t0 * hidden;
         if (vec && keep)
-            launch_kernel(combine_vec_kernel<TY, TO, FDT, kKeep>, grid, block, kCombineLdsKeep, stream,
+            launch_kernel(combine_vec_kernel<TY, TO, FDT, kKeep>, grid, block, keep_lds, stream,
                           e0, e1, static_cast<const SY*>(y), num_y_rows, hidden, p, f, topk, o,
                           sh.chunks);
         else if (vec)
