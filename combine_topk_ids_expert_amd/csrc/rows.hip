@@ -7,9 +7,10 @@
 // Both are HBM-bound byte copies.  A workgroup owns a column chunk of at most
 // 128 vectors of one row (the chunks of a row are neighbours in the grid) and
 // each thread moves exactly one 16-byte vector: one load, then one store per
-// destination; the scatter form runs at most 8 workgroups per CU.  Short-lived workgroups with one access per thread sustained
-// the highest write rate on MI355X (several accesses per thread, or looping
-// workgroups, wrote slower).  The write-once destination rows are stored
+// destination; the scatter form runs at most 6 or 8 workgroups per CU.
+// Short-lived workgroups with one access per thread sustained the highest
+// write rate on MI355X (several accesses per thread, or looping workgroups,
+// wrote slower).  The write-once destination rows are stored
 // system-coherent: non-temporal while the source rows fit in the Infinity
 // Cache, allocating beyond that (store16, dispatch_store_policy).  The source
 // rows are loaded with the default policy.  Each measured fastest of the
