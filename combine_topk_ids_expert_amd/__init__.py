@@ -462,9 +462,11 @@ def prepare_moe_input_noalloc(topk_ids: torch.Tensor, expert_offsets: torch.Tens
 
 
 def shuffle_rows(input: torch.Tensor, dst2src_map: torch.Tensor,
-                 output: torch.Tensor | None = None, _bind: bool = False) -> torch.Tensor:
+                 output: torch.Tensor | tuple | None = None, _bind: bool = False) -> torch.Tensor:
     """output[r] = input[dst2src_map[r]] byte for byte (rows with an index out
-    of range keep their contents).  Any dtype; row = everything past dim 0."""
+    of range keep their contents).  Any dtype; row = everything past dim 0.
+    ``output`` is the tensor to write, or its shape (as sglang's shuffle_rows
+    takes it), or None; either of the latter two allocates it."""
     lib = load_library()
     _check_dev("input", input)
     dev = input.device
@@ -473,6 +475,8 @@ def shuffle_rows(input: torch.Tensor, dst2src_map: torch.Tensor,
     n_dst = dst2src_map.numel()
     if output is None:
         output = torch.empty((n_dst,) + tuple(input.shape[1:]), dtype=input.dtype, device=dev)
+    elif not isinstance(output, torch.Tensor):
+        output = torch.empty(tuple(output), dtype=input.dtype, device=dev)
     _check_dev("output", output, dev)
     if output.dtype != input.dtype or output.shape[1:] != input.shape[1:] or len(output) != n_dst:
         raise ValueError("output must be [len(dst2src_map), *input.shape[1:]] of input's dtype")

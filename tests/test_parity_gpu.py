@@ -150,6 +150,20 @@ def test_dispatch_matches_oracle(T, H, dtype, E, k, A):
     gu.check_dispatch(x, meta, k)
 
 
+def test_shuffle_rows_takes_an_output_shape():
+    """sglang's shuffle_rows takes the output's shape; so does this one."""
+    _print_case("shuffle_rows with an output shape")
+    rng = np.random.default_rng(4)
+    x = torch.randn((50, 384), device=DEV).to(torch.bfloat16)
+    m = torch.from_numpy(rng.integers(-2, 52, 70).astype(np.int32)).to(DEV)
+    got = mx.shuffle_rows(x, m, (70, 384))
+    torch.cuda.synchronize()
+    assert got.shape == (70, 384) and got.dtype == torch.bfloat16
+    want = oracle.shuffle_rows(gu.bits(x), m.cpu().numpy())
+    used = (m.cpu().numpy() >= 0) & (m.cpu().numpy() < 50)
+    np.testing.assert_array_equal(gu.bits(got)[used], want[used])
+
+
 def test_dispatch_misaligned_base():
     """A base pointer off the 16-byte grid takes a narrower access width and
     still copies exactly."""
