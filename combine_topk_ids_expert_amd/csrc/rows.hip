@@ -107,32 +107,88 @@ __global__ __launch_bounds__(kRowThreads) void shuffle_rows_kernel(
     copy_vector_to<T>(in, c, row_bytes / V, dst, row_bytes, nullptr, 1, r + 1, (int32_t)r);
 }
 
+// Destination indices a side-row thread loads before its stores.
+constexpr int kSideBatch = 8;
+
+// Side rows (the block scales of FP8 rows) of tokens [t0, t0 + group) of
+// n: thread i of the workgroup takes vector i % ns of token t0 + i / ns (ns
+// vectors of S per side row), loads it and the token's destination indices
+// kSideBatch at a time, then stores it to each destination row.
+template <typename S, int P>
+__device__ __forceinline__ void copy_side_rows(const uint8_t* __restrict__ side_src,
+                                               int64_t side_row_bytes, int64_t ns, int64_t t0,
+                                               int32_t group, int64_t n,
+                                               const int32_t* __restrict__ output_perm,
+                                               int32_t topk, uint8_t* __restrict__ side_dst,
+                                               int64_t num_dst_rows) {
+    for (int64_t c0 = 0; c0 < ns * group; c0 += blockDim.x) {
+        const int64_t i = c0 + threadIdx.x;
+        const int64_t u = i / ns;
+        const int64_t p = i - u * ns;
+        const int64_t t = t0 + u;
+        const bool live = u < group && t < n;
+        const S* in = reinterpret_cast<const S*>(side_src + t * side_row_bytes) + p;
+        S v{};
+        if (live && MX_CAN_LOAD(in, sizeof(S), kSiteRowSrc)) v = *in;
+        for (int j0 = 0; j0 < topk; j0 += kSideBatch) {
+            int32_t dr[kSideBatch];
+#pragma unroll
+            for (int jj = 0; jj < kSideBatch; ++jj) {
+                const int32_t* q = output_perm + t * topk + j0 + jj;
+                dr[jj] = live && j0 + jj < topk && MX_CAN_LOAD(q, 4, kSiteRowIndex) ? *q : -1;
+            }
+#pragma unroll
+            for (int jj = 0; jj < kSideBatch; ++jj) {
+                const int32_t r = dr[jj];
+                if (r < 0 || r >= num_dst_rows) continue;
+                uint8_t* row = side_dst + (int64_t)r * side_row_bytes;
+                if constexpr (sizeof(S) == 16)
+                    store16<P>(v, row, side_row_bytes, p * 16, kSiteRowDst);
+                else if (MX_CAN_STORE(reinterpret_cast<S*>(row) + p, sizeof(S), kSiteRowDst))
+                    __builtin_nontemporal_store(v, reinterpret_cast<S*>(row) + p);
+            }
+        }
+    }
+}
+
 // dst[output_perm[t*k + j]] = src[t] for every j: one workgroup per token t
-// and column chunk, one vector per thread; the side row (if any) goes with
-// chunk 0.  P is the cache policy of the 16-byte stores.
+// and column chunk, one vector per thread.  P is the cache policy of the
+// 16-byte stores.  With side rows (SV > 0) the n tokens of the launch are
+// taken in groups of `group`: the group's group * chunks row workgroups,
+// then one workgroup for the group's side rows (copy_side_rows).  Side rows
+// copied by chunk 0 of each token after its row had cost the Zipf workload's
+// FP8 dispatch (4 KiB rows, 128-byte scale rows) 140.5 us against 106 us
+// without them, with the caches flushed before the call; the separate side
+// workgroups took it to 113.5 us.  With the caches warm the separate form
+// measured 105.6 us against 99.6 us: there the longer chunk-0 workgroups had
+// thinned the scattered row writes in flight.
 template <int V, int SV, int P>
 __global__ __launch_bounds__(kRowThreads) void dispatch_rows_kernel(
     const uint8_t* __restrict__ src, int64_t row_bytes, int32_t topk,
     const int32_t* __restrict__ output_perm, uint8_t* __restrict__ dst, int64_t num_dst_rows,
     const uint8_t* __restrict__ side_src, int64_t side_row_bytes,
-    uint8_t* __restrict__ side_dst, int32_t chunks) {
+    uint8_t* __restrict__ side_dst, int32_t chunks, int64_t n, int32_t group) {
     using T = typename Vec<V>::T;
-    int64_t chunk;
-    const int64_t t = chunk_row(chunks, chunk);
-    const int32_t* rows = output_perm + t * topk;
+    int64_t t, chunk;
+    if constexpr (SV > 0) {
+        const uint32_t per = (uint32_t)group * (uint32_t)chunks + 1;
+        const uint32_t g = blockIdx.x / per;
+        const uint32_t w = blockIdx.x - g * per;
+        if (w == per - 1) {
+            copy_side_rows<typename Vec<SV>::T, P>(side_src, side_row_bytes, side_row_bytes / SV,
+                                                   (int64_t)g * group, group, n, output_perm,
+                                                   topk, side_dst, num_dst_rows);
+            return;
+        }
+        t = (int64_t)g * group + w / (uint32_t)chunks;
+        chunk = w % (uint32_t)chunks;
+        if (t >= n) return;
+    } else {
+        t = chunk_row(chunks, chunk);
+    }
     const int64_t c = chunk * blockDim.x + threadIdx.x;
     copy_vector_to<T, P>(reinterpret_cast<const T*>(src + t * row_bytes), c, row_bytes / V, dst,
-                         row_bytes, rows, topk, num_dst_rows);
-    if constexpr (SV > 0) {
-        using S = typename Vec<SV>::T;
-        if (chunk == 0) {
-            const int64_t ns = side_row_bytes / SV;
-            for (int64_t c0 = 0; c0 < ns; c0 += blockDim.x)
-                copy_vector_to<S, P>(reinterpret_cast<const S*>(side_src + t * side_row_bytes),
-                                     c0 + threadIdx.x, ns, side_dst, side_row_bytes, rows, topk,
-                                     num_dst_rows);
-        }
-    }
+                         row_bytes, output_perm + t * topk, topk, num_dst_rows);
 }
 
 int vec_width(int64_t row_bytes, const void* a, const void* b) {
@@ -146,13 +202,13 @@ template <int V, int P>
 void launch_dispatch_v(dim3 grid, dim3 block, size_t lds, int32_t chunks, int side_vec,
                        const uint8_t* s, int64_t row_bytes, int32_t topk,
                        const int32_t* output_perm, uint8_t* d, int64_t num_dst_rows,
-                       const uint8_t* ss, int64_t side_row_bytes, uint8_t* sd,
-                       hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
+                       const uint8_t* ss, int64_t side_row_bytes, uint8_t* sd, int64_t n,
+                       int32_t group, hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
     switch (side_vec) {
-    case 0: launch_kernel(dispatch_rows_kernel<V, 0, P>, grid, block, lds, stream, e0, e1, s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd, chunks); break;
-    case 16: launch_kernel(dispatch_rows_kernel<V, 16, P>, grid, block, lds, stream, e0, e1, s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd, chunks); break;
-    case 4: launch_kernel(dispatch_rows_kernel<V, 4, P>, grid, block, lds, stream, e0, e1, s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd, chunks); break;
-    default: launch_kernel(dispatch_rows_kernel<V, 1, P>, grid, block, lds, stream, e0, e1, s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd, chunks); break;
+    case 0: launch_kernel(dispatch_rows_kernel<V, 0, P>, grid, block, lds, stream, e0, e1, s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd, chunks, n, group); break;
+    case 16: launch_kernel(dispatch_rows_kernel<V, 16, P>, grid, block, lds, stream, e0, e1, s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd, chunks, n, group); break;
+    case 4: launch_kernel(dispatch_rows_kernel<V, 4, P>, grid, block, lds, stream, e0, e1, s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd, chunks, n, group); break;
+    default: launch_kernel(dispatch_rows_kernel<V, 1, P>, grid, block, lds, stream, e0, e1, s, row_bytes, topk, output_perm, d, num_dst_rows, ss, side_row_bytes, sd, chunks, n, group); break;
     }
 }
 
@@ -192,27 +248,43 @@ hipError_t launch_dispatch_rows(const void* src, int64_t num_tokens, int32_t top
         const int sv = vec_width(side_row_bytes, side_src, side_dst);
         side_vec = sv >= 16 ? 16 : sv >= 4 ? 4 : 1;
     }
-    const RowShape sh = row_shape(row_bytes / v, kRowThreads);
+    RowShape sh = row_shape(row_bytes / v, kRowThreads);
+    // Side rows: `group` tokens share one side workgroup (as many whole side
+    // rows as it has threads, at least one).  A launch of n tokens then has
+    // ceil(n / group) * (group * chunks + 1) workgroups, at most
+    // n * (chunks + 1) when n is a multiple of group, which every batch but
+    // the last is.
+    int32_t group = 1;
+    if (side_vec != 0) {
+        const int64_t ns = side_row_bytes / side_vec;
+        group = ns <= sh.threads ? (int32_t)(sh.threads / ns) : 1;
+        int64_t rows = ((int64_t)1 << 31) / ((int64_t)(sh.chunks + 1) * sh.threads);
+        if (rows < 1) rows = 1;
+        if (group > rows) group = (int32_t)rows;
+        sh.rows_per_launch = rows - rows % group;
+    }
     const bool keep = dispatch_store_policy(num_tokens * (row_bytes + side_row_bytes)) == kKeep;
     const size_t lds = !keep && row_bytes >= kWideRowBytes ? kDispatchLdsWide : kDispatchLds;
     const uint8_t* s = static_cast<const uint8_t*>(src);
     uint8_t* d = static_cast<uint8_t*>(dst);
     const uint8_t* ss = static_cast<const uint8_t*>(side_src);
     uint8_t* sd = static_cast<uint8_t*>(side_dst);
-    return for_row_batches(num_tokens, sh, [&](int64_t t0, int64_t, dim3 grid, dim3 block,
+    return for_row_batches(num_tokens, sh, [&](int64_t t0, int64_t n, dim3 grid, dim3 block,
                                                hipEvent_t e0, hipEvent_t e1) {
+        if (side_vec != 0)
+            grid.x = (unsigned)((n + group - 1) / group * ((int64_t)group * sh.chunks + 1));
         const uint8_t* st = s + t0 * row_bytes;
         const int32_t* pt = output_perm + t0 * topk;
         const uint8_t* sst = ss ? ss + t0 * side_row_bytes : nullptr;
         switch (v) {
         case 16:
-            if (keep) launch_dispatch_v<16, kKeep>(grid, block, lds, sh.chunks, side_vec, st, row_bytes, topk, pt, d, num_dst_rows, sst, side_row_bytes, sd, stream, e0, e1);
-            else launch_dispatch_v<16, kStream>(grid, block, lds, sh.chunks, side_vec, st, row_bytes, topk, pt, d, num_dst_rows, sst, side_row_bytes, sd, stream, e0, e1);
+            if (keep) launch_dispatch_v<16, kKeep>(grid, block, lds, sh.chunks, side_vec, st, row_bytes, topk, pt, d, num_dst_rows, sst, side_row_bytes, sd, n, group, stream, e0, e1);
+            else launch_dispatch_v<16, kStream>(grid, block, lds, sh.chunks, side_vec, st, row_bytes, topk, pt, d, num_dst_rows, sst, side_row_bytes, sd, n, group, stream, e0, e1);
             break;
-        case 8: launch_dispatch_v<8, kStream>(grid, block, lds, sh.chunks, side_vec, st, row_bytes, topk, pt, d, num_dst_rows, sst, side_row_bytes, sd, stream, e0, e1); break;
-        case 4: launch_dispatch_v<4, kStream>(grid, block, lds, sh.chunks, side_vec, st, row_bytes, topk, pt, d, num_dst_rows, sst, side_row_bytes, sd, stream, e0, e1); break;
-        case 2: launch_dispatch_v<2, kStream>(grid, block, lds, sh.chunks, side_vec, st, row_bytes, topk, pt, d, num_dst_rows, sst, side_row_bytes, sd, stream, e0, e1); break;
-        default: launch_dispatch_v<1, kStream>(grid, block, lds, sh.chunks, side_vec, st, row_bytes, topk, pt, d, num_dst_rows, sst, side_row_bytes, sd, stream, e0, e1); break;
+        case 8: launch_dispatch_v<8, kStream>(grid, block, lds, sh.chunks, side_vec, st, row_bytes, topk, pt, d, num_dst_rows, sst, side_row_bytes, sd, n, group, stream, e0, e1); break;
+        case 4: launch_dispatch_v<4, kStream>(grid, block, lds, sh.chunks, side_vec, st, row_bytes, topk, pt, d, num_dst_rows, sst, side_row_bytes, sd, n, group, stream, e0, e1); break;
+        case 2: launch_dispatch_v<2, kStream>(grid, block, lds, sh.chunks, side_vec, st, row_bytes, topk, pt, d, num_dst_rows, sst, side_row_bytes, sd, n, group, stream, e0, e1); break;
+        default: launch_dispatch_v<1, kStream>(grid, block, lds, sh.chunks, side_vec, st, row_bytes, topk, pt, d, num_dst_rows, sst, side_row_bytes, sd, n, group, stream, e0, e1); break;
         }
     }, start_event, stop_event);
 }

@@ -207,6 +207,56 @@ def test_dispatch_fp8_with_scale_rows():
     gu.check_dispatch(inp["x"], meta, w.k, inp["scales"])
 
 
+def _raw(t: torch.Tensor) -> np.ndarray:
+    return t.contiguous().view(torch.uint8).cpu().numpy().reshape(t.shape[0], -1)
+
+
+@pytest.mark.parametrize("T,H,E,k,side_cols,side_dtype", [
+    (77, 256, 16, 8, 56, torch.float32),     # 224-byte side rows, 14 vectors of 16 bytes
+    (130, 512, 32, 10, 3, torch.float32),    # 12-byte side rows (4-byte vectors), k > 8
+    (65, 1024, 8, 3, 7, torch.uint8),        # 7-byte side rows (single bytes)
+    (40, 128, 16, 8, 600, torch.float32),    # side rows wider than the workgroup
+    (20, 16400, 8, 8, 56, torch.float32),    # 17 column chunks per row
+    (50, 256, 8, 1, 32, torch.float32),      # k = 1
+    (1, 64, 4, 2, 32, torch.float32),        # one token
+])
+def test_dispatch_side_row_shapes(T, H, E, k, side_cols, side_dtype):
+    """dispatch_rows with side rows of several widths, where some picks are
+    dropped (-1 in the output permutation): row and side row of token t land
+    in every destination t*k + j names, bit for bit as the oracle's gather
+    with the inverse map, and no other row is written."""
+    _print_case("dispatch side rows", T, H, E, k, side_cols, side_dtype)
+    rng = np.random.default_rng(T * 31 + side_cols)
+    ids = routing.uniform_topk(rng, T, E, k)
+    meta = gu.check_prepare(ids, E, 1)
+    outp = meta["_t"]["output_permutation"].clone()
+    outp.view(T, k)[::5] = -1                          # tokens with no pick kept
+    outp.view(-1)[3::7] = -1                           # and single dropped picks
+    rows = meta["_t"]["input_permutation"].numel()
+    outp_h = outp.cpu().numpy().reshape(-1)
+    d2s = np.full(rows, -1, dtype=np.int32)
+    for i, r in enumerate(outp_h):
+        if r >= 0:
+            d2s[r] = i // k
+    used = d2s >= 0
+    x = routing.normal_rows(T, H, "bf16", seed=T + 1, device=DEV)
+    if side_dtype == torch.uint8:
+        side = torch.from_numpy(rng.integers(0, 256, (T, side_cols), dtype=np.uint8)).to(DEV)
+    else:
+        side = torch.from_numpy(rng.standard_normal((T, side_cols)).astype(np.float32)).to(DEV)
+    xd = torch.empty((rows, H), dtype=x.dtype, device=DEV)
+    sd = torch.empty((rows, side_cols), dtype=side.dtype, device=DEV)
+    xd.view(torch.uint8).fill_(gu.SENTINEL)
+    sd.view(torch.uint8).fill_(gu.SENTINEL)
+    mx.dispatch_rows(x, outp, k, xd, side, sd)
+    torch.cuda.synchronize()
+    for got, src, what in ((xd, x, "rows"), (sd, side, "side rows")):
+        want = oracle.shuffle_rows(_raw(src), d2s)
+        g = _raw(got)
+        np.testing.assert_array_equal(g[used], want[used], err_msg=what)
+        assert np.all(g[~used] == gu.SENTINEL), f"{what}: a row no pick names was written"
+
+
 # --------------------------------------------------------------------------
 # combine
 # --------------------------------------------------------------------------
