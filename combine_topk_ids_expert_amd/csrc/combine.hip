@@ -156,7 +156,9 @@ __device__ __forceinline__ float readlane_f(float v, int lane) {
 // lane*4 and 256 + lane*4 within the wave's 512 columns, so that every
 // 16-byte access of a wave covers 1 KiB of one row: 8 consecutive fp32
 // columns per lane would leave every other 16 bytes of each load or store
-// instruction to the next one.  Each wave loads the token's row indices and
+// instruction to the next one.  Measured on MI355X at T = 65536 (bf16 y, fp32
+// out): 16-byte loads of 8 consecutive columns with two such half-filled
+// 16-byte stores ran 2703 us against 1528 us for this layout, same bits.  Each wave loads the token's row indices and
 // weights one per lane (one vector load each) and broadcasts them with
 // readlane; every loop around a readlane is uniform, so threads past the row
 // end stay in the loops and only skip their memory accesses.
