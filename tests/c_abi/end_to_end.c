@@ -14,13 +14,19 @@
  * Inputs are seeded splitmix64 draws (S. Vigna's published generator); they
  * carry none of the method's arithmetic.
  *
- * Usage: end_to_end            exit status 0 iff every case matches
+ * Usage: end_to_end              exit status 0 iff every case matches
+ *        end_to_end --host-cost  also times each call at the decode shape
+ *                                (T = 32, H = 4096, E = 256, top-8): host
+ *                                time to enqueue one call, and GPU time per
+ *                                call with calls back to back
  */
+#define _POSIX_C_SOURCE 199309L  /* clock_gettime */
 #include <hip/hip_runtime_api.h>
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
+#include <time.h>
 
 #include "mxmoe.h"
 
@@ -247,7 +253,93 @@ static void run_case(const Case* c, hipStream_t stream) {
     fflush(stdout);
 }
 
-int main(void) {
+static double now_us(void) {
+    struct timespec ts;
+    clock_gettime(CLOCK_MONOTONIC, &ts);
+    return ts.tv_sec * 1e6 + ts.tv_nsec * 1e-3;
+}
+
+/* Host and GPU time per call of each entry point at the decode shape, with
+ * `reps` calls enqueued back to back on one stream. */
+static void host_cost(hipStream_t stream) {
+    const int64_t T = 32, H = 4096, n = T * 8;
+    const int32_t k = 8, E = 256, A = 1, reps = 2000;
+    const int64_t cap = mx_dispatch_capacity(T, k, E, A), row_bytes = H * 2;
+    int64_t* ids = (int64_t*)host_alloc((size_t)n * 8);
+    for (int64_t i = 0; i < n; ++i) ids[i] = (int64_t)(next_u64() % (uint64_t)E);
+    void* d_ids = dev_alloc((size_t)n * 8);
+    HIP_OK(hipMemcpy(d_ids, ids, (size_t)n * 8, hipMemcpyHostToDevice));
+    int32_t* d_eo = (int32_t*)dev_alloc((size_t)(E + 1) * 4);
+    int32_t* d_inp = (int32_t*)dev_alloc((size_t)cap * 4);
+    int32_t* d_outp = (int32_t*)dev_alloc((size_t)n * 4);
+    void* d_x = dev_alloc((size_t)(T * row_bytes));
+    void* d_xd = dev_alloc((size_t)(cap * row_bytes));
+    void* d_w = dev_alloc((size_t)n * 4);
+    void* d_out = dev_alloc((size_t)(T * row_bytes));
+    HIP_OK(hipMemset(d_x, 0, (size_t)(T * row_bytes)));
+    HIP_OK(hipMemset(d_xd, 0, (size_t)(cap * row_bytes)));
+    HIP_OK(hipMemset(d_w, 0, (size_t)n * 4));
+    hipEvent_t e0, e1;
+    HIP_OK(hipEventCreate(&e0));
+    HIP_OK(hipEventCreate(&e1));
+    const char* names[] = {"mx_prepare_moe_input", "mx_dispatch_rows", "mx_apply_shuffle_mul_sum",
+                           "mx_prepare_dispatch"};
+    for (int call = 0; call < 4; ++call) {
+        double host = 0.0, host_first = 0.0, drain = 0.0;
+        float gpu_ms = 0.0f;
+        for (int pass = 0; pass < 2; ++pass) {  /* the first pass warms up */
+            HIP_OK(hipStreamSynchronize(stream));
+            HIP_OK(hipEventRecord(e0, stream));
+            const double t0 = now_us();
+            for (int r = 0; r < reps; ++r) {
+                mx_status st = MX_OK;
+                switch (call) {
+                case 0:
+                    st = mx_prepare_moe_input(d_ids, MX_I64, T, k, E, 1024, (int32_t)H, (int32_t)H,
+                                              512, A, d_eo, NULL, NULL, d_inp, cap, d_outp, NULL,
+                                              128, NULL, 0, stream);
+                    break;
+                case 1:
+                    st = mx_dispatch_rows(d_x, T, k, row_bytes, d_outp, d_xd, cap, NULL, 0, NULL,
+                                          stream);
+                    break;
+                case 2:
+                    st = mx_apply_shuffle_mul_sum(d_xd, MX_BF16, cap, H, d_outp, d_w, MX_F32, T,
+                                                  k, d_out, MX_BF16, stream);
+                    break;
+                default:
+                    st = mx_prepare_dispatch(d_ids, MX_I64, T, k, E, 1024, (int32_t)H,
+                                             (int32_t)H, 512, A, d_eo, NULL, NULL, d_inp, cap,
+                                             d_outp, NULL, 128, NULL, 0, d_x, row_bytes, d_xd,
+                                             cap, NULL, 0, NULL, stream);
+                    break;
+                }
+                if (st != MX_OK) {
+                    fprintf(stderr, "%s: %s\n", names[call], mx_status_string(st));
+                    exit(3);
+                }
+                if (r == 99) host_first = (now_us() - t0) / 100;
+            }
+            const double t1 = now_us();
+            host = (t1 - t0) / reps;
+            HIP_OK(hipEventRecord(e1, stream));
+            HIP_OK(hipEventSynchronize(e1));
+            drain = now_us() - t1;
+            HIP_OK(hipEventElapsedTime(&gpu_ms, e0, e1));
+        }
+        printf("host_cost: %s: %.2f us host per call over the first 100 calls, %.2f over %d "
+               "(then %.0f us until the GPU finished); %.2f us GPU per call back to back\n",
+               names[call], host_first, host, reps, drain, gpu_ms * 1e3 / reps);
+    }
+    fflush(stdout);
+    HIP_OK(hipEventDestroy(e0));
+    HIP_OK(hipEventDestroy(e1));
+    void* bufs[] = {d_ids, d_eo, d_inp, d_outp, d_x, d_xd, d_w, d_out};
+    for (size_t i = 0; i < sizeof bufs / sizeof bufs[0]; ++i) HIP_OK(hipFree(bufs[i]));
+    free(ids);
+}
+
+int main(int argc, char** argv) {
     int ndev = 0;
     HIP_OK(hipGetDeviceCount(&ndev));
     HIP_OK(hipSetDevice(0));
@@ -267,6 +359,7 @@ int main(void) {
         {"empty", 0, 8, 256, 128, 1, 1, 4096, MX_BF16, 0},
     };
     for (size_t i = 0; i < sizeof cases / sizeof cases[0]; ++i) run_case(&cases[i], stream);
+    if (argc > 1 && strcmp(argv[1], "--host-cost") == 0) host_cost(stream);
     HIP_OK(hipStreamDestroy(stream));
     if (g_failures) {
         fprintf(stderr, "end_to_end: %d comparison(s) failed\n", g_failures);
